@@ -1,0 +1,227 @@
+/*
+ * nvfp4moe -- NVFP4 token-wise quantization and the W4A4 MoE grouped GEMM
+ * path for one AMD MI355X (gfx950), behind a plain C ABI.
+ *
+ * Sources.  The pages this library follows are three news reports on the
+ * miniTE technical report:
+ *   [RU] "miniTE ускоряет RL в NVFP4 на B300: 1,39× к BF16 на Qwen3-30B-A3B"
+ *        (hamidun.com; the Arabic page of the same address family is its twin)
+ *   [JA] "miniTE報告、NVFP4強化学習の安定性を検証" (aib.vote)
+ * [RU], key-facts list: native NVFP4 W4A4 (4-bit weights and activations).
+ * [RU], section "Диагностика, выравнивание и быстрые ядра": the NVFP4
+ *        kernels, the scaling scheme and grouped GEMMs over MoE experts
+ *        carry the overhead that made naive FP4 slower than BF16.
+ * [JA], fourth paragraph: the token-wise NVFP4 path is sped up with a
+ *        contiguous data layout, device-side metadata, amax reuse, grouped
+ *        GEMM and op fusion; quantization policy, linear layers and compute
+ *        backend are kept apart (this library is the compute backend).
+ * [JA], first paragraph: the backward pass runs in BF16.
+ *
+ * NVFP4 as defined by this library (the pages do not define it): per row,
+ * 16 consecutive elements along K share one E4M3 (OCP E4M3FN) scale byte;
+ * each element is a 4-bit E2M1 code (bit 3 = sign, magnitudes
+ * 0,.5,1,1.5,2,3,4,6); one FP32 global decode scale g per tensor or per
+ * row-group.  Value = e2m1(code) * e4m3(scale) * g.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, owned by the caller.  The library
+ *     never allocates, frees or synchronises; work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and the call returns.
+ *   - Row-major layouts; leading dimension = row length unless stated.
+ *   - Errors the host can see (NULL pointer, negative size, bad enum, shape
+ *     or alignment) are returned BEFORE any HIP call.  Then the current
+ *     device is checked to be gfx950 (NVFP4MOE_EARCH otherwise).  Launch
+ *     failures return NVFP4MOE_ELAUNCH.
+ *   - Errors that depend on device data (an expert id outside [0, E)) never
+ *     stop the host: they OR a bit into the optional device word `status`
+ *     (int32, caller-zeroed, sticky) and the offending item is skipped.
+ *   - Zero-sized work (rows == 0, T == 0, ...) is valid and launches nothing
+ *     except what is needed to write well-defined outputs.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* nvfp4moe_stream_t; /* == hipStream_t */
+
+/* status codes */
+#define NVFP4MOE_OK 0
+#define NVFP4MOE_EINVAL (-1)     /* NULL pointer, negative size, bad enum */
+#define NVFP4MOE_ESHAPE (-2)     /* shape or alignment not supported */
+#define NVFP4MOE_EARCH (-3)      /* current device is not gfx950 */
+#define NVFP4MOE_ELAUNCH (-4)    /* a kernel launch failed */
+#define NVFP4MOE_EWORKSPACE (-5) /* workspace missing or too small */
+
+/* device status bits */
+#define NVFP4MOE_STATUS_BAD_EXPERT 1 /* a routing id was outside [0, E) */
+
+/* dtype enum */
+#define NVFP4MOE_F32 0
+#define NVFP4MOE_BF16 1
+#define NVFP4MOE_U8 2
+
+/* GEMM layouts for nvfp4moe_grouped_gemm_bf16 */
+#define NVFP4MOE_NT 0 /* C[M,N]   = A[M,K] . B_e[N,K]^T  (forward, baseline) */
+#define NVFP4MOE_NN 1 /* C[M,N]   = A[M,K] . B_e[K,N]    (data gradient)     */
+#define NVFP4MOE_TN 2 /* C_e[K,N] = A_e[M_e,K]^T . B_e[M_e,N] (weight grad)  */
+
+/* W4A4 GEMM epilogues */
+#define NVFP4MOE_EPI_NONE 0
+
+/* ABI version of this header; returned by nvfp4moe_abi_version(). */
+#define NVFP4MOE_ABI_VERSION 1
+
+int nvfp4moe_abi_version(void);
+/* Static string for a status code (never NULL). */
+const char* nvfp4moe_status_string(int status);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of `rows` x `K` values (steps of the
+ * scaling scheme, [RU] fast-kernels section; amax reuse, [JA] fourth
+ * paragraph).  The rows form `groups` equal consecutive row-groups; each
+ * group has its own global scale (groups = 1 for an activation tensor,
+ * groups = E for a stacked [E*N, K] expert weight).
+ *
+ *   x        [rows][K] of x_dtype (NVFP4MOE_F32 or NVFP4MOE_BF16), 16-byte
+ *            aligned.  Finite values.
+ *   amax_in  [groups] fp32 or NULL.  When given, it is the amax used for the
+ *            global scale (amax reuse; a stale value saturates, it is not an
+ *            error).  When NULL, the amax of each group is computed and
+ *            written to amax_out (which must then be non-NULL) and used.
+ *   amax_out [groups] fp32 or NULL; written only when amax_in is NULL.
+ *   q        [rows][K/2] bytes out: two E2M1 codes per byte, element 2j in
+ *            the low nibble; 8-byte aligned.
+ *   scales   [rows][K/16] bytes out: E4M3 scale per block, row-major,
+ *            unswizzled.
+ *   gscale   [groups] fp32 out: g = amax / 2688 (1 when amax == 0).
+ *   status   unused (may be NULL); kept for a uniform signature.
+ * Per 16-block with amax a: t = a/6, u = t/g, S = E4M3_RNE_satfinite(u),
+ * s = decode(S), d = s*g; code = sign(x) | E2M1_RNE_satfinite(|x|/d)
+ * (magnitude 0 when d == 0).  All steps IEEE fp32, correctly rounded;
+ * results are bit-exact and independent of launch shape.
+ * Errors: EINVAL (NULL, negative, bad dtype, groups < 1, amax_in and
+ * amax_out both NULL), ESHAPE (K % 16 != 0, rows % groups != 0, alignment).
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t groups,
+                   const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales,
+                   float* gscale, int32_t* status, nvfp4moe_stream_t stream);
+
+/*
+ * moe_permute -- routing metadata for the contiguous per-expert layout and
+ * (optionally) the row gather into it, with the amax of the gathered rows
+ * fused in (contiguous layout, device-side metadata, amax reuse: [JA],
+ * fourth paragraph).
+ *
+ * Assignment i = t*k + j (token t, slot j) with expert topk_ids[t][j] goes
+ * to permuted row dest[i]; rows of expert e are [offsets[e], offsets[e+1]);
+ * inside a segment rows keep assignment order (a stable counting sort,
+ * deterministic).  src[dest[i]] = i.  offsets[E] = number of valid
+ * assignments (T*k unless some id is out of range: such an assignment gets
+ * dest = -1, is not placed, and sets NVFP4MOE_STATUS_BAD_EXPERT).
+ *
+ *   topk_ids  [T][k] int32 (device).            T >= 0, 1 <= k, 1 <= E <= 4096
+ *   x         [T][row_elems] of x_dtype, or NULL (metadata only).  16-byte
+ *             aligned; row bytes a multiple of 16.
+ *   x_perm    [T*k][row_elems] out (ignored when x is NULL).
+ *   offsets   [E+1] int32 out; dest, src [T*k] int32 out (src entries past
+ *             offsets[E] are -1).
+ *   amax_out  fp32 [1] or NULL: max |x| over the gathered rows (F32/BF16
+ *             payloads only; 0 for an empty gather).
+ *   workspace device scratch of moe_permute_workspace_size(T, k, E) bytes.
+ */
+size_t moe_permute_workspace_size(int64_t T, int k, int E);
+int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype,
+                int64_t row_elems, void* x_perm, int32_t* offsets, int32_t* dest, int32_t* src,
+                float* amax_out, void* workspace, size_t ws_bytes, int32_t* status,
+                nvfp4moe_stream_t stream);
+
+/*
+ * moe_gather -- out[p] = w[src[p]] * x[src[p] / k] for p < R (w = 1 when
+ * topk_w is NULL); rows with src[p] < 0 are written as zeros.  With
+ * topk_w == NULL any dtype is copied verbatim (NVFP4MOE_U8 row payloads,
+ * e.g. packed NVFP4 codes or scales); with weights the payload must be
+ * F32/BF16 and is scaled in fp32 and rounded to out_dtype (RNE).  This is
+ * the backward of the unpermute-combine ([JA] first and fourth paragraphs).
+ *   x [T][row_elems], src [R], out [R][row_elems]; 16-byte aligned rows.
+ */
+int moe_gather(const void* x, int x_dtype, int64_t row_elems, const int32_t* src,
+               const float* topk_w, int k, int64_t R, void* out, int out_dtype,
+               nvfp4moe_stream_t stream);
+
+/*
+ * moe_unpermute -- out[t] = sum_{j=0..k-1} w[t][j] * y_perm[dest[t*k+j]]
+ * (w = 1 when topk_w is NULL: the gradient of the row gather), accumulated
+ * in fp32 in ascending j with fused multiply-add, then rounded to out_dtype
+ * (RNE).  Entries with dest < 0 contribute nothing.  ([JA] fourth paragraph:
+ * contiguous layout.)
+ *   y_perm [*][D] of y_dtype (F32/BF16), dest [T*k], topk_w [T][k] fp32 or
+ *   NULL, out [T][D] of out_dtype (F32/BF16).  D % 8 == 0, 16-byte aligned.
+ */
+int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const float* topk_w,
+                  int64_t T, int k, int64_t D, void* out, int out_dtype, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_w4a4 -- the grouped NVFP4 x NVFP4 GEMM over the contiguous
+ * per-expert layout ([RU] fast-kernels section; [JA] fourth paragraph):
+ *   C[r][n] = a_g * b_g[e] * sum_k deq(A)[r][k] * deq(B_e)[n][k]
+ * for rows r in [offsets[e], offsets[e+1]).  deq = e2m1 * e4m3 scale
+ * (exact); products accumulate in fp32.  Rows >= offsets[E] are not written.
+ *   a_q [M_total][K/2], a_s [M_total][K/16], a_g [1]      (activations)
+ *   b_q [E][N][K/2],    b_s [E][N][K/16],    b_g [E]      (expert weights)
+ *   offsets [E+1] int32 on the device (never read by the host)
+ *   c [M_total][N] of c_dtype (F32/BF16)
+ * K % 32 == 0, N % 32 == 0, pointers 16-byte aligned.  epilogue must be
+ * NVFP4MOE_EPI_NONE.  workspace may be NULL (none needed).
+ */
+int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                      const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                      const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
+                      void* c, int c_dtype, int epilogue, float* amax_out, void* workspace,
+                      size_t ws_bytes, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_bf16 -- grouped BF16 GEMM, fp32 accumulation (the BF16
+ * backward, [JA] first paragraph; also the BF16 baseline of the forward).
+ *   NVFP4MOE_NT: a [M_total][K], b [E][N][K] -> c [M_total][N]
+ *   NVFP4MOE_NN: a [M_total][K], b [E][K][N] -> c [M_total][N]
+ *   NVFP4MOE_TN: a [M_total][K], b [M_total][N] -> c [E][K][N],
+ *                c_e = sum over rows r of expert e of a[r]^T b[r]
+ *                (an empty expert gives zeros, or leaves c_e unchanged
+ *                when accumulating)
+ * accumulate = 1 adds into c (F32 output only); 0 overwrites.  Rows of c
+ * beyond offsets[E] are not written (NT/NN).  K % 32 == 0 and N % 32 == 0
+ * (TN: K % 32 == 0, N % 32 == 0; M_e arbitrary); 16-byte aligned pointers.
+ * workspace may be NULL.
+ */
+int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* expert_offsets,
+                      int E, int64_t M_total, int64_t N, int64_t K, void* c, int c_dtype,
+                      int accumulate, void* workspace, size_t ws_bytes, nvfp4moe_stream_t stream);
+
+/*
+ * silu_gate_fwd -- H[r][f] = silu(Y1[r][f]) * Y1[r][F+f] (gate half first),
+ * fp32 math, bf16 out (RNE), and amax_out[0] = max |H| over the stored bf16
+ * values, ready for amax reuse by the next quantization ([JA] fourth
+ * paragraph: op fusion, amax reuse).  y1 [R][2F] bf16, h [R][F] bf16,
+ * F % 8 == 0.  amax_out may be NULL.
+ */
+int silu_gate_fwd(const void* y1, int64_t R, int64_t F, void* h, float* amax_out,
+                  nvfp4moe_stream_t stream);
+
+/*
+ * silu_gate_bwd -- dY1 = [dH*U*silu'(G) | dH*silu(G)], fp32 math, bf16 out.
+ * y1 [R][2F] bf16, dh [R][F] bf16, dy1 [R][2F] bf16; F % 8 == 0.
+ */
+int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t F, void* dy1,
+                  nvfp4moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,80 @@
+// Shared host/device helpers for the nvfp4moe HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4moe.h"
+
+namespace nvfp4moe {
+
+// ---------------------------------------------------------------- host side
+// Returns NVFP4MOE_OK when the current device is gfx950, NVFP4MOE_EARCH
+// otherwise.  The answer is cached per device ordinal.
+int check_arch();
+
+inline hipStream_t as_stream(nvfp4moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4MOE_OK : NVFP4MOE_ELAUNCH;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int dtype_bytes(int dt) {
+  return dt == NVFP4MOE_F32 ? 4 : dt == NVFP4MOE_BF16 ? 2 : dt == NVFP4MOE_U8 ? 1 : 0;
+}
+
+// Number of workgroups for grid-stride HBM-bound kernels: enough waves to
+// keep every CU busy without a huge tail.
+constexpr int kStreamBlocks = 256 * 8;
+
+// -------------------------------------------------------------- device side
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Non-negative floats order like their bit patterns: max-reduce |x| with
+// unsigned integer atomics.
+__device__ __forceinline__ void atomic_max_abs(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(fabsf(v)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Block-wide max of non-negative values followed by one atomicMax per block.
+// All threads of the block must call it.
+template <int NT>
+__device__ __forceinline__ void block_atomic_max(float* dst, float v) {
+  __shared__ float red[NT / 64];
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, red[i]);
+    atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(m));
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);
+
+}  // namespace nvfp4moe

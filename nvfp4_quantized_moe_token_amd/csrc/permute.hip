@@ -1,0 +1,455 @@
+// MoE token permutation: routing metadata, row gather, unpermute-combine.
+//
+// Contiguous per-expert data layout with the per-expert offsets produced and
+// consumed on the device, and the activation amax fused into the gather
+// ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph).
+//
+// Metadata is a deterministic stable counting sort of the flattened
+// assignments i = t*k + j by expert id:
+//   1. count_kernel  -- per chunk of kChunk assignments, a histogram over
+//                       experts (LDS atomics; counts are order-free).
+//   2. scan_kernel   -- one workgroup: per-expert totals -> offsets, and
+//                       the first row of every (chunk, expert) pair.
+//   3. rank_kernel   -- per chunk, four waves walk their 256 assignments in
+//                       64-lane steps; equal ids inside a step are matched
+//                       with ballots over the id bits, so the rank of an
+//                       assignment is a popcount, never an atomic: the
+//                       result does not depend on scheduling.
+// Out-of-range ids are skipped (dest = -1) and flagged in the status word.
+#include "common.hpp"
+
+namespace nvfp4moe {
+namespace {
+
+constexpr int kChunk = 1024;      // assignments per chunk (4 waves x 4 steps x 64)
+constexpr int kMaxExperts = 4096;
+
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                    int32_t* __restrict__ counts, float* __restrict__ amax_out) {
+  __shared__ int32_t hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && amax_out) *amax_out = 0.0f;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += 256) {
+    const int64_t a = base + i;
+    if (a < R) {
+      const int32_t e = ids[a];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// counts[c][e] (in) -> first permuted row of (chunk c, expert e) (out);
+// offsets[e] = exclusive prefix of the per-expert totals.  1024 threads are
+// split into `slices` threads per expert, each owning a contiguous range of
+// chunks, so every sequential walk is at most ceil(nchunks / slices) long.
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int64_t nchunks, int E,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int32_t ssum[kMaxExperts];   // per (expert, slice) partial sums
+  __shared__ int32_t ebase[kMaxExperts];  // per expert first row
+  __shared__ int32_t wsum[16];
+  const int slices = E >= 1024 ? 1 : 1024 / E;
+  const int64_t cps = (nchunks + slices - 1) / slices;
+  // Phase 1: slice sums.
+  for (int e0 = 0; e0 < E; e0 += 1024 / slices) {
+    const int e = e0 + (int)threadIdx.x / slices, sl = (int)threadIdx.x % slices;
+    if (e < E) {
+      int32_t sum = 0;
+      const int64_t c1 = (sl + 1) * cps < nchunks ? (sl + 1) * cps : nchunks;
+      for (int64_t c = sl * cps; c < c1; ++c) sum += counts[c * E + e];
+      ssum[e * slices + sl] = sum;
+    }
+  }
+  __syncthreads();
+  // Phase 2: exclusive scan of the expert totals (each thread owns `per`
+  // consecutive experts).
+  const int per = (E + 1023) / 1024;
+  int32_t local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = threadIdx.x * per + i;
+    if (e < E)
+      for (int sl = 0; sl < slices; ++sl) local += ssum[e * slices + sl];
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int32_t incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int32_t run = incl - local;
+  for (int w = 0; w < wid; ++w) run += wsum[w];
+  for (int i = 0; i < per; ++i) {
+    const int e = threadIdx.x * per + i;
+    if (e < E) {
+      offsets[e] = run;
+      ebase[e] = run;
+      for (int sl = 0; sl < slices; ++sl) run += ssum[e * slices + sl];
+    }
+  }
+  if (threadIdx.x == 1023) offsets[E] = run;
+  __syncthreads();
+  // Phase 3: every slice walks its chunk range from its own start row.
+  for (int e0 = 0; e0 < E; e0 += 1024 / slices) {
+    const int e = e0 + (int)threadIdx.x / slices, sl = (int)threadIdx.x % slices;
+    if (e < E) {
+      int32_t r = ebase[e];
+      for (int q = 0; q < sl; ++q) r += ssum[e * slices + q];
+      const int64_t c1 = (sl + 1) * cps < nchunks ? (sl + 1) * cps : nchunks;
+      for (int64_t c = sl * cps; c < c1; ++c) {
+        const int32_t v = counts[c * E + e];
+        counts[c * E + e] = r;
+        r += v;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                   const int32_t* __restrict__ chunk_base, int32_t* __restrict__ dest,
+                                                   int32_t* __restrict__ src, int32_t* __restrict__ status) {
+  // E <= 1024: four waves, one cursor row each; otherwise wave 0 walks the
+  // whole chunk with a single cursor row.
+  __shared__ int32_t cursor[kMaxExperts];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const bool split = E <= 1024;
+  const int64_t cbase = (int64_t)blockIdx.x * kChunk;
+  const int64_t wbase = cbase + wid * (kChunk / 4);
+  if (split) {
+    for (int e = threadIdx.x; e < 4 * E; e += 256) cursor[e] = 0;
+    __syncthreads();
+    for (int s = 0; s < kChunk / 4; s += 64) {
+      const int64_t a = wbase + s + lane;
+      const int32_t e = a < R ? ids[a] : -1;
+      if (e >= 0 && e < E) atomicAdd(&cursor[wid * E + e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+      int32_t r = chunk_base[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int32_t c = cursor[w * E + e];
+        cursor[w * E + e] = r;
+        r += c;
+      }
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += 256) cursor[e] = chunk_base[(int64_t)blockIdx.x * E + e];
+  }
+  __syncthreads();
+  if (!split && wid != 0) return;
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const int nsteps = split ? kChunk / 4 / 64 : kChunk / 64;
+  const int64_t start = split ? wbase : cbase;
+  int32_t* cur = split ? &cursor[wid * E] : cursor;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s = 0; s < nsteps; ++s) {
+    const int64_t a = start + (int64_t)s * 64 + lane;
+    const int32_t raw = a < R ? ids[a] : -1;
+    const bool valid = raw >= 0 && raw < E;
+    if (a < R && !valid && status) atomicOr(status, NVFP4MOE_STATUS_BAD_EXPERT);
+    const int32_t e = valid ? raw : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const uint64_t m = __ballot((e >> b) & 1);
+      match &= ((e >> b) & 1) ? m : ~m;
+    }
+    if (valid) {
+      const int32_t row = cur[e] + __popcll(match & lt);
+      dest[a] = row;
+      src[row] = (int32_t)a;
+    } else if (a < R) {
+      dest[a] = -1;
+    }
+    // The highest lane of each group advances its expert's cursor: one
+    // writer per expert, after every lane of the wave has read it.
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (match >> lane) == 1ull) cur[e] += __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// src entries past offsets[E] (skipped assignments) are -1.
+__global__ void src_tail_kernel(const int32_t* __restrict__ offsets, int E, int64_t R, int32_t* __restrict__ src) {
+  const int64_t valid = offsets[E];
+  for (int64_t p = valid + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < R; p += (int64_t)gridDim.x * blockDim.x)
+    src[p] = -1;
+}
+
+// Row gather (optionally weighted and dtype-converting) with fused amax.
+// One workgroup walks rows p = blockIdx.x, blockIdx.x + gridDim.x, ...;
+// every thread moves 16-byte pieces of the row.
+template <int IN, int OUT, bool WEIGHTED>
+__global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__ x, int64_t row_elems,
+                                                     const int32_t* __restrict__ src, const float* __restrict__ w,
+                                                     int k, int64_t R, uint8_t* __restrict__ out,
+                                                     float* __restrict__ amax_out) {
+  constexpr int ib = IN == NVFP4MOE_F32 ? 4 : IN == NVFP4MOE_BF16 ? 2 : 1;
+  constexpr int ob = OUT == NVFP4MOE_F32 ? 4 : OUT == NVFP4MOE_BF16 ? 2 : 1;
+  float m = 0.0f;
+  if (IN == OUT && !WEIGHTED) {
+    const int64_t n16 = row_elems * ib / 16;
+    for (int64_t p = blockIdx.x; p < R; p += gridDim.x) {
+      const int32_t s = src[p];
+      uint4* o = reinterpret_cast<uint4*>(out + p * row_elems * ob);
+      if (s < 0) {
+        for (int64_t c = threadIdx.x; c < n16; c += 256) o[c] = make_uint4(0, 0, 0, 0);
+        continue;
+      }
+      const uint4* in = reinterpret_cast<const uint4*>(x + (int64_t)(s / k) * row_elems * ib);
+      for (int64_t c = threadIdx.x; c < n16; c += 256) {
+        const uint4 v = in[c];
+        o[c] = v;
+        if (amax_out) {
+          const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (IN == NVFP4MOE_BF16) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[j])), fabsf(bf16_hi(ws[j]))));
+            else if (IN == NVFP4MOE_F32) m = fmaxf(m, fabsf(__uint_as_float(ws[j])));
+          }
+        }
+      }
+    }
+  } else {
+    // Element path in groups of 8 (row_elems % 8 == 0).
+    const int64_t n8 = row_elems / 8;
+    for (int64_t p = blockIdx.x; p < R; p += gridDim.x) {
+      const int32_t s = src[p];
+      const float wt = (WEIGHTED && s >= 0) ? w[s] : 1.0f;
+      for (int64_t c = threadIdx.x; c < n8; c += 256) {
+        float v[8];
+        if (s < 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        } else {
+          const uint8_t* in = x + ((int64_t)(s / k) * row_elems + c * 8) * ib;
+          if (IN == NVFP4MOE_BF16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(in);
+            const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[2 * j] = bf16_lo(ws[j]);
+              v[2 * j + 1] = bf16_hi(ws[j]);
+            }
+          } else {
+            const uint4 u0 = reinterpret_cast<const uint4*>(in)[0], u1 = reinterpret_cast<const uint4*>(in)[1];
+            v[0] = __uint_as_float(u0.x); v[1] = __uint_as_float(u0.y);
+            v[2] = __uint_as_float(u0.z); v[3] = __uint_as_float(u0.w);
+            v[4] = __uint_as_float(u1.x); v[5] = __uint_as_float(u1.y);
+            v[6] = __uint_as_float(u1.z); v[7] = __uint_as_float(u1.w);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= wt;
+        }
+        uint8_t* o = out + (p * row_elems + c * 8) * ob;
+        if (OUT == NVFP4MOE_BF16) {
+          uint4 u;
+          u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+          u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
+          *reinterpret_cast<uint4*>(o) = u;
+          if (amax_out) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(__uint_as_float(f32_to_bf16_rne(v[j]) << 16)));
+          }
+        } else {
+          reinterpret_cast<uint4*>(o)[0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                       __float_as_uint(v[2]), __float_as_uint(v[3]));
+          reinterpret_cast<uint4*>(o)[1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                                       __float_as_uint(v[6]), __float_as_uint(v[7]));
+          if (amax_out) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+          }
+        }
+      }
+    }
+  }
+  if (amax_out) block_atomic_max<256>(amax_out, m);
+}
+
+template <int IN, int OUT, bool WEIGHTED>
+void launch_gather(const void* x, int64_t row_elems, const int32_t* src, const float* w, int k, int64_t R, void* out,
+                   float* amax_out, hipStream_t st) {
+  int64_t grid = R < 2048 ? R : 2048;
+  if (grid < 1) grid = 1;
+  gather_kernel<IN, OUT, WEIGHTED><<<(unsigned)grid, 256, 0, st>>>(
+      reinterpret_cast<const uint8_t*>(x), row_elems, src, w, k, R, reinterpret_cast<uint8_t*>(out), amax_out);
+}
+
+int gather_dispatch(const void* x, int x_dtype, int64_t row_elems, const int32_t* src, const float* w, int k,
+                    int64_t R, void* out, int out_dtype, float* amax_out, hipStream_t st) {
+  if (!w && x_dtype == out_dtype) {
+    if (x_dtype == NVFP4MOE_BF16)
+      launch_gather<NVFP4MOE_BF16, NVFP4MOE_BF16, false>(x, row_elems, src, w, k, R, out, amax_out, st);
+    else if (x_dtype == NVFP4MOE_F32)
+      launch_gather<NVFP4MOE_F32, NVFP4MOE_F32, false>(x, row_elems, src, w, k, R, out, amax_out, st);
+    else
+      launch_gather<NVFP4MOE_U8, NVFP4MOE_U8, false>(x, row_elems, src, w, k, R, out, nullptr, st);
+    return launch_status();
+  }
+#define NVG(I, O)                                                                                       \
+  if (x_dtype == I && out_dtype == O) {                                                                \
+    if (w) launch_gather<I, O, true>(x, row_elems, src, w, k, R, out, amax_out, st);                   \
+    else launch_gather<I, O, false>(x, row_elems, src, w, k, R, out, amax_out, st);                    \
+    return launch_status();                                                                            \
+  }
+  NVG(NVFP4MOE_BF16, NVFP4MOE_BF16)
+  NVG(NVFP4MOE_BF16, NVFP4MOE_F32)
+  NVG(NVFP4MOE_F32, NVFP4MOE_F32)
+  NVG(NVFP4MOE_F32, NVFP4MOE_BF16)
+#undef NVG
+  return NVFP4MOE_EINVAL;
+}
+
+// out[t] = sum_j w[t][j] * y[dest[t*k+j]], fp32 fma in ascending j.
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ y, const int32_t* __restrict__ dest,
+                                                        const float* __restrict__ w, int64_t T, int k, int64_t D,
+                                                        uint8_t* __restrict__ out) {
+  constexpr int ib = IN == NVFP4MOE_F32 ? 4 : 2;
+  constexpr int ob = OUT == NVFP4MOE_F32 ? 4 : 2;
+  const int64_t n8 = D / 8;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    for (int64_t c = threadIdx.x; c < n8; c += 256) {
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int32_t r = dest[t * k + j];
+        if (r < 0) continue;
+        const float wt = w ? w[t * k + j] : 1.0f;
+        const uint8_t* in = y + ((int64_t)r * D + c * 8) * ib;
+        float v[8];
+        if (IN == NVFP4MOE_BF16) {
+          const uint4 u = *reinterpret_cast<const uint4*>(in);
+          const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] = bf16_lo(ws[q]);
+            v[2 * q + 1] = bf16_hi(ws[q]);
+          }
+        } else {
+          const uint4 u0 = reinterpret_cast<const uint4*>(in)[0], u1 = reinterpret_cast<const uint4*>(in)[1];
+          v[0] = __uint_as_float(u0.x); v[1] = __uint_as_float(u0.y);
+          v[2] = __uint_as_float(u0.z); v[3] = __uint_as_float(u0.w);
+          v[4] = __uint_as_float(u1.x); v[5] = __uint_as_float(u1.y);
+          v[6] = __uint_as_float(u1.z); v[7] = __uint_as_float(u1.w);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wt, v[q], acc[q]);
+      }
+      uint8_t* o = out + (t * D + c * 8) * ob;
+      if (OUT == NVFP4MOE_BF16) {
+        uint4 u;
+        u.x = pack_bf16x2(acc[0], acc[1]); u.y = pack_bf16x2(acc[2], acc[3]);
+        u.z = pack_bf16x2(acc[4], acc[5]); u.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(o) = u;
+      } else {
+        reinterpret_cast<uint4*>(o)[0] = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                                                     __float_as_uint(acc[2]), __float_as_uint(acc[3]));
+        reinterpret_cast<uint4*>(o)[1] = make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                                                     __float_as_uint(acc[6]), __float_as_uint(acc[7]));
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace nvfp4moe
+
+using namespace nvfp4moe;
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const int64_t chunks = cdiv(T * k, kChunk);
+  return (size_t)((chunks > 0 ? chunks : 1) * E * 4 + 256);
+}
+
+extern "C" int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype,
+                           int64_t row_elems, void* x_perm, int32_t* offsets, int32_t* dest, int32_t* src,
+                           float* amax_out, void* workspace, size_t ws_bytes, int32_t* status,
+                           nvfp4moe_stream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || row_elems < 0) return NVFP4MOE_EINVAL;
+  if (E > kMaxExperts || k > 64) return NVFP4MOE_ESHAPE;
+  if (!offsets || (T > 0 && (!topk_ids || !dest || !src))) return NVFP4MOE_EINVAL;
+  if (x) {
+    const int eb = dtype_bytes(x_dtype);
+    if (!eb) return NVFP4MOE_EINVAL;
+    if (T > 0 && !x_perm) return NVFP4MOE_EINVAL;
+    if ((row_elems * eb) % 16 != 0 || !aligned(x, 16) || (x_perm && !aligned(x_perm, 16))) return NVFP4MOE_ESHAPE;
+    if (amax_out && x_dtype == NVFP4MOE_U8) return NVFP4MOE_EINVAL;
+  }
+  const int64_t R = T * k;
+  if (R > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  if (ws_bytes < moe_permute_workspace_size(T, k, E) || (R > 0 && !workspace)) return NVFP4MOE_EWORKSPACE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  hipStream_t st = as_stream(stream);
+  const int64_t chunks = cdiv(R, kChunk);
+  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
+  if (R == 0) {
+    fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
+    if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+    return launch_status();
+  }
+  count_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, x ? amax_out : nullptr);
+  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets);
+  rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
+  src_tail_kernel<<<(unsigned)(cdiv(R, 256) < 1024 ? cdiv(R, 256) : 1024), 256, 0, st>>>(offsets, E, R, src);
+  int rc = launch_status();
+  if (rc != NVFP4MOE_OK) return rc;
+  if (!x) {
+    if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+    return launch_status();
+  }
+  return gather_dispatch(x, x_dtype, row_elems, src, nullptr, k, R, x_perm, x_dtype, amax_out, st);
+}
+
+extern "C" int moe_gather(const void* x, int x_dtype, int64_t row_elems, const int32_t* src, const float* topk_w,
+                          int k, int64_t R, void* out, int out_dtype, nvfp4moe_stream_t stream) {
+  if (row_elems < 0 || R < 0 || k < 1) return NVFP4MOE_EINVAL;
+  const int ib = dtype_bytes(x_dtype), ob = dtype_bytes(out_dtype);
+  if (!ib || !ob) return NVFP4MOE_EINVAL;
+  if (R > 0 && (!x || !src || !out)) return NVFP4MOE_EINVAL;
+  if (topk_w || x_dtype != out_dtype) {
+    if (x_dtype == NVFP4MOE_U8 || out_dtype == NVFP4MOE_U8) return NVFP4MOE_EINVAL;
+    if (row_elems % 8 != 0) return NVFP4MOE_ESHAPE;
+  }
+  if ((row_elems * ib) % 16 != 0 || (row_elems * ob) % 16 != 0 || !aligned(x, 16) || !aligned(out, 16))
+    return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (R == 0 || row_elems == 0) return NVFP4MOE_OK;
+  return gather_dispatch(x, x_dtype, row_elems, src, topk_w, k, R, out, out_dtype, nullptr, as_stream(stream));
+}
+
+extern "C" int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const float* topk_w, int64_t T,
+                             int k, int64_t D, void* out, int out_dtype, nvfp4moe_stream_t stream) {
+  if (T < 0 || k < 1 || D < 0) return NVFP4MOE_EINVAL;
+  if ((y_dtype != NVFP4MOE_F32 && y_dtype != NVFP4MOE_BF16) || (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16))
+    return NVFP4MOE_EINVAL;
+  if (T > 0 && D > 0 && (!y_perm || !dest || !out)) return NVFP4MOE_EINVAL;
+  if (D % 8 != 0 || !aligned(y_perm, 16) || !aligned(out, 16)) return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (T == 0 || D == 0) return NVFP4MOE_OK;
+  hipStream_t st = as_stream(stream);
+  const unsigned grid = (unsigned)(T < 4096 ? T : 4096);
+  const uint8_t* y = reinterpret_cast<const uint8_t*>(y_perm);
+  uint8_t* o = reinterpret_cast<uint8_t*>(out);
+  if (y_dtype == NVFP4MOE_BF16 && out_dtype == NVFP4MOE_BF16)
+    unpermute_kernel<NVFP4MOE_BF16, NVFP4MOE_BF16><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
+  else if (y_dtype == NVFP4MOE_BF16)
+    unpermute_kernel<NVFP4MOE_BF16, NVFP4MOE_F32><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
+  else if (out_dtype == NVFP4MOE_BF16)
+    unpermute_kernel<NVFP4MOE_F32, NVFP4MOE_BF16><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
+  else
+    unpermute_kernel<NVFP4MOE_F32, NVFP4MOE_F32><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
+  return launch_status();
+}

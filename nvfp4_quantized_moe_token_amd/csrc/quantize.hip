@@ -1,0 +1,189 @@
+// NVFP4 quantization: amax reduction and the 1x16-block quantizer.
+//
+// The scaling scheme and the NVFP4 kernels are where naive FP4 loses its
+// speed ("miniTE ускоряет RL в NVFP4 на B300", section "Диагностика,
+// выравнивание и быстрые ядра"); the global amax is computed once and
+// reused ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph).
+//
+// Layout: one lane owns one 16-element block: it reads the block (32 bytes
+// of bf16 or 64 of fp32), reduces its amax in registers, derives the E4M3
+// scale, and writes 8 bytes of codes plus 1 scale byte.  Consecutive lanes
+// own consecutive blocks, so the code stores of a wave are one contiguous
+// 512-byte run and the loads cover one contiguous 2 KiB (bf16) span.
+//
+// Exactness.  Every step follows the IEEE fp32 definition: t = a/6 and
+// u = t/g use correctly rounded division (this file is built without fast
+// math and with contraction off).  The element ratio fl32(x/d) is formed as
+// RN32(RN64(x * RN64(1/d))): x and d have 24-bit significands, so x/d is
+// either exactly representable or at least 2^-49 (relative) away from any
+// fp32 rounding midpoint, while the fp64 product is within 2^-52 of x/d;
+// rounding it to fp32 therefore gives exactly fl32(x/d).  The E2M1 rounding
+// of that fp32 ratio uses the hardware converter with a unit scale (RNE,
+// saturating to 6, sign kept, including -0 and +-inf), checked against the
+// oracle over every rounding threshold.
+#include "common.hpp"
+
+namespace nvfp4moe {
+namespace {
+
+constexpr float kGlobalDiv = 2688.0f;  // 6 * 448
+
+__device__ __forceinline__ float global_scale(float amax) {
+  return amax > 0.0f ? amax / kGlobalDiv : 1.0f;
+}
+
+// OCP E4M3FN code of u >= 0 (u may be +inf): round to nearest even,
+// saturate at 448 (0x7E); subnormal step 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float u) {
+  u = fminf(u, 448.0f);
+  if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);  // 0..8, exact scaling
+  uint32_t b = __float_as_uint(u);
+  b += 0x7FFFFu + ((b >> 20) & 1u);  // RNE to 3 mantissa bits
+  return (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t S) { return __builtin_amdgcn_cvt_f32_fp8((int)S, 0); }
+
+template <int NT>
+__global__ __launch_bounds__(NT) void amax_kernel(const uint4* __restrict__ x, int64_t n16_per_group,
+                                                  int is_bf16, float* __restrict__ amax) {
+  const uint4* g = x + (int64_t)blockIdx.y * n16_per_group;
+  float m = 0.0f;
+  for (int64_t i = blockIdx.x * (int64_t)NT + threadIdx.x; i < n16_per_group; i += (int64_t)gridDim.x * NT) {
+    const uint4 w = g[i];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    if (is_bf16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[j])), fabsf(bf16_hi(ws[j]))));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(__uint_as_float(ws[j])));
+    }
+  }
+  block_atomic_max<NT>(&amax[blockIdx.y], m);
+}
+
+// Quantize the 16 fp32 values v of one block with global scale g.
+__device__ __forceinline__ void quantize_block(const float (&v)[16], float g, uint2& codes, uint32_t& S) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  const float t = a / 6.0f;
+  const float u = t > 0.0f ? t / g : 0.0f;
+  S = e4m3_encode(u);
+  const float s = e4m3_decode(S);
+  const float d = s * g;
+  const double inv = d > 0.0f ? 1.0 / (double)d : 0.0;  // d == 0: every ratio becomes +-0
+  uint32_t w0 = 0, w1 = 0;
+#define NVQ_PAIR(W, I, SEL)                                                    \
+  W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, (float)((double)v[I] * inv), \
+                                               (float)((double)v[(I) + 1] * inv), 1.0f, SEL)
+  NVQ_PAIR(w0, 0, 0);
+  NVQ_PAIR(w0, 2, 1);
+  NVQ_PAIR(w0, 4, 2);
+  NVQ_PAIR(w0, 6, 3);
+  NVQ_PAIR(w1, 8, 0);
+  NVQ_PAIR(w1, 10, 1);
+  NVQ_PAIR(w1, 12, 2);
+  NVQ_PAIR(w1, 14, 3);
+#undef NVQ_PAIR
+  codes = make_uint2(w0, w1);
+}
+
+template <int NT, bool BF16>
+__global__ __launch_bounds__(NT) void quantize_kernel(const uint4* __restrict__ x, int64_t nblk, int64_t blk_per_group,
+                                                      int64_t groups, const float* __restrict__ amax,
+                                                      uint2* __restrict__ q, uint8_t* __restrict__ scales,
+                                                      float* __restrict__ gscale) {
+  const int64_t tid = blockIdx.x * (int64_t)NT + threadIdx.x;
+  for (int64_t i = tid; i < groups; i += (int64_t)gridDim.x * NT) gscale[i] = global_scale(amax[i]);
+  int64_t cur_group = -1;
+  float g = 1.0f;
+  for (int64_t b = tid; b < nblk; b += (int64_t)gridDim.x * NT) {
+    const int64_t grp = groups == 1 ? 0 : b / blk_per_group;
+    if (grp != cur_group) {
+      cur_group = grp;
+      g = global_scale(amax[grp]);
+    }
+    float v[16];
+    if (BF16) {
+      const uint4 w0 = x[2 * b], w1 = x[2 * b + 1];
+      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_lo(ws[i]);
+        v[2 * i + 1] = bf16_hi(ws[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 w = x[4 * b + i];
+        v[4 * i] = __uint_as_float(w.x);
+        v[4 * i + 1] = __uint_as_float(w.y);
+        v[4 * i + 2] = __uint_as_float(w.z);
+        v[4 * i + 3] = __uint_as_float(w.w);
+      }
+    }
+    uint2 codes;
+    uint32_t S;
+    quantize_block(v, g, codes, S);
+    q[b] = codes;
+    scales[b] = (uint8_t)S;
+  }
+}
+
+}  // namespace
+
+// Enqueue the quantizer (and the amax reduction when amax_in is NULL).
+// Arguments are already validated.
+static int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t groups,
+                           const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales, float* gscale,
+                           hipStream_t st) {
+  constexpr int NT = 256;
+  const int64_t rpg = rows / groups;
+  const float* amax = amax_in;
+  if (!amax_in) {
+    fill_u32_kernel<<<(unsigned)cdiv(groups, 256), 256, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, groups);
+    const int64_t n16 = rpg * K * dtype_bytes(x_dtype) / 16;
+    if (n16 > 0) {
+      int64_t bx = cdiv(n16, NT * 4);
+      const int64_t cap = groups >= 4096 ? 1 : 4096 / groups;
+      if (bx > cap) bx = cap;
+      amax_kernel<NT><<<dim3((unsigned)bx, (unsigned)groups), NT, 0, st>>>(
+          reinterpret_cast<const uint4*>(x), n16, x_dtype == NVFP4MOE_BF16, amax_out);
+    }
+    amax = amax_out;
+  }
+  const int64_t nblk = rows * (K / 16);
+  const int64_t work = nblk > groups ? nblk : groups;
+  int64_t grid = cdiv(work, NT);
+  if (grid > 256 * 16) grid = 256 * 16;
+  const int64_t bpg = rpg * (K / 16) > 0 ? rpg * (K / 16) : 1;
+  if (x_dtype == NVFP4MOE_BF16)
+    quantize_kernel<NT, true><<<(unsigned)grid, NT, 0, st>>>(reinterpret_cast<const uint4*>(x), nblk, bpg, groups,
+                                                             amax, reinterpret_cast<uint2*>(q), scales, gscale);
+  else
+    quantize_kernel<NT, false><<<(unsigned)grid, NT, 0, st>>>(reinterpret_cast<const uint4*>(x), nblk, bpg, groups,
+                                                              amax, reinterpret_cast<uint2*>(q), scales, gscale);
+  return launch_status();
+}
+
+}  // namespace nvfp4moe
+
+extern "C" int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t groups,
+                              const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales, float* gscale,
+                              int32_t* status, nvfp4moe_stream_t stream) {
+  using namespace nvfp4moe;
+  (void)status;
+  if (rows < 0 || K < 0 || groups < 1) return NVFP4MOE_EINVAL;
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (!gscale || (!amax_in && !amax_out)) return NVFP4MOE_EINVAL;
+  if (rows * K > 0 && (!x || !q || !scales)) return NVFP4MOE_EINVAL;
+  if (K % 16 != 0 || rows % groups != 0) return NVFP4MOE_ESHAPE;
+  if (rows * K > 0 && (!aligned(x, 16) || !aligned(q, 8))) return NVFP4MOE_ESHAPE;
+  if (!aligned(gscale, 4) || (amax_in && !aligned(amax_in, 4)) || (amax_out && !aligned(amax_out, 4)))
+    return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  return quantize_launch(x, x_dtype, rows, K, groups, amax_in, amax_out, q, scales, gscale, as_stream(stream));
+}

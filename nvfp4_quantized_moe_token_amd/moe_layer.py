@@ -1,0 +1,81 @@
+"""One MoE layer on the NVFP4 token-wise path, chained from the C-ABI entry
+points (every step runs in the library's HIP kernels; this module only
+orders the calls and owns the buffers).
+
+Forward ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph:
+contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
+  moe_permute (metadata + gather + amax of X)  ->  nvfp4_quantize(X_perm,
+  amax_in=amax_X)  ->  grouped_gemm_w4a4 (gate+up)  ->  silu_gate_fwd (+amax
+  of H)  ->  nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)
+  ->  moe_unpermute (routing-weighted combine).
+Backward in BF16 (same page, first paragraph), no amax reduction at all:
+  moe_gather(dY, weighted)  ->  NN dgrad / TN wgrad of the down projection
+  ->  silu_gate_bwd  ->  NN dgrad / TN wgrad of gate+up  ->  moe_unpermute
+  (unweighted sum back to tokens).
+"""
+
+import torch
+
+from . import ops
+
+
+def quantize_expert_weights(w):
+    """NVFP4 weights of stacked experts [E, N, K] (one global scale per
+    expert).  Runs once per optimizer step, outside the per-batch path."""
+    E, N, K = w.shape
+    q, s, g, amax = ops.nvfp4_quantize(w.reshape(E * N, K), groups=E)
+    return dict(q=q.view(E, N, K // 2), s=s.view(E, N, K // 16), g=g, amax=amax)
+
+
+class Buffers:
+    """Device buffers of one layer step, allocated once and reused."""
+
+    def __init__(self, T, k, E, D, F, device, backward=False):
+        R = T * k
+        bf, f32, u8, i32 = torch.bfloat16, torch.float32, torch.uint8, torch.int32
+        e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        self.T, self.k, self.E, self.D, self.F = T, k, E, D, F
+        self.ws = e(max(ops.moe_permute_workspace_size(T, k, E), 1), dt=u8)
+        self.x_perm = e(R, D)
+        self.amax = e(2, dt=f32)            # [amax_X, amax_H]
+        self.a1_q, self.a1_s, self.a1_g = e(R, D // 2, dt=u8), e(R, D // 16, dt=u8), e(1, dt=f32)
+        self.y1 = e(R, 2 * F)
+        self.h = e(R, F)
+        self.a2_q, self.a2_s, self.a2_g = e(R, F // 2, dt=u8), e(R, F // 16, dt=u8), e(1, dt=f32)
+        self.y2 = e(R, D)
+        self.out = e(T, D)
+        if backward:
+            self.dy2 = e(R, D)
+            self.dh = e(R, F)
+            self.dy1 = e(R, 2 * F)
+            self.dx_perm = e(R, D)
+            self.dx = e(T, D)
+            self.dw_dn = e(E, D, F, dt=f32)
+            self.dw_gu = e(E, 2 * F, D, dt=f32)
+
+
+def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
+    """W4A4 MoE forward; returns the routing metadata dict."""
+    E = buf.E
+    meta = ops.moe_permute(topk_ids, E, x=x, x_perm=buf.x_perm, amax_out=buf.amax[0:1], workspace=buf.ws)
+    ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s, gscale=buf.a1_g)
+    ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], meta["offsets"],
+                          out=buf.y1)
+    ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])
+    ops.nvfp4_quantize(buf.h, amax_in=buf.amax[1:2], q=buf.a2_q, scales=buf.a2_s, gscale=buf.a2_g)
+    ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"], wq_dn["g"], meta["offsets"],
+                          out=buf.y2)
+    ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=topk_w, out=buf.out)
+    return meta
+
+
+def backward(dy, topk_w, w_gu, w_dn, meta, buf):
+    """BF16 backward of ``forward`` (weight gradients in fp32)."""
+    ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
+    off = meta["offsets"]
+    ops.grouped_gemm_bf16(ops.NN, buf.dy2, w_dn, off, out=buf.dh)
+    ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, off, out=buf.dw_dn)
+    ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
+    ops.grouped_gemm_bf16(ops.NN, buf.dy1, w_gu, off, out=buf.dx_perm)
+    ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, off, out=buf.dw_gu)
+    ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)

@@ -1,0 +1,181 @@
+"""Thin Python binding of the nvfp4moe C ABI.
+
+Same names as the C entry points.  torch supplies device memory (outputs are
+allocated here with torch.empty) and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  Argument marshalling
+only: no arithmetic happens in Python.
+"""
+
+import torch
+
+from . import _lib
+
+F32, BF16, U8 = _lib.F32, _lib.BF16, _lib.U8
+NT, NN, TN = _lib.NT, _lib.NN, _lib.TN
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: U8}
+_TORCH = {F32: torch.float32, BF16: torch.bfloat16, U8: torch.uint8}
+
+
+class NVFP4MoEError(RuntimeError):
+    def __init__(self, fn, rc):
+        super().__init__("%s failed: %s (%d)" % (fn, _lib.status_string(rc), rc))
+        self.rc = rc
+
+
+def _check(fn, rc):
+    if rc != _lib.OK:
+        raise NVFP4MoEError(fn, rc)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("nvfp4moe ops take GPU tensors")
+            if not t.is_contiguous():
+                raise ValueError("nvfp4moe ops take contiguous tensors")
+
+
+def nvfp4_quantize(x, groups=1, amax_in=None, amax_out=None, q=None, scales=None, gscale=None):
+    """NVFP4-quantize a [rows, K] fp32/bf16 tensor.  Returns (q, scales,
+    gscale, amax) where amax is amax_in when given, else the computed one."""
+    _dev(x, amax_in, amax_out, q, scales, gscale)
+    rows, K = x.shape
+    dev = x.device
+    q = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev) if scales is None else scales
+    gscale = torch.empty((groups,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    if amax_in is None and amax_out is None:
+        amax_out = torch.empty((groups,), dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    rc = lib.nvfp4_quantize(_ptr(x), _DT[x.dtype], rows, K, groups, _ptr(amax_in), _ptr(amax_out),
+                            _ptr(q), _ptr(scales), _ptr(gscale), None, _stream())
+    _check("nvfp4_quantize", rc)
+    return q, scales, gscale, (amax_in if amax_in is not None else amax_out)
+
+
+def moe_permute_workspace_size(T, k, E):
+    return _lib.load().moe_permute_workspace_size(T, k, E)
+
+
+def moe_permute(topk_ids, num_experts, x=None, x_perm=None, amax_out=None, want_amax=False, status=None,
+                workspace=None):
+    """Routing metadata (offsets, dest, src) and the optional gather of x
+    rows into the contiguous per-expert layout.  Returns a dict."""
+    _dev(topk_ids, x, x_perm, amax_out, status)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    R = T * k
+    offsets = torch.empty((num_experts + 1,), dtype=torch.int32, device=dev)
+    dest = torch.empty((R,), dtype=torch.int32, device=dev)
+    src = torch.empty((R,), dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    ws_bytes = lib.moe_permute_workspace_size(T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    row_elems = 0
+    x_dtype = BF16
+    if x is not None:
+        row_elems = x.shape[1] if x.dim() == 2 else x[0].numel()
+        x_dtype = _DT[x.dtype]
+        if x_perm is None:
+            x_perm = torch.empty((R,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        if want_amax and amax_out is None:
+            amax_out = torch.empty((1,), dtype=torch.float32, device=dev)
+    rc = lib.moe_permute(_ptr(topk_ids), T, k, num_experts, _ptr(x), x_dtype, row_elems, _ptr(x_perm),
+                         _ptr(offsets), _ptr(dest), _ptr(src), _ptr(amax_out), _ptr(workspace),
+                         workspace.numel(), _ptr(status), _stream())
+    _check("moe_permute", rc)
+    return dict(offsets=offsets, dest=dest, src=src, x_perm=x_perm, amax=amax_out)
+
+
+def moe_gather(x, src, k, topk_w=None, out=None, out_dtype=None):
+    """out[p] = w[src[p]] * x[src[p] // k] (a verbatim row copy when no weights)."""
+    _dev(x, src, topk_w, out)
+    R = src.numel()
+    row_elems = x.shape[1] if x.dim() == 2 else x[0].numel()
+    odt = x.dtype if out_dtype is None else out_dtype
+    out = torch.empty((R,) + tuple(x.shape[1:]), dtype=odt, device=x.device) if out is None else out
+    rc = _lib.load().moe_gather(_ptr(x), _DT[x.dtype], row_elems, _ptr(src), _ptr(topk_w), k, R, _ptr(out),
+                                _DT[out.dtype], _stream())
+    _check("moe_gather", rc)
+    return out
+
+
+def moe_unpermute(y_perm, dest, T, k, topk_w=None, out=None, out_dtype=torch.bfloat16):
+    """out[t] = sum_j w[t, j] * y_perm[dest[t*k + j]]."""
+    _dev(y_perm, dest, topk_w, out)
+    D = y_perm.shape[1]
+    out = torch.empty((T, D), dtype=out_dtype, device=y_perm.device) if out is None else out
+    rc = _lib.load().moe_unpermute(_ptr(y_perm), _DT[y_perm.dtype], _ptr(dest), _ptr(topk_w), T, k, D, _ptr(out),
+                                   _DT[out.dtype], _stream())
+    _check("moe_unpermute", rc)
+    return out
+
+
+def grouped_gemm_w4a4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out=None, out_dtype=torch.float32):
+    """C[r] = a_g * b_g[e] * deq(A)[r] . deq(B_e)^T for rows r of expert e."""
+    _dev(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out)
+    M = a_q.shape[0]
+    K = a_q.shape[1] * 2
+    E, N = b_q.shape[0], b_q.shape[1]
+    out = torch.empty((M, N), dtype=out_dtype, device=a_q.device) if out is None else out
+    rc = _lib.load().grouped_gemm_w4a4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g),
+                                       _ptr(offsets), E, M, N, K, _ptr(out), _DT[out.dtype], _lib.EPI_NONE,
+                                       None, None, 0, _stream())
+    _check("grouped_gemm_w4a4", rc)
+    return out
+
+
+def grouped_gemm_bf16(layout, a, b, offsets, num_experts=None, out=None, out_dtype=torch.float32, accumulate=False):
+    """Grouped BF16 GEMM; layout NT / NN / TN as in the C header."""
+    _dev(a, b, offsets, out)
+    M = a.shape[0]
+    E = offsets.numel() - 1 if num_experts is None else num_experts
+    if layout == NT:
+        K, N = a.shape[1], b.shape[1]
+        shape = (M, N)
+    elif layout == NN:
+        K, N = a.shape[1], b.shape[2]
+        shape = (M, N)
+    elif layout == TN:
+        K, N = a.shape[1], b.shape[1]
+        shape = (E, K, N)
+    else:
+        raise ValueError("layout must be NT, NN or TN")
+    out = torch.empty(shape, dtype=out_dtype, device=a.device) if out is None else out
+    rc = _lib.load().grouped_gemm_bf16(layout, _ptr(a), _ptr(b), _ptr(offsets), E, M, N, K, _ptr(out),
+                                       _DT[out.dtype], int(bool(accumulate)), None, 0, _stream())
+    _check("grouped_gemm_bf16", rc)
+    return out
+
+
+def silu_gate_fwd(y1, h=None, amax_out=None, want_amax=True):
+    """H = silu(G) * U for y1 = [G | U]; returns (h, amax)."""
+    _dev(y1, h, amax_out)
+    R, F2 = y1.shape
+    F = F2 // 2
+    h = torch.empty((R, F), dtype=torch.bfloat16, device=y1.device) if h is None else h
+    if want_amax and amax_out is None:
+        amax_out = torch.empty((1,), dtype=torch.float32, device=y1.device)
+    rc = _lib.load().silu_gate_fwd(_ptr(y1), R, F, _ptr(h), _ptr(amax_out), _stream())
+    _check("silu_gate_fwd", rc)
+    return h, amax_out
+
+
+def silu_gate_bwd(y1, dh, dy1=None):
+    _dev(y1, dh, dy1)
+    R, F2 = y1.shape
+    dy1 = torch.empty((R, F2), dtype=torch.bfloat16, device=y1.device) if dy1 is None else dy1
+    rc = _lib.load().silu_gate_bwd(_ptr(y1), _ptr(dh), R, F2 // 2, _ptr(dy1), _stream())
+    _check("silu_gate_bwd", rc)
+    return dy1

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from nvfp4_quantized_moe_token_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
+              "grouped_gemm_w4a4", "grouped_gemm_bf16", "silu_gate_fwd", "silu_gate_bwd",
+              "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from nvfp4_quantized_moe_token_amd import _lib
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_version_and_status_strings(lib):
+    from nvfp4_quantized_moe_token_amd import _lib
+    macro = int(re.search(r"#define NVFP4MOE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.nvfp4moe_abi_version() == macro == _lib.ABI_VERSION
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert lib.nvfp4moe_status_string(rc)
+    assert lib.nvfp4moe_status_string(12345) == b"unknown status"
+
+
+def test_header_constants_match_binding():
+    from nvfp4_quantized_moe_token_amd import _lib
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define NVFP4MOE_(\w+) \(?(-?\d+)\)?", text))
+    assert int(consts["OK"]) == _lib.OK and int(consts["EINVAL"]) == _lib.EINVAL
+    assert int(consts["ESHAPE"]) == _lib.ESHAPE and int(consts["EWORKSPACE"]) == _lib.EWORKSPACE
+    assert int(consts["F32"]) == _lib.F32 and int(consts["BF16"]) == _lib.BF16 and int(consts["U8"]) == _lib.U8
+    assert int(consts["NT"]) == _lib.NT and int(consts["NN"]) == _lib.NN and int(consts["TN"]) == _lib.TN
+
+
+FAKE = 0x10000  # a 64 KiB-aligned fake device address: never dereferenced
+
+
+def test_quantize_validation(lib):
+    q = lib.nvfp4_quantize
+    # NULL x with work to do
+    assert q(None, 1, 4, 32, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    # bad dtype
+    assert q(FAKE, 7, 4, 32, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    # negative sizes, groups < 1
+    assert q(FAKE, 1, -1, 32, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert q(FAKE, 1, 4, 32, 0, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    # both amax_in and amax_out NULL
+    assert q(FAKE, 1, 4, 32, 1, None, None, FAKE, FAKE, FAKE, None, None) == -1
+    # K % 16, rows % groups
+    assert q(FAKE, 1, 4, 24, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert q(FAKE, 1, 5, 32, 2, None, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    # misaligned x
+    assert q(FAKE + 4, 1, 4, 32, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+
+
+def test_permute_validation(lib):
+    p = lib.moe_permute
+    ws = lib.moe_permute_workspace_size(100, 8, 128)
+    assert ws >= 128 * 4
+    assert lib.moe_permute_workspace_size(-1, 8, 128) == 0
+    assert p(FAKE, 100, 0, 128, None, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, ws, None, None) == -1  # k = 0
+    assert p(FAKE, 100, 8, 5000, None, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 10 ** 9, None, None) == -2  # E too big
+    assert p(FAKE, 100, 8, 128, None, 1, 0, None, None, FAKE, FAKE, None, FAKE, ws, None, None) == -1  # offsets NULL
+    assert p(FAKE, 100, 8, 128, None, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None, None) == -5
+    assert p(FAKE, 100, 8, 128, FAKE, 1, 12, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None, None) == -2  # 24 B rows
+    assert p(FAKE, 100, 8, 128, FAKE, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None) == -1  # amax of u8
+
+
+def test_gather_unpermute_validation(lib):
+    assert lib.moe_gather(FAKE, 1, 64, FAKE, None, 0, 10, FAKE, 1, None) == -1
+    assert lib.moe_gather(FAKE, 2, 64, FAKE, FAKE, 8, 10, FAKE, 2, None) == -1  # weighted bytes
+    assert lib.moe_gather(FAKE, 1, 12, FAKE, FAKE, 8, 10, FAKE, 1, None) == -2
+    assert lib.moe_unpermute(FAKE, 2, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
+    assert lib.moe_unpermute(FAKE, 1, FAKE, None, 4, 8, 60, FAKE, 1, None) == -2
+    assert lib.moe_unpermute(None, 1, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
+
+
+def test_gemm_validation(lib):
+    g = lib.grouped_gemm_w4a4
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None, None, 0, None]
+    bad = list(args); bad[12] = 9
+    assert g(*bad) == -1                       # dtype
+    bad = list(args); bad[13] = 1
+    assert g(*bad) == -1                       # epilogue
+    bad = list(args); bad[10] = 48
+    assert g(*bad) == -2                       # K % 32
+    bad = list(args); bad[9] = 40
+    assert g(*bad) == -2                       # N % 32
+    bad = list(args); bad[6] = None
+    assert g(*bad) == -1                       # offsets
+    b = lib.grouped_gemm_bf16
+    assert b(3, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None, 0, None) == -1
+    assert b(0, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 1, 1, None, 0, None) == -1  # accumulate bf16
+    assert b(1, FAKE, FAKE, FAKE, 4, 64, 64, 48, FAKE, 0, 0, None, 0, None) == -2
+    assert b(2, FAKE + 8, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None, 0, None) == -2
+
+
+def test_silu_validation(lib):
+    assert lib.silu_gate_fwd(None, 4, 64, FAKE, None, None) == -1
+    assert lib.silu_gate_fwd(FAKE, 4, 60, FAKE, None, None) == -2
+    assert lib.silu_gate_bwd(FAKE, FAKE, -1, 64, FAKE, None) == -1
+
+
+def test_ops_refuse_cpu_tensors():
+    import torch
+    from nvfp4_quantized_moe_token_amd import ops
+    with pytest.raises(ValueError):
+        ops.nvfp4_quantize(torch.zeros(4, 32))
+
+
+def test_ctypes_pointer_width():
+    assert ctypes.sizeof(ctypes.c_void_p) == 8

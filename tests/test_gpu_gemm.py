@@ -1,0 +1,200 @@
+"""GPU parity of the grouped GEMMs against the fp64 oracle:
+|C - C_ref| <= 1e-3 * sum_k |a*b| per element (plus bf16 output rounding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _helpers import assert_gemm_close, gpu, require_gpu, to_gpu, to_np
+from oracle import gemm, moe, nvfp4
+from oracle.layer import bf16_round, quantize_weights
+
+pytestmark = gpu
+
+
+def _nv_operands(rng, M, N, K, E, a_scale=1.0, b_scale=0.02):
+    x = (rng.standard_normal((M, K)) * a_scale).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] *= 20
+    w = (rng.standard_normal((E, N, K)) * b_scale).astype(np.float32)
+    a = nvfp4.quantize(x)
+    b = quantize_weights(w)
+    return a, b
+
+
+def _gpu_w4a4(a, b, offs, out_dtype):
+    from nvfp4_quantized_moe_token_amd import ops
+    out = ops.grouped_gemm_w4a4(to_gpu(a[0], torch.uint8), to_gpu(a[1], torch.uint8), to_gpu(a[2], torch.float32),
+                                to_gpu(b[0], torch.uint8), to_gpu(b[1], torch.uint8), to_gpu(b[2], torch.float32),
+                                to_gpu(np.asarray(offs, np.int32), torch.int32), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M,N,K,counts", [
+    (300, 160, 96, [0, 1, 200, 0, 99]),       # empty experts, a 1-row expert, M and N tails, K = 1.5 tiles
+    (257, 256, 256, [257]),                   # one expert, one row past two full tiles
+    (640, 96, 32, [128, 128, 0, 384]),        # exact tiles, K = one half-tile
+])
+def test_w4a4_small(M, N, K, counts, out_dtype):
+    require_gpu()
+    rng = np.random.default_rng(M + N + K)
+    E = len(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a, b = _nv_operands(rng, M, N, K, E)
+    c = _gpu_w4a4(a, b, offs, out_dtype)
+    ref, ab = gemm.grouped_gemm_w4a4(a[0], a[1], a[2], b[0], b[1], b[2], offs)
+    assert_gemm_close(c, ref, ab, bf16_out=out_dtype == torch.bfloat16)
+
+
+def test_w4a4_rows_past_offsets_untouched():
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(5)
+    M, N, K = 200, 64, 64
+    offs = np.array([0, 50, 120], np.int32)   # rows 120.. belong to no expert
+    a, b = _nv_operands(rng, M, N, K, 2)
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    ops.grouped_gemm_w4a4(to_gpu(a[0], torch.uint8), to_gpu(a[1], torch.uint8), to_gpu(a[2], torch.float32),
+                          to_gpu(b[0], torch.uint8), to_gpu(b[1], torch.uint8), to_gpu(b[2], torch.float32),
+                          to_gpu(offs, torch.int32), out=out)
+    c = to_np(out)
+    assert (c[120:] == 7.0).all()
+    ref, ab = gemm.grouped_gemm_w4a4(a[0], a[1], a[2], b[0], b[1], b[2], offs)
+    assert_gemm_close(c[:120], ref[:120], ab[:120])
+
+
+def test_dense_small_config():
+    require_gpu()
+    d = workloads.dense_small()
+    a = nvfp4.quantize(d["x"])
+    w = nvfp4.quantize(d["w"])
+    b = (w[0][None], w[1][None], w[2])
+    c = _gpu_w4a4(a, b, [0, 128], torch.float32)
+    ref, ab = gemm.dense_gemm_w4a4(a[0], a[1], a[2], w[0], w[1], w[2])
+    assert_gemm_close(c, ref, ab)
+
+
+def test_qwen3_4b_up_sampled():
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.qwen3_4b_up()
+    x, w = to_gpu(d["x"], torch.bfloat16), to_gpu(d["w"], torch.bfloat16)
+    aq, as_, ag, _ = ops.nvfp4_quantize(x)
+    bq, bs, bg, _ = ops.nvfp4_quantize(w)
+    M = x.shape[0]
+    offs = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    c = ops.grouped_gemm_w4a4(aq, as_, ag, bq[None], bs[None], bg, offs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(0).choice(M, 48, replace=False))
+    ref, ab = gemm.grouped_gemm_w4a4(to_np(aq), to_np(as_), to_np(ag), to_np(bq)[None], to_np(bs)[None],
+                                     to_np(bg), [0, M], rows=rows)
+    assert_gemm_close(to_np(c)[rows], ref, ab, bf16_out=True)
+
+
+@pytest.mark.parametrize("cfg", ["moe_4k", "moe_16k_skew"])
+def test_moe_gate_up_sampled(cfg):
+    # Full-size grouped GEMM1 launch; the oracle checks, for a seeded subset
+    # of experts (always including the largest), the first and last row of
+    # every 128-row tile plus random rows.
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer, ops
+    d = workloads.CONFIGS[cfg]()
+    E, k = d["E"], d["k"]
+    x = to_gpu(d["x"], torch.bfloat16)
+    r = ops.moe_permute(to_gpu(d["topk_ids"], torch.int32), E, x=x, want_amax=True)
+    aq, as_, ag, _ = ops.nvfp4_quantize(r["x_perm"], amax_in=r["amax"])
+    wq = moe_layer.quantize_expert_weights(to_gpu(d["w_gu"], torch.bfloat16))
+    c = ops.grouped_gemm_w4a4(aq, as_, ag, wq["q"], wq["s"], wq["g"], r["offsets"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    off = to_np(r["offsets"])
+    counts = np.diff(off)
+    rng = np.random.default_rng(1)
+    experts = set(rng.choice(np.nonzero(counts)[0], 6, replace=False).tolist()) | {int(counts.argmax())}
+    rows = []
+    for e in sorted(experts):
+        lo, hi = off[e], off[e + 1]
+        for t0 in range(lo, hi, 128):
+            rows += [t0, min(t0 + 127, hi - 1)]
+        rows += rng.integers(lo, hi, 8).tolist()
+    rows = np.unique(np.array(rows))
+    wgq, wgs, wgg = to_np(wq["q"]), to_np(wq["s"]), to_np(wq["g"])
+    ref, ab = gemm.grouped_gemm_w4a4(to_np(aq), to_np(as_), to_np(ag), wgq, wgs, wgg, off, rows=rows)
+    assert_gemm_close(to_np(c)[rows], ref, ab, bf16_out=True, what=cfg)
+
+
+def _bf(rng, shape, scale=1.0):
+    return bf16_round((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_bf16_small(layout, out_dtype):
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(11)
+    counts = [0, 1, 200, 0, 70]
+    E = len(counts)
+    M = sum(counts)
+    K, N = 96, 160
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = _bf(rng, (M, K))
+    b = _bf(rng, (E, N, K) if layout == "NT" else (E, K, N) if layout == "NN" else (M, N), 0.05)
+    lay = {"NT": ops.NT, "NN": ops.NN, "TN": ops.TN}[layout]
+    c = ops.grouped_gemm_bf16(lay, to_gpu(a, torch.bfloat16), to_gpu(b, torch.bfloat16),
+                              to_gpu(offs, torch.int32), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, ab = gemm.grouped_gemm_bf16(layout, a, b, offs)
+    assert_gemm_close(to_np(c), ref, ab, bf16_out=out_dtype == torch.bfloat16, what=layout)
+    if layout == "TN":
+        assert (to_np(c)[0] == 0).all() and (to_np(c)[3] == 0).all()
+
+
+def test_bf16_tn_accumulate():
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(12)
+    counts = [33, 0, 130]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M, K, N = sum(counts), 64, 96
+    a, b = _bf(rng, (M, K)), _bf(rng, (M, N))
+    c0 = rng.standard_normal((3, K, N)).astype(np.float32)
+    out = to_gpu(c0, torch.float32)
+    ops.grouped_gemm_bf16(ops.TN, to_gpu(a, torch.bfloat16), to_gpu(b, torch.bfloat16), to_gpu(offs, torch.int32),
+                          out=out, accumulate=True)
+    torch.cuda.synchronize()
+    ref, ab = gemm.grouped_gemm_bf16("TN", a, b, offs)
+    assert_gemm_close(to_np(out), ref + c0, ab + np.abs(c0), what="TN accumulate")
+    np.testing.assert_array_equal(to_np(out)[1], c0[1])
+
+
+def test_moe_8k_backward_shapes_sampled():
+    # Full-size NN and TN launches of the down projection's backward; the
+    # oracle checks sampled rows (NN) and two experts' weight gradients (TN).
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.moe_8k_update()
+    E, k, F = d["E"], d["k"], d["F"]
+    r = ops.moe_permute(to_gpu(d["topk_ids"], torch.int32), E)
+    off = to_np(r["offsets"])
+    R = int(off[-1])
+    rng = np.random.default_rng(2)
+    dy2 = _bf(rng, (R, 2048), 1e-3)
+    h = _bf(rng, (R, F))
+    w_dn = d["w_dn"]
+    dy2_g, h_g = to_gpu(dy2, torch.bfloat16), to_gpu(h, torch.bfloat16)
+    dh = ops.grouped_gemm_bf16(ops.NN, dy2_g, to_gpu(w_dn, torch.bfloat16), r["offsets"], out_dtype=torch.bfloat16)
+    dw = ops.grouped_gemm_bf16(ops.TN, dy2_g, h_g, r["offsets"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(R, 64, replace=False))
+    experts = np.searchsorted(off, rows, side="right") - 1
+    dh_np = to_np(dh)
+    for rr, e in zip(rows, experts):
+        ref, ab = gemm.grouped_gemm_bf16("NN", dy2[rr:rr + 1], w_dn[e:e + 1], [0, 1])
+        assert_gemm_close(dh_np[rr:rr + 1], ref, ab, bf16_out=True, what="NN row %d" % rr)
+    dw_np = to_np(dw)
+    for e in (0, 77):
+        lo, hi = off[e], off[e + 1]
+        ref, ab = gemm.grouped_gemm_bf16("TN", dy2[lo:hi], h[lo:hi], [0, hi - lo])
+        assert_gemm_close(dw_np[e], ref[0], ab[0], what="TN expert %d" % e)

@@ -1,0 +1,174 @@
+"""GPU parity of moe_permute / moe_gather / moe_unpermute.  Offsets, dest,
+src and gathered rows must equal the oracle's exactly; weighted sums are
+checked within their fp32/bf16 rounding."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _helpers import assert_bf16_close, gpu, require_gpu, to_gpu, to_np
+from conftest import GOLDEN
+from oracle import moe, nvfp4
+
+pytestmark = gpu
+
+
+def _meta(ids_np, E, x_np=None, dtype=torch.bfloat16, status=None):
+    from nvfp4_quantized_moe_token_amd import ops
+    ids = to_gpu(ids_np, torch.int32)
+    x = None if x_np is None else to_gpu(x_np, dtype)
+    r = ops.moe_permute(ids, E, x=x, want_amax=x is not None, status=status)
+    torch.cuda.synchronize()
+    return r
+
+
+def _check_meta(ids_np, E, r):
+    off, dest, src = moe.permute_metadata(ids_np, E)
+    np.testing.assert_array_equal(to_np(r["offsets"]), off)
+    np.testing.assert_array_equal(to_np(r["dest"]), dest)
+    np.testing.assert_array_equal(to_np(r["src"]), src)
+    return off, dest, src
+
+
+def test_worked_example():
+    require_gpu()
+    d = {}
+    for line in open(os.path.join(GOLDEN, "permute_example.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            d[key] = [int(v) for v in vals]
+    ids = np.array(d["ids"], np.int32).reshape(d["T"][0], d["k"][0])
+    r = _meta(ids, d["E"][0])
+    assert to_np(r["offsets"]).tolist() == d["offsets"]
+    assert to_np(r["dest"]).tolist() == d["dest"]
+    assert to_np(r["src"]).tolist() == d["src"]
+
+
+@pytest.mark.parametrize("cfg", ["moe_4k", "moe_16k_skew", "moe_8k_update"])
+def test_config_routing_and_gather(cfg):
+    require_gpu()
+    d = workloads.CONFIGS[cfg](weights=False)
+    r = _meta(d["topk_ids"], d["E"], d["x"])
+    off, dest, src = _check_meta(d["topk_ids"], d["E"], r)
+    xp = to_np(r["x_perm"])
+    rows = np.random.default_rng(0).choice(xp.shape[0], 4096, replace=False)
+    np.testing.assert_array_equal(xp[rows], d["x"][src[rows] // d["k"]])
+    assert to_np(r["amax"])[0] == np.abs(d["x"]).max()
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (5, 3, 4, 1), (1000, 8, 16, 2), (777, 2, 3, 3),
+                                        (3000, 8, 2000, 4), (4096, 8, 128, 5)])
+def test_random_routing(T, k, E, seed):
+    require_gpu()
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)   # duplicates inside a token allowed
+    _check_meta(ids, E, _meta(ids, E))
+
+
+def test_all_to_one_expert_and_empty_experts():
+    require_gpu()
+    ids = np.full((2000, 4), 5, np.int32)
+    _check_meta(ids, 9, _meta(ids, 9))
+
+
+def test_zero_tokens():
+    require_gpu()
+    ids = np.zeros((0, 8), np.int32)
+    r = _meta(ids, 16, np.zeros((0, 64), np.float32))
+    assert to_np(r["offsets"]).tolist() == [0] * 17
+    assert to_np(r["amax"])[0] == 0.0
+
+
+def test_bad_expert_ids_flagged_and_skipped():
+    require_gpu()
+    ids = np.array([[0, 1], [7, 2], [1, -1], [2, 0]], np.int32)   # 7 and -1 are out of range for E = 4
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    r = _meta(ids, 4, status=status)
+    from nvfp4_quantized_moe_token_amd import _lib
+    assert int(status.item()) & _lib.STATUS_BAD_EXPERT
+    dest = to_np(r["dest"])
+    assert dest[2] == -1 and dest[5] == -1
+    off = to_np(r["offsets"])
+    assert off[-1] == 6
+    valid = ids.reshape(-1)
+    keep = (valid >= 0) & (valid < 4)
+    o2, d2, s2 = moe.permute_metadata(np.where(keep, valid, 0)[keep].reshape(1, -1), 4)
+    np.testing.assert_array_equal(off, o2)
+    src = to_np(r["src"])
+    assert (src[6:] == -1).all()
+    np.testing.assert_array_equal(np.nonzero(keep)[0][s2], src[:6])
+
+
+def test_deterministic():
+    require_gpu()
+    d = workloads.moe_4k(weights=False)
+    a = _meta(d["topk_ids"], 128)
+    b = _meta(d["topk_ids"], 128)
+    for key in ("offsets", "dest", "src"):
+        np.testing.assert_array_equal(to_np(a[key]), to_np(b[key]))
+
+
+def test_packed_gather_commutes_with_quantize():
+    # quantize(permute(X)) == permute(quantize(X)) bit for bit on the GPU.
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.moe(512, 1.1, 0.01, 32.0, weights=False, name="t")
+    x = to_gpu(d["x"], torch.bfloat16)
+    ids = to_gpu(d["topk_ids"], torch.int32)
+    r = ops.moe_permute(ids, 128, x=x, want_amax=True)
+    q1, s1, g1, _ = ops.nvfp4_quantize(r["x_perm"], amax_in=r["amax"])
+    q0, s0, g0, _ = ops.nvfp4_quantize(x)
+    q2 = ops.moe_gather(q0, r["src"], 8)
+    s2 = ops.moe_gather(s0, r["src"], 8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(q1), to_np(q2))
+    np.testing.assert_array_equal(to_np(s1), to_np(s2))
+    assert to_np(g0)[0] == to_np(g1)[0]
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
+                                          (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
+def test_weighted_gather(in_dt, out_dt):
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(7)
+    T, k, E, D = 300, 4, 10, 136
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    dy = (rng.standard_normal((T, D)) * 1e-3).astype(np.float32)
+    r = _meta(ids, E)
+    out = ops.moe_gather(to_gpu(dy, in_dt), r["src"], k, topk_w=to_gpu(w, torch.float32), out_dtype=out_dt)
+    torch.cuda.synchronize()
+    src = to_np(r["src"])
+    dyv = to_np(to_gpu(dy, in_dt))
+    ref = moe.gather_rows(dyv, src, k, w)
+    if out_dt == torch.float32:
+        np.testing.assert_allclose(to_np(out), ref, rtol=2.0 ** -23, atol=0)
+    else:
+        assert_bf16_close(to_np(out), ref, what="weighted gather")
+
+
+@pytest.mark.parametrize("weighted", [True, False])
+def test_unpermute(weighted):
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.moe_4k(weights=False)
+    T, k, D = d["T"], d["k"], d["D"]
+    r = _meta(d["topk_ids"], 128)
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal((T * k, D)).astype(np.float32)
+    yg = to_gpu(y, torch.bfloat16)
+    w = to_gpu(d["topk_w"], torch.float32) if weighted else None
+    out = ops.moe_unpermute(yg, r["dest"], T, k, topk_w=w)
+    out32 = ops.moe_unpermute(yg, r["dest"], T, k, topk_w=w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    dest = to_np(r["dest"])
+    ref = moe.unpermute(to_np(yg), dest, k, d["topk_w"] if weighted else None)
+    scale = moe.unpermute_absbound(to_np(yg), dest, k, d["topk_w"] if weighted else None)
+    assert_bf16_close(to_np(out), ref, scale=scale, what="unpermute bf16")
+    err = np.abs(to_np(out32) - ref)
+    assert (err <= 2.0 ** -21 * scale + 1e-30).all()

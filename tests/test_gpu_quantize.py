@@ -1,0 +1,151 @@
+"""GPU parity of nvfp4_quantize: packed codes, scale bytes and global scales
+must equal the oracle's bit for bit."""
+
+import os
+
+import numpy as np
+import torch
+
+import workloads
+from _helpers import gpu, require_gpu, to_gpu, to_np
+from conftest import GOLDEN
+from oracle import nvfp4
+from oracle.layer import bf16_round
+
+pytestmark = gpu
+
+
+def _gpu_quant(x_np, dtype, groups=1, amax=None):
+    from nvfp4_quantized_moe_token_amd import ops
+    x = to_gpu(x_np, dtype)
+    amax_t = None if amax is None else to_gpu(np.asarray(amax, np.float32).reshape(groups), torch.float32)
+    q, s, g, a = ops.nvfp4_quantize(x, groups=groups, amax_in=amax_t)
+    torch.cuda.synchronize()
+    return to_np(q), to_np(s), to_np(g), to_np(a)
+
+
+def _assert_same(x_np, dtype, groups=1, amax=None):
+    q, s, g, a = _gpu_quant(x_np, dtype, groups, amax)
+    xv = x_np if dtype == torch.float32 else bf16_round(x_np)
+    rq, rs, rg, ra = nvfp4.quantize(xv, groups=groups, amax=amax)
+    np.testing.assert_array_equal(a.view(np.uint32), ra.view(np.uint32))
+    np.testing.assert_array_equal(g.view(np.uint32), rg.view(np.uint32))
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(q, rq)
+
+
+def test_golden_blocks_gpu():
+    require_gpu()
+    path = os.path.join(GOLDEN, "quant_blocks.txt")
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, amax, xs, ss, qs = [p.strip() for p in line.split(";")]
+        vals = [float.fromhex(t) if t.strip().lower().startswith(("0x", "-0x")) else float(t) for t in xs.split(",")]
+        x = np.array(vals, np.float32)[None, :]
+        q, s, g, _ = _gpu_quant(x, torch.float32, amax=None if amax == "-" else [float(amax)])
+        assert s.tobytes() == bytes.fromhex(ss.replace(" ", "")), name
+        assert q.tobytes() == bytes.fromhex(qs.replace(" ", "")), name
+
+
+def test_threshold_sweep_unit_scale():
+    # g = 1 and block amax 6 give d = 1, so every element ratio is the
+    # element itself: sweep every E2M1 threshold +-3 ulps, both signs.
+    require_gpu()
+    pts = [0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6]
+    vals = []
+    for p in pts:
+        p = np.float32(p)
+        lo = hi = p
+        vals.append(p)
+        for _ in range(3):
+            lo = np.nextafter(lo, np.float32(-1))
+            hi = np.nextafter(hi, np.float32(7))
+            vals += [lo, hi]
+    v = np.array([x for x in vals if 0 <= x <= 6], np.float32)
+    v = np.concatenate([v, -v])
+    n = (v.size + 14) // 15
+    v = np.concatenate([v, np.zeros(n * 15 - v.size, np.float32)]).reshape(n, 15)
+    x = np.concatenate([np.full((n, 1), 6.0, np.float32), v], axis=1)
+    _assert_same(x, torch.float32, amax=[2688.0])
+
+
+def test_all_bf16_values_several_scales():
+    # Every finite bf16 value, in blocks, under several global amax values
+    # (including stale ones that saturate) -> every code path.
+    require_gpu()
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    f = f[np.isfinite(f)]
+    f = f[: (f.size // 64) * 64].reshape(-1, 64)
+    for amax in [float(np.abs(f).max()), 1.0, 2688.0, 3.0e-30, 7.5e20]:
+        _assert_same(f, torch.bfloat16, amax=[amax])
+
+
+def test_random_fp32_outliers_and_tiny():
+    require_gpu()
+    rng = np.random.default_rng(0)
+    for scale in [1.0, 1e-3, 1e-35, 1e30]:
+        x = (rng.standard_normal((96, 512)) * scale).astype(np.float32)
+        m = rng.random(x.shape) < 0.01
+        x[m] *= 64
+        x[rng.random(x.shape) < 0.05] = 0.0
+        x[rng.random(x.shape) < 0.01] = -0.0
+        _assert_same(x, torch.float32)
+        _assert_same(x, torch.float32, amax=[float(np.abs(x).max()) * 0.3])   # stale, saturating
+
+
+def test_dense_small_fp32():
+    require_gpu()
+    d = workloads.dense_small()
+    _assert_same(d["x"], torch.float32)
+    _assert_same(d["w"], torch.float32)
+
+
+def test_qwen3_4b_up_activation_full():
+    require_gpu()
+    d = workloads.qwen3_4b_up()
+    _assert_same(d["x"], torch.bfloat16)
+
+
+def test_qwen3_4b_up_weight_sampled_rows():
+    # Full-size launch; rows are independent once the amax is known, so the
+    # oracle checks a seeded sample of rows with the same global amax.
+    require_gpu()
+    d = workloads.qwen3_4b_up()
+    w = d["w"]
+    q, s, g, a = _gpu_quant(w, torch.bfloat16)
+    amax = np.float32(np.abs(w).max())
+    assert a[0] == amax
+    rows = np.sort(np.random.default_rng(1).choice(w.shape[0], 512, replace=False))
+    rq, rs, rg, _ = nvfp4.quantize(w[rows], amax=[amax])
+    np.testing.assert_array_equal(q[rows], rq)
+    np.testing.assert_array_equal(s[rows], rs)
+    assert g[0] == rg[0]
+
+
+def test_grouped_expert_weights():
+    require_gpu()
+    rng = np.random.default_rng(2)
+    E, N, K = 6, 40, 96
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    w[2] *= 100.0
+    w[4] = 0.0                       # an all-zero expert: g = 1
+    _assert_same(w.reshape(E * N, K), torch.bfloat16, groups=E)
+
+
+def test_empty_and_single_block():
+    require_gpu()
+    _assert_same(np.zeros((0, 64), np.float32), torch.float32)
+    _assert_same(np.array([[1.5] + [0.0] * 15], np.float32), torch.bfloat16)
+
+
+def test_deterministic_repeat():
+    require_gpu()
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1000, 256)).astype(np.float32)
+    a = _gpu_quant(x, torch.bfloat16)
+    b = _gpu_quant(x, torch.bfloat16)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
