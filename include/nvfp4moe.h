@@ -176,8 +176,11 @@ int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const fl
  *   b_q [E][N][K/2],    b_s [E][N][K/16],    b_g [E]      (expert weights)
  *   offsets [E+1] int32 on the device (never read by the host)
  *   c [M_total][N] of c_dtype (F32/BF16)
- * K % 32 == 0, N % 32 == 0, pointers 16-byte aligned.  epilogue must be
- * NVFP4MOE_EPI_NONE.  workspace may be NULL (none needed).
+ * K % 64 == 0 (every 64-element step holds whole 16-blocks and 4-byte
+ * aligned scale words), N % 32 == 0; a_q, b_q, c 16-byte aligned, a_s, b_s
+ * 4-byte aligned.  epilogue must be NVFP4MOE_EPI_NONE.  workspace may be
+ * NULL (none needed).  Errors: EINVAL (NULL, negative, bad enum), ESHAPE
+ * (the shape and alignment rules above).
  */
 int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
                       const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
@@ -197,6 +200,8 @@ int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
  * accumulate = 1 adds into c (F32 output only); 0 overwrites.  Rows of c
  * beyond offsets[E] are not written (NT/NN).  K % 32 == 0 and N % 32 == 0
  * (TN: K % 32 == 0, N % 32 == 0; M_e arbitrary); 16-byte aligned pointers.
+ * Operands are read through 32-bit buffer offsets: NN needs K*N*2 < 2^31,
+ * TN needs M_total*K*2 and M_total*N*2 < 2^31 (else ESHAPE).
  * workspace may be NULL.
  */
 int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* expert_offsets,

@@ -20,6 +20,18 @@ int check_arch() {
   return ok ? NVFP4MOE_OK : NVFP4MOE_EARCH;
 }
 
+static int g_cu_count[64];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  if (dev >= 0 && dev < 64) g_cu_count[dev] = n;
+  return n;
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = v;

@@ -13,6 +13,9 @@ namespace nvfp4moe {
 // otherwise.  The answer is cached per device ordinal.
 int check_arch();
 
+// Compute units of the current device (cached per device ordinal).
+int device_cu_count();
+
 inline hipStream_t as_stream(nvfp4moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int launch_status() {

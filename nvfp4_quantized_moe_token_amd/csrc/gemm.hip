@@ -10,40 +10,52 @@
 // gfx950 scaled-MFMA format (one power-of-two E8M0 scale per 32 values), and
 // an E2M1 x E4M3 product has up to 6 significant bits, so it is exact in
 // fp16 (range 2^-10 .. 2688) but not in fp8.  The W4A4 kernel therefore
-// stages packed codes and scale bytes from HBM (0.5625 B per element),
-// expands them exactly to fp16 while writing the LDS tile (hardware E2M1
-// decode with a unit scale, then one packed fp16 multiply by the block
-// scale), and runs fp16 MFMA with fp32 accumulation; the two global scales
-// are applied in the fp32 epilogue.
+// moves only packed codes and scale bytes (0.5625 B per element) from HBM
+// into LDS; each wave expands the fragments it feeds to the MFMA exactly to
+// fp16 in registers (hardware E2M1 decode with a unit scale, then one packed
+// fp16 multiply by the block scale) and runs fp16 MFMA 32x32x16 with fp32
+// accumulation.  The two global scales are applied in the fp32 epilogue.
 //
-// Tiling.  A workgroup of 256 threads (2 x 2 waves) computes a 128 x 128
-// output tile; each wave owns 64 x 64 = 2 x 2 MFMA 32x32x16 tiles.  K moves
-// in steps of 64 through two LDS stages (double buffer, one barrier per
-// step); global loads of step k+1 are issued before the MFMAs of step k.
-// LDS rows are 64 elements (128 B) with the 16-byte chunks XOR-swizzled by
-// row, so fragment reads (ds_read_b128) and both writer patterns avoid bank
-// conflicts.  Operands whose reduction dimension is not contiguous in memory
-// (B of the NN layout, both operands of TN) are transposed in registers
-// (4 x 8 blocks, v_perm) on their way to LDS.
+// Data movement.  Every operand tile goes HBM -> LDS by buffer loads that
+// write LDS directly (16 bytes per lane), so no registers stage the tiles
+// and out-of-range rows/columns read as zeros (buffer range checks).  A ring
+// of S LDS stages keeps S-1 K-steps in flight; each step waits for its own
+// loads (s_waitcnt vmcnt) and one workgroup barrier.  Tile layouts in LDS:
+//  * K-major bf16 tiles (rows x 64 k): 128-byte rows, 16-byte chunks
+//    XOR-swizzled by row; fragments are ds_read_b128.
+//  * MN-major bf16 tiles (64 k x columns, as stored in HBM): rows of the
+//    reduction index, chunks XOR-swizzled by (row mod 4); fragments are
+//    read transposed with ds_read_b64_tr_b16 (two per fragment).
+//  * NVFP4 tiles (rows x 64 k): 32 bytes of codes per row (halves swizzled)
+//    and the row's 4 scale bytes.  Lane half h of an MFMA takes the 32 codes
+//    k in [32h, 32h+32) of the step, 8 per MFMA, for A and B alike (a fixed
+//    permutation of the reduction order), so one ds_read_b128 feeds 4 MFMAs.
 //
-// Scheduling.  The host knows only the total row count.  For row-grouped
-// layouts (NT, NN, W4A4) the grid has one slot per possible (m-tile, n-tile)
-// pair, ceil(M/128) + E m-tile slots; each workgroup maps its slot to an
-// expert and row range by scanning the device offsets (wave-wide prefix
-// sums), and surplus slots exit at once.  TN tiles are (expert, k-tile,
-// n-tile) and reduce over the expert's rows.
+// Scheduling.  The host knows only the total row count, so the kernel is
+// persistent: the grid is (CUs x resident workgroups), rounded to a multiple
+// of the 8 XCDs.  Each workgroup counts the real tiles from the device
+// offsets (a wave-wide prefix sum over experts), and the tiles are dealt to
+// XCDs in 8 contiguous equal ranges (workgroup b runs on XCD b % 8), so
+// consecutive tiles -- the n-tiles of one row block, the row blocks of one
+// expert -- share that XCD's L2.  Row-grouped layouts (NT, NN, W4A4) order
+// tiles by (expert row block, n-tile); TN tiles are (expert, k-tile, n-tile)
+// and reduce over the expert's rows.
 #include "common.hpp"
 
 namespace nvfp4moe {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-constexpr int BM = 128, BN = 128, BK = 64, NT = 256;
-constexpr int STAGE_ELEMS = (BM + BN) * BK;  // 16-bit elements per stage
+constexpr int BK = 64;                       // reduction elements per pipeline step
+constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
 enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3 };
 
@@ -64,23 +76,80 @@ struct Params {
   int k_tiles_tn;      // TN: tiles along K (rows of C_e)
 };
 
-// Offset (in 16-bit elements) of chunk c (8 elements) of LDS row `row`.
-__device__ __forceinline__ int lds_off(int row, int c) { return row * BK + ((c ^ ((row ^ (row >> 3)) & 7)) << 3); }
+// ---- small device helpers ----
 
-// Map m-tile slot `slot` to (expert, first row, end row) by a prefix sum of
-// per-expert tile counts.  Runs on wave 0; returns false for surplus slots.
-__device__ bool find_tile(const int32_t* __restrict__ off, int E, int64_t M, int slot, int& e_out, int64_t& r0,
-                          int64_t& r1) {
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRawBufferWord3);
+}
+// One wave-wide LDS-direct load: lane l's `size` bytes land at LDS byte
+// address lds + size*l (lds wave-uniform).  Issued as inline assembly so the
+// compiler does not make every later LDS read wait for it: the kernel keeps
+// the count of its own loads (s_waitcnt vmcnt) and orders LDS with barriers.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// K-major bf16 tile: chunk c (8 elements) of row r at byte r*128 + 16*(c ^ kswz(r)).
+__device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+// MN-major bf16 tile: chunk c of reduction row k at byte k*rowbytes + 16*(c ^ mswz(k)).
+// Any 4 consecutive rows k = 4i..4i+3 then put a transposed read's 32- and
+// 64-byte row segments on disjoint banks.
+__device__ __forceinline__ int mswz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }  // {0, 6, 10, 12}
+// NVFP4 code tile: half h (16 bytes) of row r at byte r*32 + 16*(h ^ nswz(r)).
+__device__ __forceinline__ int nswz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// Clamped [lo, hi) row range of expert e.
+__device__ __forceinline__ void expert_range(const int32_t* __restrict__ off, int e, int64_t M, int& lo, int& hi) {
+  lo = off[e];
+  hi = off[e + 1];
+  lo = lo < 0 ? 0 : lo > M ? (int)M : lo;
+  hi = hi < lo ? lo : hi > M ? (int)M : hi;
+}
+
+// Number of BM-row blocks over all experts.  Runs on one whole wave.
+template <int BM>
+__device__ int count_row_blocks(const int32_t* __restrict__ off, int E, int64_t M) {
   const int lane = threadIdx.x & 63;
-  int running = 0;
+  int total = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int cnt = 0;
+    if (e < E) {
+      int lo, hi;
+      expert_range(off, e, M, lo, hi);
+      cnt = (hi - lo + BM - 1) / BM;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    total += cnt;
+  }
+  return total;
+}
+
+// Map row block `slot` to (expert, first row, end row) by a prefix sum of
+// per-expert block counts.  Runs on one whole wave; false past the last block.
+template <int BM>
+__device__ bool find_row_block(const int32_t* __restrict__ off, int E, int64_t M, int64_t slot, int& e_out,
+                               int64_t& r0, int64_t& r1) {
+  const int lane = threadIdx.x & 63;
+  int64_t running = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
     int lo = 0, hi = 0, cnt = 0;
     if (e < E) {
-      lo = off[e];
-      hi = off[e + 1];
-      lo = lo < 0 ? 0 : lo > M ? (int)M : lo;
-      hi = hi < lo ? lo : hi > M ? (int)M : hi;
+      expert_range(off, e, M, lo, hi);
       cnt = (hi - lo + BM - 1) / BM;
     }
     int incl = cnt;
@@ -96,7 +165,7 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int64_t M, int
       const int srcl = __ffsll((unsigned long long)mask) - 1;
       e_out = __shfl(e, srcl, 64);
       const int lo_s = __shfl(lo, srcl, 64), hi_s = __shfl(hi, srcl, 64), ex = __shfl(incl - cnt, srcl, 64);
-      r0 = lo_s + (int64_t)(slot - running - ex) * BM;
+      r0 = lo_s + (slot - running - ex) * BM;
       r1 = r0 + BM < hi_s ? r0 + BM : hi_s;
       return true;
     }
@@ -105,81 +174,120 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int64_t M, int
   return false;
 }
 
-// ---- loaders: global -> registers (issue) and registers -> LDS (commit) ----
+// ---- HBM -> LDS loaders (one pipeline step, this wave's share) ----
+//
+// Each wave-wide load moves 1 KiB (64 lanes x 16 B) to a contiguous LDS
+// range; a lane's 16 bytes are chosen so that the range holds the swizzled
+// layout.  Offsets are relative to a range-checked operand region: offsets
+// at or past its end, or marked kOOB, read as zeros.
 
-// K-major bf16 tile: 128 rows x 64 k from a row-major [*, ld] matrix.
-struct KMajorRegs {
-  uint4 v[4];
+// K-major bf16 tile of ROWS rows x 64 k; row r of the tile is row r of the
+// region, element k0 + k.  `ld` is the row pitch in elements.
+template <int ROWS, int NW>
+struct KMajorLoader {
+  static_assert(ROWS % (8 * NW) == 0, "K-major tile: rows per wave");
+  static constexpr int N_INSTR = ROWS / (8 * NW);
+  __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
+                                              int64_t k0, int64_t K) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const int row = idx * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ kswz(row);
+      const int64_t k = k0 + c * 8;
+      const uint32_t voff = k < K ? (uint32_t)((row * ld + k) * 2) : kOOB;
+      dma16(r, lds + idx * 1024, voff);
+    }
+  }
 };
-__device__ __forceinline__ void kmajor_issue(KMajorRegs& r, const uint16_t* __restrict__ base, int64_t ld, int64_t row0,
-                                             int64_t row_end, int64_t k0, int64_t K) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = threadIdx.x + NT * i, row = u >> 3, c = u & 7;
-    const int64_t gr = row0 + row, gk = k0 + c * 8;
-    r.v[i] = (gr < row_end && gk < K) ? *reinterpret_cast<const uint4*>(base + gr * ld + gk) : make_uint4(0, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void kmajor_commit(const KMajorRegs& r, uint16_t* lds) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = threadIdx.x + NT * i, row = u >> 3, c = u & 7;
-    *reinterpret_cast<uint4*>(lds + lds_off(row, c)) = r.v[i];
-  }
-}
 
-// MN-major bf16 tile: 64 reduction rows x 128 columns of a row-major
-// [*, ld] matrix, stored transposed ([column][k]) in LDS.
-struct MNMajorRegs {
-  uint4 v[4];
+// MN-major bf16 tile of 64 reduction rows x COLS columns; reduction row kr
+// is region row (row0 + kr), column n0 + n; `ld` is the row pitch.
+template <int COLS, int NW>
+struct MNMajorLoader {
+  static_assert(COLS == 128 || COLS == 256, "MN-major tile width");
+  static constexpr int CPR = COLS / 8;  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per 1 KiB load
+  static_assert((64 / RPI) % NW == 0, "MN-major tile: loads per wave");
+  static constexpr int N_INSTR = 64 / RPI / NW;
+  __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
+                                              int64_t row0, int64_t n0, int64_t ncols) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const int kr = idx * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ mswz(kr);
+      const int64_t n = n0 + c * 8;
+      const uint32_t voff = n < ncols ? (uint32_t)(((row0 + kr) * ld + n) * 2) : kOOB;
+      dma16(r, lds + idx * 1024, voff);
+    }
+  }
 };
-__device__ __forceinline__ void mnmajor_issue(MNMajorRegs& r, const uint16_t* __restrict__ base, int64_t ld, int64_t k0,
-                                              int64_t k_end, int64_t n0, int64_t ncols) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int ng = lane & 15, kq = (lane >> 4) + 4 * wid;
-  const int64_t gn = n0 + ng * 8;
+
+// NVFP4 codes of ROWS rows x 64 k (32 B per row); offsets relative to the
+// codes region (row pitch K/2 bytes).
+template <int ROWS, int NW>
+struct NVCodeLoader {
+  static_assert(ROWS % (32 * NW) == 0, "NVFP4 tile: rows per wave");
+  static constexpr int N_INSTR = ROWS / (32 * NW);
+  __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t K,
+                                              int64_t k0) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t gk = k0 + kq * 4 + i;
-    r.v[i] = (gk < k_end && gn < ncols) ? *reinterpret_cast<const uint4*>(base + gk * ld + gn) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < N_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const int row = idx * 32 + (lane >> 1);
+      const int h = (lane & 1) ^ nswz(row);
+      dma16(r, lds + idx * 1024, (uint32_t)(row * (K / 2) + k0 / 2 + h * 16));
+    }
   }
-}
-__device__ __forceinline__ void mnmajor_commit(const MNMajorRegs& r, uint16_t* lds) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int ng = lane & 15, kq = (lane >> 4) + 4 * wid;
-  const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-  const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-  const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
-  const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = j >> 1;
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    uint2 d;
-    d.x = __builtin_amdgcn_perm(w1[m], w0[m], sel);  // k = 4kq, 4kq+1
-    d.y = __builtin_amdgcn_perm(w3[m], w2[m], sel);  // k = 4kq+2, 4kq+3
-    const int row = ng * 8 + j;
-    *reinterpret_cast<uint2*>(lds + lds_off(row, kq >> 1) + (kq & 1) * 4) = d;
-  }
+};
+
+// ---- fragment readers (LDS -> MFMA operands) ----
+
+// K-major bf16 fragment: rows base + (lane % 32), k = 16*kk + 8*(lane/32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_kmajor(const uint8_t* tile, int base, int kk, int lane) {
+  const int row = base + (lane & 31);
+  const int c = kk * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(tile + row * 128 + ((c ^ kswz(row)) << 4));
 }
 
-// NVFP4 K-major tile: 128 rows x 64 k (two 16-blocks of 32 per thread),
-// expanded exactly to fp16.
-struct NVRegs {
+// MN-major bf16 fragment through two transposed reads: column base +
+// (lane % 32), k = 16*kk + 8*(lane/32) + 4*j + 0..3 for read j.  Within a
+// 16-lane group, lane 4t+s addresses reduction row (k0 + t), columns
+// 4s..4s+3 of the group's 16; the hardware returns to lane i the column i
+// of that 4 x 16 block (probed on the device).
+template <int COLS>
+__device__ __forceinline__ bf16x8_t frag_mnmajor(const uint8_t* tile, int base, int kk, int lane) {
+  const int col = base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  bf16x8_t out;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kr = 16 * kk + 8 * (lane >> 5) + 4 * j + ((lane & 15) >> 2);
+    const int off = kr * (COLS * 2) + (((col >> 3) ^ mswz(kr)) << 4) + ((col & 7) << 1);
+    const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off));
+    out[4 * j + 0] = v[0];
+    out[4 * j + 1] = v[1];
+    out[4 * j + 2] = v[2];
+    out[4 * j + 3] = v[3];
+  }
+  return out;
+}
+
+// NVFP4 fragment: the lane's 32 codes (row base + lane % 32, k in
+// [32h, 32h+32), h = lane / 32) and its two block scales.
+struct NVFrag {
   uint4 q;
-  uint32_t s;
+  uint32_t s;  // low byte: block 2h, next byte: block 2h+1
 };
-__device__ __forceinline__ void nv_issue(NVRegs& r, const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
-                                         int64_t K, int64_t row0, int64_t row_end, int64_t k0) {
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int64_t gr = row0 + row, gk = k0 + half * 32;
-  if (gr < row_end && gk < K) {
-    r.q = *reinterpret_cast<const uint4*>(q + gr * (K / 2) + gk / 2);
-    r.s = *reinterpret_cast<const uint16_t*>(s + gr * (K / 16) + gk / 16);
-  } else {
-    r.q = make_uint4(0, 0, 0, 0);
-    r.s = 0;
-  }
+__device__ __forceinline__ NVFrag frag_nv(const uint8_t* codes, const uint8_t* scales, int base, int lane) {
+  const int row = base + (lane & 31), h = lane >> 5;
+  NVFrag f;
+  f.q = *reinterpret_cast<const uint4*>(codes + row * 32 + ((h ^ nswz(row)) << 4));
+  f.s = *reinterpret_cast<const uint16_t*>(scales + row * 4 + h * 2);
+  return f;
 }
 __device__ __forceinline__ uint32_t nv_pair(uint32_t w, f16x2_t sc, int sel) {
   f16x2_t v;
@@ -192,209 +300,391 @@ __device__ __forceinline__ uint32_t nv_pair(uint32_t w, f16x2_t sc, int sel) {
   v = v * sc;  // exact: <= 6 significant bits, inside the fp16 normal range
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ void nv_commit(const NVRegs& r, uint16_t* lds) {
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.s, 0);
-  const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.s, 1);
-  const f16x2_t sc0 = {s0, s0}, sc1 = {s1, s1};
-  const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
-    const f16x2_t sc = wi < 2 ? sc0 : sc1;
-    uint4 o;
-    o.x = nv_pair(w[wi], sc, 0);
-    o.y = nv_pair(w[wi], sc, 1);
-    o.z = nv_pair(w[wi], sc, 2);
-    o.w = nv_pair(w[wi], sc, 3);
-    *reinterpret_cast<uint4*>(lds + lds_off(row, half * 4 + wi)) = o;
+// MFMA operand kk (k = 32h + 8kk + 0..7): 8 codes expanded exactly to fp16.
+__device__ __forceinline__ f16x8_t nv_expand(const NVFrag& f, int kk) {
+  const uint32_t w = kk == 0 ? f.q.x : kk == 1 ? f.q.y : kk == 2 ? f.q.z : f.q.w;
+  const _Float16 s =
+      (_Float16)(kk < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)f.s, 0) : __builtin_amdgcn_cvt_f32_fp8((int)f.s, 1));
+  const f16x2_t sc = {s, s};
+  uint4 o;
+  o.x = nv_pair(w, sc, 0);
+  o.y = nv_pair(w, sc, 1);
+  o.z = nv_pair(w, sc, 2);
+  o.w = nv_pair(w, sc, 3);
+  return __builtin_bit_cast(f16x8_t, o);
+}
+
+// Scheduling hint: N_MFMA MFMAs with N_DS LDS reads interleaved one after
+// each MFMA (the reads feed the next sub-step), then any reads left over.
+template <int N_MFMA, int N_DS>
+__device__ __forceinline__ void interleave_mfma_ds() {
+  if constexpr (N_MFMA > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (N_DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+    interleave_mfma_ds<N_MFMA - 1, (N_DS > 0 ? N_DS - 1 : 0)>();
+  } else if constexpr (N_DS > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, N_DS, 0);
+  }
+}
+
+// Scheduling hint: N_MFMA MFMAs, each followed by up to PER VALU
+// instructions (the operand expansion of the next sub-step).
+template <int N_MFMA, int PER>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  if constexpr (N_MFMA > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);  // VALU
+    interleave_mfma_valu<N_MFMA - 1, PER>();
   }
 }
 
 // ---- the kernel ----
 
-template <int MODE>
-__global__ __launch_bounds__(NT) void gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE_ELEMS];
-  __shared__ int64_t s_tile[3];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+template <int MODE, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");
+  constexpr bool NV = MODE == W4A4;
+  constexpr int A_BYTES = NV ? BM * 32 : BM * BK * 2;
+  constexpr int B_BYTES = NV ? BN * 32 : BN * BK * 2;
+  constexpr int SC_BYTES = NV ? (BM + BN) * 4 : 0;  // A scales then B scales
+  constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  static_assert(!NV || (BM + BN) % (64 * NW) == 0, "NVFP4 scales: rows per wave");
+  constexpr int SC_INSTR = NV ? (BM + BN) / (64 * NW) : 0;
+  // Per-wave loads per step, for the vmcnt waits.
+  constexpr int A_INSTR = NV ? NVCodeLoader<BM, NW>::N_INSTR
+                        : MODE == TN_BF16 ? MNMajorLoader<BM, NW>::N_INSTR
+                                          : KMajorLoader<BM, NW>::N_INSTR;
+  constexpr int B_INSTR = NV ? NVCodeLoader<BN, NW>::N_INSTR
+                        : MODE == NT_BF16 ? KMajorLoader<BN, NW>::N_INSTR
+                                          : MNMajorLoader<BN, NW>::N_INSTR;
+  constexpr int NDMA = A_INSTR + B_INSTR + SC_INSTR;
+  static_assert(S >= 2 && S <= 4 && NDMA * (S - 2) <= 63, "pipeline depth");
 
-  int expert;
-  int64_t m0, m_end;     // output rows (row-grouped) or C_e rows (TN)
-  int64_t n0;
-  int64_t k_begin, k_end;  // reduction range
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  __shared__ int64_t s_tile[4];
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wid / WN, wn = wid % WN;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void_t*)smem;  // LDS byte address
+
+  // Real tile count, then this XCD's contiguous share of it.
+  int64_t total;
   if (MODE == TN_BF16) {
-    const int per_e = p.k_tiles_tn * p.n_tiles;
-    expert = blockIdx.x / per_e;
-    const int rem = blockIdx.x % per_e;
-    m0 = (int64_t)(rem / p.n_tiles) * BM;
-    m_end = p.K;
-    n0 = (int64_t)(rem % p.n_tiles) * BN;
-    int lo = p.offsets[expert], hi = p.offsets[expert + 1];
-    lo = lo < 0 ? 0 : lo > p.M ? (int)p.M : lo;
-    hi = hi < lo ? lo : hi > p.M ? (int)p.M : hi;
-    k_begin = lo;
-    k_end = hi;
+    total = (int64_t)p.E * p.k_tiles_tn * p.n_tiles;
   } else {
-    const int slot = blockIdx.x / p.n_tiles;
-    n0 = (int64_t)(blockIdx.x % p.n_tiles) * BN;
     if (wid == 0) {
-      int e;
-      int64_t r0, r1;
-      const bool ok = find_tile(p.offsets, p.E, p.M, slot, e, r0, r1);
-      if (lane == 0) {
-        s_tile[0] = ok ? e : -1;
-        s_tile[1] = r0;
-        s_tile[2] = r1;
-      }
+      const int blocks = count_row_blocks<BM>(p.offsets, p.E, p.M);
+      if (lane == 0) s_tile[3] = blocks;
     }
-    __syncthreads();
-    if (s_tile[0] < 0) return;
-    expert = (int)s_tile[0];
-    m0 = s_tile[1];
-    m_end = s_tile[2];
-    k_begin = 0;
-    k_end = p.K;
+    lds_barrier();
+    total = s_tile[3] * p.n_tiles;
   }
+  const int xcd = blockIdx.x & 7;
+  const int64_t t_end = total * (xcd + 1) / 8, t_step = gridDim.x >> 3;
 
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Operand views.
-  const uint16_t* A16 = reinterpret_cast<const uint16_t*>(p.a);
-  const uint16_t* B16 = reinterpret_cast<const uint16_t*>(p.b);
-  const uint8_t* Aq = reinterpret_cast<const uint8_t*>(p.a);
-  const uint8_t* Bq = reinterpret_cast<const uint8_t*>(p.b) + (MODE == W4A4 ? (int64_t)expert * p.N * (p.K / 2) : 0);
-  const uint8_t* Bs = MODE == W4A4 ? p.bs + (int64_t)expert * p.N * (p.K / 16) : nullptr;
-  const uint16_t* Be = MODE == NT_BF16 ? B16 + (int64_t)expert * p.N * p.K
-                     : MODE == NN_BF16 ? B16 + (int64_t)expert * p.K * p.N
-                                       : B16;
-
-  KMajorRegs ra_k, rb_k;
-  MNMajorRegs ra_mn, rb_mn;
-  NVRegs ra_nv, rb_nv;
-
-  auto issue = [&](int64_t kb) {
-    if (MODE == NT_BF16) {
-      kmajor_issue(ra_k, A16, p.K, m0, m_end, kb, p.K);
-      kmajor_issue(rb_k, Be, p.K, n0, p.N, kb, p.K);
-    } else if (MODE == NN_BF16) {
-      kmajor_issue(ra_k, A16, p.K, m0, m_end, kb, p.K);
-      mnmajor_issue(rb_mn, Be, p.N, kb, p.K, n0, p.N);
-    } else if (MODE == TN_BF16) {
-      mnmajor_issue(ra_mn, A16, p.K, kb, k_end, m0, p.K);
-      mnmajor_issue(rb_mn, B16, p.N, kb, k_end, n0, p.N);
+  for (int64_t L = total * xcd / 8 + (blockIdx.x >> 3); L < t_end; L += t_step) {
+    int expert;
+    int64_t m0, m_end;  // output rows (row-grouped) or C_e rows (TN)
+    int64_t n0;
+    int64_t red;        // reduction length
+    int lo = 0;         // TN: first row of the expert
+    lds_barrier();      // previous tile: every wave is done with LDS and s_tile
+    if (MODE == TN_BF16) {
+      const int per_e = p.k_tiles_tn * p.n_tiles;
+      expert = (int)(L / per_e);
+      const int rem = (int)(L % per_e);
+      m0 = (int64_t)(rem / p.n_tiles) * BM;
+      m_end = p.K;
+      n0 = (int64_t)(rem % p.n_tiles) * BN;
+      int hi;
+      expert_range(p.offsets, expert, p.M, lo, hi);
+      red = hi - lo;
     } else {
-      nv_issue(ra_nv, Aq, p.as, p.K, m0, m_end, kb);
-      nv_issue(rb_nv, Bq, Bs, p.K, n0, p.N, kb);
-    }
-  };
-  auto commit = [&](int stage) {
-    uint16_t* As = smem + stage * STAGE_ELEMS;
-    uint16_t* Bsm = As + BM * BK;
-    if (MODE == NT_BF16) {
-      kmajor_commit(ra_k, As);
-      kmajor_commit(rb_k, Bsm);
-    } else if (MODE == NN_BF16) {
-      kmajor_commit(ra_k, As);
-      mnmajor_commit(rb_mn, Bsm);
-    } else if (MODE == TN_BF16) {
-      mnmajor_commit(ra_mn, As);
-      mnmajor_commit(rb_mn, Bsm);
-    } else {
-      nv_commit(ra_nv, As);
-      nv_commit(rb_nv, Bsm);
-    }
-  };
-
-  const int64_t nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-  if (nk > 0) {
-    issue(k_begin);
-    commit(0);
-    __syncthreads();
-  }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int stage = (int)(kt & 1);
-    if (kt + 1 < nk) issue(k_begin + (kt + 1) * BK);
-    const uint16_t* As = smem + stage * STAGE_ELEMS;
-    const uint16_t* Bsm = As + BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      uint4 af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const uint4*>(As + lds_off(wm * 64 + i * 32 + (lane & 31), c));
-        bf[i] = *reinterpret_cast<const uint4*>(Bsm + lds_off(wn * 64 + i * 32 + (lane & 31), c));
+      if (wid == 0) {
+        int e = -1;
+        int64_t r0 = 0, r1 = 0;
+        const bool ok = find_row_block<BM>(p.offsets, p.E, p.M, L / p.n_tiles, e, r0, r1);
+        if (lane == 0) {
+          s_tile[0] = ok ? e : -1;
+          s_tile[1] = r0;
+          s_tile[2] = r1;
+        }
       }
+      lds_barrier();
+      if (s_tile[0] < 0) break;  // uniform: only when offsets changed under the kernel
+      expert = (int)s_tile[0];
+      m0 = s_tile[1];
+      m_end = s_tile[2];
+      n0 = (L % p.n_tiles) * BN;
+      red = p.K;
+    }
+
+    // Operand regions of this tile (range-checked buffers).
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(nullptr, 0), rb = ra, rsa = ra, rsb = ra;
+    if constexpr (MODE == NT_BF16 || MODE == NN_BF16) {
+      ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + m0 * p.K, (m_end - m0) * p.K * 2);
+    } else if constexpr (MODE == TN_BF16) {
+      ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + (int64_t)lo * p.K, red * p.K * 2);
+    } else {
+      ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * (p.K / 2), (m_end - m0) * (p.K / 2));
+      rsa = make_rsrc(p.as + m0 * (p.K / 16), (m_end - m0) * (p.K / 16));
+    }
+    if constexpr (MODE == NT_BF16) {
+      const int64_t nv = p.N - n0 < BN ? p.N - n0 : BN;
+      rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + ((int64_t)expert * p.N + n0) * p.K, nv * p.K * 2);
+    } else if constexpr (MODE == NN_BF16) {
+      rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)expert * p.K * p.N, p.K * p.N * 2);
+    } else if constexpr (MODE == TN_BF16) {
+      rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
+    } else {
+      const int64_t nv = p.N - n0 < BN ? p.N - n0 : BN;
+      const int64_t brow = (int64_t)expert * p.N + n0;
+      rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
+      rsb = make_rsrc(p.bs + brow * (p.K / 16), nv * (p.K / 16));
+    }
+
+    auto load_step = [&](int64_t kt, int stage) {
+      const uint32_t st = smem_lds + stage * STAGE;
+      const int64_t k0 = kt * BK;
+      if constexpr (MODE == NT_BF16) {
+        KMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, p.K);
+        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K, k0, p.K);
+      } else if constexpr (MODE == NN_BF16) {
+        KMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, p.K);
+        MNMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+      } else if constexpr (MODE == TN_BF16) {
+        MNMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, m0, p.K);
+        MNMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+      } else {
+        NVCodeLoader<BM, NW>::load(st, wid, ra, p.K, k0);
+        NVCodeLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K, k0);
+        // Scales: 64 rows (4 bytes each) per load, A rows first.
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < SC_INSTR; ++i) {
+          const int idx = wid + NW * i;
+          const bool is_a = idx * 64 < BM;
+          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+          dma4(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 256, (uint32_t)(row * (p.K / 16) + k0 / 16));
+        }
+      }
+    };
+
+    f32x16_t acc[FM][FN];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (MODE == W4A4)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[i]),
-                                                                __builtin_bit_cast(f16x8_t, bf[j]), acc[i][j], 0, 0, 0);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nk = (red + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) load_step(s, s);
+
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      // This wave's loads for step kt are done once at most `ahead` later
+      // steps' loads are outstanding; the barrier then makes every wave's
+      // loads visible and frees the stage read in the previous step.
+      const int64_t ahead = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
+      if (ahead >= 2)
+        wait_vmcnt<(S >= 4 ? 2 : 0) * NDMA>();
+      else if (ahead == 1)
+        wait_vmcnt<(S >= 3 ? 1 : 0) * NDMA>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + S - 1 < nk) load_step(kt + S - 1, (int)((kt + S - 1) % S));
+
+      const uint8_t* st = smem + (int)(kt % S) * STAGE;
+      if constexpr (NV) {
+        NVFrag fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = frag_nv(st, st + A_BYTES + B_BYTES, wm * WTM + i * 32, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[j] = frag_nv(st + A_BYTES, st + A_BYTES + B_BYTES + BM * 4, wn * WTN + j * 32, lane);
+        // Operands of sub-step kk+1 are expanded while the MFMAs of kk run.
+        f16x8_t av[2][FM], bv[2][FN];
+        auto expand = [&](int kk, int buf) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) av[buf][i] = nv_expand(fa[i], kk);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bv[buf][j] = nv_expand(fb[j], kk);
+        };
+        expand(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          if (kk + 1 < BK / 16) expand(kk + 1, (kk + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+          // ~9 VALU per expanded fragment (scale decode, 4 converts, 4 multiplies)
+          if (kk + 1 < BK / 16) interleave_mfma_valu<FM * FN, (9 * (FM + FN) + FM * FN - 1) / (FM * FN)>();
+        }
+      } else {
+        // Fragments of sub-step kk+1 are read while the MFMAs of kk run.
+        bf16x8_t av[2][FM], bv[2][FN];
+        auto read_frags = [&](int kk, int buf) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            av[buf][i] = MODE == TN_BF16 ? frag_mnmajor<BM>(st, wm * WTM + i * 32, kk, lane)
+                                         : frag_kmajor(st, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            bv[buf][j] = MODE == NT_BF16 ? frag_kmajor(st + A_BYTES, wn * WTN + j * 32, kk, lane)
+                                         : frag_mnmajor<BN>(st + A_BYTES, wn * WTN + j * 32, kk, lane);
+        };
+        // LDS reads per sub-step: one per K-major fragment, two per MN-major one.
+        constexpr int NRD = FM * (MODE == TN_BF16 ? 2 : 1) + FN * (MODE == NT_BF16 ? 1 : 2);
+        read_frags(0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          if (kk + 1 < BK / 16) read_frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+          if (kk + 1 < BK / 16)
+            interleave_mfma_ds<FM * FN, NRD>();
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
-                                                                 __builtin_bit_cast(bf16x8_t, bf[j]), acc[i][j], 0, 0, 0);
-        }
-    }
-    if (kt + 1 < nk) commit(stage ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue.
-  float alpha = 1.0f;
-  if (MODE == W4A4) alpha = p.ag[0] * p.bg[expert];
-  const int64_t ldc = p.N;
-  float* C32 = reinterpret_cast<float*>(p.c);
-  uint16_t* C16 = reinterpret_cast<uint16_t*>(p.c);
-  const int64_t cbase = MODE == TN_BF16 ? (int64_t)expert * p.K * p.N : 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= m_end) continue;
-        const float v = acc[i][j][r] * alpha;
-        const int64_t idx = cbase + row * ldc + col;
-        if (p.c_f32) {
-          C32[idx] = p.accumulate ? C32[idx] + v : v;
-        } else {
-          C16[idx] = (uint16_t)f32_to_bf16_rne(v);
+            interleave_mfma_ds<FM * FN, 0>();
         }
       }
     }
+
+    // Epilogue.  Lane layout of a 32x32 MFMA result (probed on the device):
+    // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    float alpha = 1.0f;
+    if (MODE == W4A4) alpha = p.ag[0] * p.bg[expert];
+    const int64_t ldc = p.N;
+    float* C32 = reinterpret_cast<float*>(p.c);
+    uint16_t* C16 = reinterpret_cast<uint16_t*>(p.c);
+    const int64_t cbase = MODE == TN_BF16 ? (int64_t)expert * p.K * p.N : 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= m_end) continue;
+          const float v = acc[i][j][r] * alpha;
+          const int64_t idx = cbase + row * ldc + col;
+          if (p.c_f32) {
+            C32[idx] = p.accumulate ? C32[idx] + v : v;
+          } else {
+            C16[idx] = (uint16_t)f32_to_bf16_rne(v);
+          }
+        }
+      }
+  }
 }
 
-int launch(int mode, const Params& p0, hipStream_t st) {
+// Resident workgroups per CU of one kernel instantiation (cached; the same on
+// every gfx950 device).
+template <int MODE, int BM, int BN, int WM, int WN, int S>
+int resident_per_cu() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel<MODE, BM, BN, WM, WN, S>, WM * WN * 64, 0) !=
+          hipSuccess ||
+      occ < 1)
+    occ = 1;
+  cached = occ;
+  return occ;
+}
+
+template <int MODE, int BM, int BN, int WM, int WN, int S>
+int launch_cfg(const Params& p0, hipStream_t st) {
   Params p = p0;
   p.n_tiles = (int)cdiv(p.N, BN);
-  int64_t blocks;
-  if (mode == TN_BF16) {
+  int64_t upper;
+  if (MODE == TN_BF16) {
     p.k_tiles_tn = (int)cdiv(p.K, BM);
-    blocks = (int64_t)p.E * p.k_tiles_tn * p.n_tiles;
+    upper = (int64_t)p.E * p.k_tiles_tn * p.n_tiles;
   } else {
-    blocks = (cdiv(p.M, BM) + p.E) * p.n_tiles;
+    upper = (cdiv(p.M, BM) + p.E) * p.n_tiles;
   }
-  if (blocks <= 0) return NVFP4MOE_OK;
-  if (blocks > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
-  switch (mode) {
-    case NT_BF16: gemm_kernel<NT_BF16><<<(unsigned)blocks, NT, 0, st>>>(p); break;
-    case NN_BF16: gemm_kernel<NN_BF16><<<(unsigned)blocks, NT, 0, st>>>(p); break;
-    case TN_BF16: gemm_kernel<TN_BF16><<<(unsigned)blocks, NT, 0, st>>>(p); break;
-    default: gemm_kernel<W4A4><<<(unsigned)blocks, NT, 0, st>>>(p); break;
-  }
+  if (upper <= 0) return NVFP4MOE_OK;
+  if (upper > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  int64_t grid = (int64_t)device_cu_count() * resident_per_cu<MODE, BM, BN, WM, WN, S>();
+  if (grid > upper) grid = upper;
+  grid = cdiv(grid, 8) * 8;  // whole XCD rounds
+  gemm_kernel<MODE, BM, BN, WM, WN, S><<<(unsigned)grid, WM * WN * 64, 0, st>>>(p);
   return launch_status();
+}
+
+// Tile configurations: (BM, BN, waves along M, waves along N, LDS stages).
+// A build for tuning sweeps may force one with -DNVFP4MOE_GEMM_FORCE_CONFIG=<i>
+// (then only that one is compiled).
+#define NVFP4MOE_GEMM_CONFIGS(X) \
+  X(0, 256, 256, 2, 4, 2)        \
+  X(1, 256, 256, 4, 2, 2)        \
+  X(2, 256, 128, 2, 2, 3)        \
+  X(3, 128, 256, 2, 2, 3)        \
+  X(4, 128, 128, 2, 2, 4)        \
+  X(5, 256, 256, 2, 4, 4)        \
+  X(6, 256, 256, 4, 2, 4)        \
+  X(7, 256, 256, 2, 2, 2)        \
+  X(8, 256, 256, 2, 2, 4)
+
+#ifdef NVFP4MOE_GEMM_FORCE_CONFIG
+constexpr int kForcedConfig = NVFP4MOE_GEMM_FORCE_CONFIG;
+#else
+constexpr int kForcedConfig = -1;
+#endif
+
+// Whether a configuration is valid for a layout: LDS within the 160 KiB of
+// a gfx950 CU, and whole loads per wave for NVFP4 tiles.
+constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s) {
+  return s * (mode == W4A4 ? (bm + bn) * 36 : (bm + bn) * BK * 2) <= 160 * 1024 &&
+         (mode != W4A4 || (bm % (32 * wm * wn) == 0 && bn % (32 * wm * wn) == 0 && (bm + bn) % (64 * wm * wn) == 0));
+}
+
+template <int MODE>
+int launch_mode(int cfg, const Params& p, hipStream_t st) {
+  switch (cfg) {
+#define NVFP4MOE_CASE(I, BM_, BN_, WM_, WN_, S_)                                               \
+  case I:                                                                                      \
+    if constexpr ((kForcedConfig < 0 || kForcedConfig == I) && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_)) \
+      return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_>(p, st);                                  \
+    break;
+    NVFP4MOE_GEMM_CONFIGS(NVFP4MOE_CASE)
+#undef NVFP4MOE_CASE
+    default: break;
+  }
+  return NVFP4MOE_ESHAPE;
+}
+
+// Tile configuration per layout and shape.
+int pick_config(int mode, const Params& p) {
+  (void)p;
+  if (kForcedConfig >= 0) return kForcedConfig;
+  // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
+  // 256 x 256 tiles on 8 waves; W4A4 with 4 LDS stages (its tiles are small).
+  switch (mode) {
+    case W4A4: return 6;
+    default: return 0;
+  }
+}
+
+int launch(int mode, const Params& p, hipStream_t st) {
+  const int cfg = pick_config(mode, p);
+  switch (mode) {
+    case NT_BF16: return launch_mode<NT_BF16>(cfg, p, st);
+    case NN_BF16: return launch_mode<NN_BF16>(cfg, p, st);
+    case TN_BF16: return launch_mode<TN_BF16>(cfg, p, st);
+    default: return launch_mode<W4A4>(cfg, p, st);
+  }
 }
 
 }  // namespace
@@ -414,8 +704,8 @@ extern "C" int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const f
   if (epilogue != NVFP4MOE_EPI_NONE) return NVFP4MOE_EINVAL;
   if (!expert_offsets || !a_g || !b_g) return NVFP4MOE_EINVAL;
   if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || !c)) return NVFP4MOE_EINVAL;
-  if (K % 32 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
-  if (M_total > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 2) || !aligned(b_s, 2) ||
+  if (K % 64 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (M_total > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
       !aligned(c, 16))
     return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
@@ -453,6 +743,10 @@ extern "C" int grouped_gemm_bf16(int layout, const void* a, const void* b, const
   if (has_out && (!c || (M_total > 0 && (!a || !b)))) return NVFP4MOE_EINVAL;
   if (K % 32 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
   if (M_total > 0x7FFFFFFFLL || !aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return NVFP4MOE_ESHAPE;
+  // Buffer offsets are 32-bit: one expert's operand must stay below 2 GiB.
+  if (layout == NVFP4MOE_NN && K * N * 2 >= (1LL << 31)) return NVFP4MOE_ESHAPE;
+  if (layout == NVFP4MOE_TN && (M_total * K * 2 >= (1LL << 31) || M_total * N * 2 >= (1LL << 31)))
+    return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   if (!has_out) return NVFP4MOE_OK;

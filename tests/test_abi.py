@@ -111,7 +111,9 @@ def test_gemm_validation(lib):
     bad = list(args); bad[13] = 1
     assert g(*bad) == -1                       # epilogue
     bad = list(args); bad[10] = 48
-    assert g(*bad) == -2                       # K % 32
+    assert g(*bad) == -2                       # K % 64
+    bad = list(args); bad[10] = 96
+    assert g(*bad) == -2                       # K % 64 (a multiple of 32 is not enough)
     bad = list(args); bad[9] = 40
     assert g(*bad) == -2                       # N % 32
     bad = list(args); bad[6] = None

@@ -33,9 +33,10 @@ def _gpu_w4a4(a, b, offs, out_dtype):
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("M,N,K,counts", [
-    (300, 160, 96, [0, 1, 200, 0, 99]),       # empty experts, a 1-row expert, M and N tails, K = 1.5 tiles
+    (300, 160, 192, [0, 1, 200, 0, 99]),      # empty experts, a 1-row expert, M and N tails, K = 3 steps
     (257, 256, 256, [257]),                   # one expert, one row past two full tiles
-    (640, 96, 32, [128, 128, 0, 384]),        # exact tiles, K = one half-tile
+    (640, 96, 64, [128, 128, 0, 384]),        # exact tiles, K = one step
+    (770, 288, 128, [256, 1, 257, 256]),      # 256-row tile boundaries, N tail past 256
 ])
 def test_w4a4_small(M, N, K, counts, out_dtype):
     require_gpu()
@@ -130,14 +131,16 @@ def _bf(rng, shape, scale=1.0):
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_bf16_small(layout, out_dtype):
+@pytest.mark.parametrize("counts,K,N", [
+    ([0, 1, 200, 0, 70], 96, 160),     # empty and 1-row experts, K half a step past one
+    ([300, 0, 257, 3], 320, 288),      # several 256-wide tiles with tails in M, N and K
+])
+def test_bf16_small(layout, out_dtype, counts, K, N):
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
-    rng = np.random.default_rng(11)
-    counts = [0, 1, 200, 0, 70]
+    rng = np.random.default_rng(11 + K)
     E = len(counts)
     M = sum(counts)
-    K, N = 96, 160
     offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     a = _bf(rng, (M, K))
     b = _bf(rng, (E, N, K) if layout == "NT" else (E, K, N) if layout == "NN" else (M, N), 0.05)
@@ -148,7 +151,8 @@ def test_bf16_small(layout, out_dtype):
     ref, ab = gemm.grouped_gemm_bf16(layout, a, b, offs)
     assert_gemm_close(to_np(c), ref, ab, bf16_out=out_dtype == torch.bfloat16, what=layout)
     if layout == "TN":
-        assert (to_np(c)[0] == 0).all() and (to_np(c)[3] == 0).all()
+        for e in np.flatnonzero(np.asarray(counts) == 0):
+            assert (to_np(c)[e] == 0).all(), "empty expert %d" % e
 
 
 def test_bf16_tn_accumulate():

@@ -29,7 +29,7 @@ def _run(T, k, E, D, F, s=1.1, seed=0):
     return d, meta, buf, wq_gu, wq_dn
 
 
-@pytest.mark.parametrize("T,k,E,D,F", [(256, 8, 16, 256, 128), (100, 2, 5, 128, 96)])
+@pytest.mark.parametrize("T,k,E,D,F", [(256, 8, 16, 256, 128), (100, 2, 5, 128, 192)])
 def test_layer_stagewise(T, k, E, D, F):
     require_gpu()
     d, meta, buf, wq_gu, wq_dn = _run(T, k, E, D, F)
