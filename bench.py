@@ -9,10 +9,21 @@ Qwen3-30B-A3B-shaped full update at 8192 tokens (d_model 2048, 128 experts,
 top-8, FFN 768), synthetic seeded inputs, inputs resident in HBM.  Expert
 weight quantization runs once per optimizer step and is timed separately.
 
-Prints one JSON line (rank 0, N = 1).
+Per-op times are HIP events recorded inside the timed steps, on the stream
+the library launches on (torch's current stream).  Beside the step, the
+BF16 grouped GEMM runs on the gate+up shape of the W4A4 one (the baseline
+the W4A4 GEMM is compared with), and the CPU oracle runs on a bounded
+sample of the same workload.
+
+Prints one JSON line (N = 1).
+
+    python bench.py [--steps K] [--warmup W] [--workload moe_8k_update]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # HBM traffic summary
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -22,18 +33,63 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.0   # dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_moe_8k_update.txt")
+CALIB_BYTES = 1 << 30       # the plain copy that calibrates the traffic counters
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def source_digest():
+    """sha256 over the HIP sources: recorded with PMC traffic so that a
+    changed kernel invalidates it."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "nvfp4_quantized_moe_token_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def gemm_flops(R, D, F):
     """Algorithmic FLOPs of the two expert projections for R routed rows."""
     return 2.0 * R * (2 * F) * D, 2.0 * R * D * F
+
+
+def op_work(name, T, k, E, D, F):
+    """(flops, algorithmic HBM bytes) of one launch of each op of the step:
+    every operand read once and every result written once."""
+    R = T * k
+    f1, f2 = gemm_flops(R, D, F)
+    nv = lambda rows, cols: rows * cols * (0.5 + 1.0 / 16)  # noqa: E731  NVFP4 bytes per element
+    table = {
+        "moe_permute": (0.0, T * D * 2 + R * D * 2 + R * 4 * 3),
+        "quantize_x": (0.0, R * D * 2 + nv(R, D)),
+        "w4a4_gate_up": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
+        "silu_gate_fwd": (0.0, R * 2 * F * 2 + R * F * 2),
+        "quantize_h": (0.0, R * F * 2 + nv(R, F)),
+        "w4a4_down": (f2, nv(R, F) + nv(E * D, F) + R * D * 2),
+        "unpermute": (0.0, R * D * 2 + T * D * 2 + R * 4),
+        "gather_dy": (0.0, T * D * 2 + R * D * 2 + R * 4),
+        "bf16_nn_down": (f2, R * D * 2 + E * D * F * 2 + R * F * 2),
+        "bf16_tn_down": (f2, R * D * 2 + R * F * 2 + E * D * F * 4),
+        "silu_gate_bwd": (0.0, R * 2 * F * 2 + R * F * 2 + R * 2 * F * 2),
+        "bf16_nn_gate_up": (f1, R * 2 * F * 2 + E * 2 * F * D * 2 + R * D * 2),
+        "bf16_tn_gate_up": (f1, R * 2 * F * 2 + R * D * 2 + E * 2 * F * D * 4),
+        "unpermute_dx": (0.0, R * D * 2 + T * D * 2),
+        "bf16_nt_gate_up_baseline": (f1, R * D * 2 + E * 2 * F * D * 2 + R * 2 * F * 2),
+    }
+    return table[name]
+
+
+# Ops of the full-update step, in launch order (the PMC summary's rows).
+STEP_OPS = ["moe_permute", "quantize_x", "w4a4_gate_up", "silu_gate_fwd", "quantize_h", "w4a4_down", "unpermute",
+            "gather_dy", "bf16_nn_down", "bf16_tn_down", "silu_gate_bwd", "bf16_nn_gate_up", "bf16_tn_gate_up",
+            "unpermute_dx"]
+MARKER = "FillFunctor<int>"  # a one-element int fill between ops in --pmc-run
 
 
 def build_inputs(cfg, torch, dev):
@@ -49,98 +105,49 @@ def build_inputs(cfg, torch, dev):
     return out
 
 
-class Timeline:
-    """Per-op HIP events on the current stream (the stream the ops launch on)."""
+def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
+    """The ops of one step, in launch order, as (name, thunk)."""
+    E, k, T = buf.E, buf.k, buf.T
 
-    def __init__(self, torch, enabled):
-        self.torch, self.enabled, self.ev = torch, enabled, []
+    def permute():
+        meta_box["m"] = ops.moe_permute(inp["ids"], E, x=inp["x"], x_perm=buf.x_perm, amax_out=buf.amax[0:1],
+                                        workspace=buf.ws)
 
-    def mark(self, name):
-        if not self.enabled:
-            return None
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.ev.append((name, e))
-        return e
-
-    def durations(self):
-        out = {}
-        for (n0, e0), (n1, e1) in zip(self.ev[:-1], self.ev[1:]):
-            if n0 == "__end__":
-                continue
-            out.setdefault(n0, []).append(e0.elapsed_time(e1))
-        return out
-
-
-def run_step(torch, ops, inp, wq_gu, wq_dn, buf, tl, backward=True):
-    E = buf.E
-    tl.mark("moe_permute")
-    meta = ops.moe_permute(inp["ids"], E, x=inp["x"], x_perm=buf.x_perm, amax_out=buf.amax[0:1], workspace=buf.ws)
-    tl.mark("quantize_x")
-    ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s, gscale=buf.a1_g)
-    tl.mark("w4a4_gate_up")
-    ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], meta["offsets"],
-                          out=buf.y1)
-    tl.mark("silu_gate_fwd")
-    ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])
-    tl.mark("quantize_h")
-    ops.nvfp4_quantize(buf.h, amax_in=buf.amax[1:2], q=buf.a2_q, scales=buf.a2_s, gscale=buf.a2_g)
-    tl.mark("w4a4_down")
-    ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"], wq_dn["g"], meta["offsets"],
-                          out=buf.y2)
-    tl.mark("unpermute")
-    ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=inp["tw"], out=buf.out)
+    m = lambda: meta_box["m"]  # noqa: E731
+    seq = [
+        ("moe_permute", permute),
+        ("quantize_x", lambda: ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
+                                                  gscale=buf.a1_g)),
+        ("w4a4_gate_up", lambda: ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"],
+                                                       wq_gu["g"], m()["offsets"], out=buf.y1)),
+        ("silu_gate_fwd", lambda: ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])),
+        ("quantize_h", lambda: ops.nvfp4_quantize(buf.h, amax_in=buf.amax[1:2], q=buf.a2_q, scales=buf.a2_s,
+                                                  gscale=buf.a2_g)),
+        ("w4a4_down", lambda: ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"],
+                                                    wq_dn["g"], m()["offsets"], out=buf.y2)),
+        ("unpermute", lambda: ops.moe_unpermute(buf.y2, m()["dest"], T, k, topk_w=inp["tw"], out=buf.out)),
+    ]
     if backward:
-        off = meta["offsets"]
-        tl.mark("gather_dy")
-        ops.moe_gather(inp["dy"], meta["src"], buf.k, topk_w=inp["tw"], out=buf.dy2)
-        tl.mark("bf16_nn_down")
-        ops.grouped_gemm_bf16(ops.NN, buf.dy2, inp["w_dn"], off, out=buf.dh)
-        tl.mark("bf16_tn_down")
-        ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, off, out=buf.dw_dn)
-        tl.mark("silu_gate_bwd")
-        ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
-        tl.mark("bf16_nn_gate_up")
-        ops.grouped_gemm_bf16(ops.NN, buf.dy1, inp["w_gu"], off, out=buf.dx_perm)
-        tl.mark("bf16_tn_gate_up")
-        ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, off, out=buf.dw_gu)
-        tl.mark("unpermute_dx")
-        ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
-    tl.mark("__end__")
-    return meta
+        seq += [
+            ("gather_dy", lambda: ops.moe_gather(inp["dy"], m()["src"], k, topk_w=inp["tw"], out=buf.dy2)),
+            ("bf16_nn_down", lambda: ops.grouped_gemm_bf16(ops.NN, buf.dy2, inp["w_dn"], m()["offsets"],
+                                                           out=buf.dh)),
+            ("bf16_tn_down", lambda: ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, m()["offsets"], out=buf.dw_dn)),
+            ("silu_gate_bwd", lambda: ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)),
+            ("bf16_nn_gate_up", lambda: ops.grouped_gemm_bf16(ops.NN, buf.dy1, inp["w_gu"], m()["offsets"],
+                                                              out=buf.dx_perm)),
+            ("bf16_tn_gate_up", lambda: ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, m()["offsets"],
+                                                              out=buf.dw_gu)),
+            ("unpermute_dx", lambda: ops.moe_unpermute(buf.dx_perm, m()["dest"], T, k, topk_w=None, out=buf.dx)),
+        ]
+    return seq
 
 
-def kernel_work(name, T, k, D, F):
-    """(flops, algorithmic bytes) of one launch of each op of the step."""
-    R = T * k
-    f1, f2 = gemm_flops(R, D, F)
-    nv = lambda rows, cols: rows * cols * (0.5 + 1.0 / 16)  # noqa: E731  NVFP4 bytes
-    table = {
-        # metadata + gather (bf16 rows read once per assignment, written once)
-        "moe_permute": (0.0, R * D * 2 * 2 + R * 4 * 3),
-        "quantize_x": (0.0, R * D * 2 + nv(R, D)),
-        "w4a4_gate_up": (f1, nv(R, D) + nv(128 * 2 * F, D) + R * 2 * F * 2),
-        "silu_gate_fwd": (0.0, R * 2 * F * 2 + R * F * 2),
-        "quantize_h": (0.0, R * F * 2 + nv(R, F)),
-        "w4a4_down": (f2, nv(R, F) + nv(128 * D, F) + R * D * 2),
-        "unpermute": (0.0, R * D * 2 + T * D * 2),
-        "gather_dy": (0.0, R * D * 2 + R * D * 2),
-        "bf16_nn_down": (f2, R * D * 2 + 128 * D * F * 2 + R * F * 2),
-        "bf16_tn_down": (f2, R * D * 2 + R * F * 2 + 128 * D * F * 4),
-        "silu_gate_bwd": (0.0, R * 2 * F * 2 + R * F * 2 + R * 2 * F * 2),
-        "bf16_nn_gate_up": (f1, R * 2 * F * 2 + 128 * 2 * F * D * 2 + R * D * 2),
-        "bf16_tn_gate_up": (f1, R * 2 * F * 2 + R * D * 2 + 128 * 2 * F * D * 4),
-        "unpermute_dx": (0.0, R * D * 2 + T * D * 2),
-    }
-    return table[name]
-
-
-def cpu_baseline(seconds_hint=True):
+def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the same workload:
-    512 tokens routed top-8 over 8 experts (every expert gets 512 rows, the
+    4096 tokens routed top-8 over 64 experts (512 rows per expert, the
     per-expert GEMM shape of the full update), forward + BF16 backward.
     Expert weight quantization happens before the timer, as on the GPU."""
-    import numpy as np
     import oracle
     import workloads
     try:
@@ -148,7 +155,7 @@ def cpu_baseline(seconds_hint=True):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
-    T, k, E, D, F = 512, 8, 8, 2048, 768
+    T, k, E, D, F = 4096, 8, 64, 2048, 768
     d = workloads.moe(T, 0.0, with_dy=True, E=E, k=k, D=D, F=F, name="cpu_sample")
     wq_gu = oracle.layer.quantize_weights(d["w_gu"])
     wq_dn = oracle.layer.quantize_weights(d["w_dn"])
@@ -159,8 +166,67 @@ def cpu_baseline(seconds_hint=True):
     f1, f2 = gemm_flops(T * k, D, F)
     flops = 3 * (f1 + f2)
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample="forward+backward of 512 tokens x top-8 over 8 experts (512 rows per expert), "
-                       "d_model 2048, FFN 768; %.1f s" % dt, seconds=round(dt, 2))
+                sample="forward+backward of 4096 tokens x top-8 over 64 experts (512 rows per expert), "
+                       "d_model 2048, FFN 768, fp64 GEMMs on %d BLAS threads; %.1f s" % (cores, dt),
+                seconds=round(dt, 2), tokens_per_s=round(T / dt, 1))
+
+
+def load_traffic():
+    """Per-op HBM bytes from the committed PMC summary, or {} when absent or
+    taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    digest, out = None, {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 2 and parts[0] == "sources":
+                digest = parts[1]
+            elif len(parts) >= 7 and parts[0] == "op":
+                out[parts[1]] = dict(fetch=float(parts[3]), write=float(parts[5]))
+    return out if digest == source_digest() else {}
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs of `bench.py --pmc-run` (FETCH_SIZE,
+    then WRITE_SIZE; counters in KiB per dispatch) into per-op HBM bytes of
+    the last step, scaled by what the counters read for a plain 1 GiB copy.
+    In that run each op is preceded by a one-element int fill (the marker),
+    so an op's dispatches are the ones between two markers."""
+    import csv
+
+    def read(d, counter):
+        rows = {}
+        for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        i = int(r["Dispatch_Id"])
+                        v = rows.get(i, (r["Kernel_Name"], 0.0))[1] + float(r["Counter_Value"])
+                        rows[i] = (r["Kernel_Name"], v)
+        return [rows[i] for i in sorted(rows)]
+
+    def per_op(rows):
+        cal = rows[-1][1] * 1024.0                      # the calibration copy comes last
+        marks = [i for i, (n, _) in enumerate(rows) if MARKER in n]
+        marks = marks[-(len(STEP_OPS) + 1):]            # the last step's markers
+        out = []
+        for j, name in enumerate(STEP_OPS):
+            seg = rows[marks[j] + 1:marks[j + 1]]
+            out.append((name, sum(v for _, v in seg) * 1024.0, sorted({n.split("(")[0] for n, _ in seg})))
+        return cal, out
+
+    cal_f, fetch = per_op(read(fetch_dir, "FETCH_SIZE"))
+    cal_w, write = per_op(read(write_dir, "WRITE_SIZE"))
+    sf, sw = CALIB_BYTES / cal_f, CALIB_BYTES / cal_w
+    lines = ["# HBM traffic per op of one moe_8k_update step, from two rocprofv3 --pmc runs of",
+             "# `bench.py --pmc-run` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the op's",
+             "# kernels) scaled by the counters' reading of a plain %d-byte device copy:" % CALIB_BYTES,
+             "# fetch x%.4f, write x%.4f.  Bytes per launch; 'sources' fingerprints the HIP sources." % (sf, sw),
+             "sources %s" % source_digest()]
+    for (name, fb, kn), (_, wb, _) in zip(fetch, write):
+        lines.append("op %s fetch %.0f write %.0f kernels %s" % (name, fb * sf, wb * sw, ";".join(kn)))
+    print("\n".join(lines))
 
 
 def main():
@@ -168,11 +234,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe_8k_update",
-                    choices=["moe_8k_update", "moe_4k", "moe_16k_skew"])
+    ap.add_argument("--workload", default="moe_8k_update", choices=["moe_8k_update", "moe_4k", "moe_16k_skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-events", action="store_true", help="skip per-op HIP events (for profiler runs)")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short run for rocprofv3 --pmc: steps only, then a 1 GiB calibration copy")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
               "(sharding is described, not built); use --gpus 1", file=sys.stderr)
@@ -201,37 +271,77 @@ def main():
     wq_bytes = (E * 2 * F * D + E * D * F) * (2 + 0.5625)
 
     buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=backward)
-    off_tl = Timeline(torch, False)
+    meta_box = {}
+    seq = step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward)
     log("warmup", args.warmup)
     for _ in range(args.warmup):
-        run_step(torch, ops, inp, wq_gu, wq_dn, buf, off_tl, backward)
+        for _, fn in seq:
+            fn()
     torch.cuda.synchronize()
 
+    if args.pmc_run:
+        mark = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(args.steps):
+            for i, (_, fn) in enumerate(seq):
+                mark.fill_(i)
+                fn()
+            mark.fill_(len(seq))
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc run done")
+        return
+
+    # Timed steps; every op is bracketed by HIP events on the launch stream.
     log("timed steps", args.steps)
+    marks = []
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(torch, ops, inp, wq_gu, wq_dn, buf, off_tl, backward)
+        evs = []
+        for name, fn in seq:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            evs.append((name, e))
+            fn()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        evs.append(("__end__", e))
+        marks.append(evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-
-    # Per-op durations from HIP events in separate instrumented steps.
     per_op = {}
-    if not args.no_events:
-        tl = Timeline(torch, True)
-        for _ in range(max(3, min(args.steps, 10))):
-            run_step(torch, ops, inp, wq_gu, wq_dn, buf, tl, backward)
-        torch.cuda.synchronize()
-        for name, v in tl.durations().items():
-            per_op[name] = sum(v) / len(v)
+    for evs in marks:
+        for (n0, e0), (_, e1) in zip(evs[:-1], evs[1:]):
+            per_op.setdefault(n0, []).append(e0.elapsed_time(e1))
+    per_op = {n: sum(v) / len(v) for n, v in per_op.items()}
+
+    # BF16 grouped GEMM on the gate+up shape of the W4A4 GEMM (same routing).
+    offs = meta_box["m"]["offsets"]
+    y1b = torch.empty_like(buf.y1)
+    base = lambda: ops.grouped_gemm_bf16(ops.NT, buf.x_perm, inp["w_gu"], offs, out=y1b)  # noqa: E731
+    for _ in range(3):
+        base()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nrep = max(5, min(args.steps, 20))
+    b0.record()
+    for _ in range(nrep):
+        base()
+    b1.record()
+    torch.cuda.synchronize()
+    per_op_extra = {"bf16_nt_gate_up_baseline": b0.elapsed_time(b1) / nrep}
 
     R = T * k
     f1, f2 = gemm_flops(R, D, F)
     step_flops = (f1 + f2) * (3 if backward else 1)
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+    traffic = load_traffic()
     kernels = {}
-    for name, ms in per_op.items():
-        fl, by = kernel_work(name, T, k, D, F)
+    for name, ms in list(per_op.items()) + list(per_op_extra.items()):
+        fl, by = op_work(name, T, k, E, D, F)
         ent = {"ms": round(ms, 4)}
         if fl:
             ent["tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
@@ -240,26 +350,33 @@ def main():
                 ent["frac_fp4_mfma_peak"] = round(ent["tflops"] / PEAK_FP4_TFLOPS, 4)
         ent["gbs"] = round(by / (ms * 1e-3) / 1e9, 1)
         ent["frac_hbm_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        if name in traffic:
+            ent["hbm_bytes_measured"] = traffic[name]["fetch"] + traffic[name]["write"]
+            ent["hbm_bytes_algorithmic"] = by
         kernels[name] = ent
 
-    roofline = None
-    if per_op:
-        dom = max(per_op, key=per_op.get)
-        fl, by = kernel_work(dom, T, k, D, F)
+    def roofline_of(name):
+        ms = per_op[name]
+        fl, by = op_work(name, T, k, E, D, F)
+        tr = traffic.get(name)
+        tr_bytes = None if tr is None else round(tr["fetch"] + tr["write"])
         if fl:
-            ach = fl / (per_op[dom] * 1e-3) / 1e12
-            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
-        else:
-            ach = by / (per_op[dom] * 1e-3) / 1e9
-            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+            ach = fl / (ms * 1e-3) / 1e12
+            return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": tr_bytes,
+                    "algorithmic_bytes": by, "ms": round(ms, 4)}
+        ach = by / (ms * 1e-3) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": tr_bytes, "ms": round(ms, 4)}
 
+    dominant = max(per_op, key=per_op.get)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline()
 
+    w4 = kernels.get("w4a4_gate_up", {})
+    bl = kernels["bf16_nt_gate_up_baseline"]
     res = {
         "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
         "value": round(tflops, 2),
@@ -271,21 +388,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-w4a4 fwd (fp16 MFMA, fp32 acc) + bf16 bwd" if backward else "nvfp4-w4a4 (fp16 MFMA, fp32 acc)",
+        "dtype": "fp16+bf16 mfma, fp32 acc" if backward else "fp16 mfma, fp32 acc",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "d_model": D, "experts": E, "top_k": k, "ffn": F,
                    "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "step_gflop": round(step_flops / 1e9, 1),
-        "roofline": roofline,
+        "roofline": roofline_of(dominant),
+        "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
+                      "bf16_same_shape_tflops": bl.get("tflops"),
+                      "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3) if w4 else None},
+        "quantize": roofline_of("quantize_x"),
         "cpu_baseline": cpu,
         "kernels": kernels,
         "weight_quantize": {"ms": round(wq_ms, 4), "gbs": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
     }
-    if "w4a4_gate_up" in kernels:
-        res["w4a4_gemm_tflops"] = kernels["w4a4_gate_up"].get("tflops")
-    if "quantize_x" in kernels:
-        res["quantize_gbs"] = kernels["quantize_x"]["gbs"]
     print(json.dumps(res), flush=True)
 
 

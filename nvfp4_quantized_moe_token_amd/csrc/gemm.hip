@@ -53,7 +53,8 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-constexpr int BK = 64;                       // reduction elements per pipeline step
+constexpr int BK = 64;                       // reduction elements per MFMA group / bf16 stage
+constexpr int NV_KS = 256;                   // reduction elements per NVFP4 stage
 constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
@@ -84,6 +85,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most `ahead` steps of NDMA loads each are outstanding
+// (ahead in [0, MAX], wave-uniform).
+template <int MAX, int NDMA>
+__device__ __forceinline__ void wait_steps_ahead(int ahead) {
+  if constexpr (MAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= MAX)
+      wait_vmcnt<MAX * NDMA>();
+    else
+      wait_steps_ahead<MAX - 1, NDMA>(ahead);
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRawBufferWord3);
@@ -96,20 +111,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, ui
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-
 // K-major bf16 tile: chunk c (8 elements) of row r at byte r*128 + 16*(c ^ kswz(r)).
 __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
 // MN-major bf16 tile: chunk c of reduction row k at byte k*rowbytes + 16*(c ^ mswz(k)).
 // Any 4 consecutive rows k = 4i..4i+3 then put a transposed read's 32- and
 // 64-byte row segments on disjoint banks.
 __device__ __forceinline__ int mswz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }  // {0, 6, 10, 12}
-// NVFP4 code tile: half h (16 bytes) of row r at byte r*32 + 16*(h ^ nswz(r)).
-__device__ __forceinline__ int nswz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-
 // Clamped [lo, hi) row range of expert e.
 __device__ __forceinline__ void expert_range(const int32_t* __restrict__ off, int e, int64_t M, int& lo, int& hi) {
   lo = off[e];
@@ -226,25 +233,6 @@ struct MNMajorLoader {
   }
 };
 
-// NVFP4 codes of ROWS rows x 64 k (32 B per row); offsets relative to the
-// codes region (row pitch K/2 bytes).
-template <int ROWS, int NW>
-struct NVCodeLoader {
-  static_assert(ROWS % (32 * NW) == 0, "NVFP4 tile: rows per wave");
-  static constexpr int N_INSTR = ROWS / (32 * NW);
-  __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t K,
-                                              int64_t k0) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < N_INSTR; ++i) {
-      const int idx = wid + NW * i;
-      const int row = idx * 32 + (lane >> 1);
-      const int h = (lane & 1) ^ nswz(row);
-      dma16(r, lds + idx * 1024, (uint32_t)(row * (K / 2) + k0 / 2 + h * 16));
-    }
-  }
-};
-
 // ---- fragment readers (LDS -> MFMA operands) ----
 
 // K-major bf16 fragment: rows base + (lane % 32), k = 16*kk + 8*(lane/32) + 0..7.
@@ -276,17 +264,19 @@ __device__ __forceinline__ bf16x8_t frag_mnmajor(const uint8_t* tile, int base, 
   return out;
 }
 
-// NVFP4 fragment: the lane's 32 codes (row base + lane % 32, k in
-// [32h, 32h+32), h = lane / 32) and its two block scales.
+// NVFP4 fragment of 64-element chunk c of a stage: the lane's 32 codes (row
+// base + lane % 32, k in [64c + 32h, 64c + 32h + 32), h = lane / 32) and its
+// two block scales.  Code rows are 128 bytes (16-byte units swizzled like
+// the K-major bf16 tile), scale rows 16 bytes.
 struct NVFrag {
   uint4 q;
-  uint32_t s;  // low byte: block 2h, next byte: block 2h+1
+  uint32_t s;  // low byte: block 4c+2h, next byte: block 4c+2h+1
 };
-__device__ __forceinline__ NVFrag frag_nv(const uint8_t* codes, const uint8_t* scales, int base, int lane) {
+__device__ __forceinline__ NVFrag frag_nv(const uint8_t* codes, const uint8_t* scales, int base, int c, int lane) {
   const int row = base + (lane & 31), h = lane >> 5;
   NVFrag f;
-  f.q = *reinterpret_cast<const uint4*>(codes + row * 32 + ((h ^ nswz(row)) << 4));
-  f.s = *reinterpret_cast<const uint16_t*>(scales + row * 4 + h * 2);
+  f.q = *reinterpret_cast<const uint4*>(codes + row * 128 + (((2 * c + h) ^ kswz(row)) << 4));
+  f.s = *reinterpret_cast<const uint16_t*>(scales + row * 16 + 4 * c + 2 * h);
   return f;
 }
 __device__ __forceinline__ uint32_t nv_pair(uint32_t w, f16x2_t sc, int sel) {
@@ -338,6 +328,21 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+// Wave-wide loads per pipeline step of one operand tile (A side or B side).
+template <int MODE, bool A_SIDE, int ROWS, int NW>
+constexpr int loads_per_wave() {
+  if constexpr (MODE == W4A4)
+    return KMajorLoader<ROWS, NW>::N_INSTR;
+  else if constexpr ((A_SIDE && MODE == TN_BF16) || (!A_SIDE && MODE != NT_BF16))
+    return MNMajorLoader<ROWS, NW>::N_INSTR;
+  else
+    return KMajorLoader<ROWS, NW>::N_INSTR;
+}
+
+template <int N>
+struct IntConst {
+  static constexpr int value = N;
+};
 // ---- the kernel ----
 
 template <int MODE, int BM, int BN, int WM, int WN, int S>
@@ -346,21 +351,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");
   constexpr bool NV = MODE == W4A4;
-  constexpr int A_BYTES = NV ? BM * 32 : BM * BK * 2;
-  constexpr int B_BYTES = NV ? BN * 32 : BN * BK * 2;
-  constexpr int SC_BYTES = NV ? (BM + BN) * 4 : 0;  // A scales then B scales
+  // Reduction elements per pipeline stage: 64 for bf16 (128-byte rows);
+  // 256 for NVFP4, so that each row brings a whole 128-byte line of codes
+  // and 16 bytes of scales per stage.
+  constexpr int KS = NV ? NV_KS : BK;
+  constexpr int A_BYTES = BM * 128;
+  constexpr int B_BYTES = BN * 128;
+  constexpr int SC_BYTES = NV ? (BM + BN) * 16 : 0;  // A scales then B scales
   constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   static_assert(!NV || (BM + BN) % (64 * NW) == 0, "NVFP4 scales: rows per wave");
   constexpr int SC_INSTR = NV ? (BM + BN) / (64 * NW) : 0;
   // Per-wave loads per step, for the vmcnt waits.
-  constexpr int A_INSTR = NV ? NVCodeLoader<BM, NW>::N_INSTR
-                        : MODE == TN_BF16 ? MNMajorLoader<BM, NW>::N_INSTR
-                                          : KMajorLoader<BM, NW>::N_INSTR;
-  constexpr int B_INSTR = NV ? NVCodeLoader<BN, NW>::N_INSTR
-                        : MODE == NT_BF16 ? KMajorLoader<BN, NW>::N_INSTR
-                                          : MNMajorLoader<BN, NW>::N_INSTR;
+  constexpr int A_INSTR = loads_per_wave<MODE, true, BM, NW>();
+  constexpr int B_INSTR = loads_per_wave<MODE, false, BN, NW>();
   constexpr int NDMA = A_INSTR + B_INSTR + SC_INSTR;
-  static_assert(S >= 2 && S <= 4 && NDMA * (S - 2) <= 63, "pipeline depth");
+  static_assert(S >= 2 && S <= 8 && NDMA * (S - 2) <= 63, "pipeline depth");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ int64_t s_tile[4];
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 
     auto load_step = [&](int64_t kt, int stage) {
       const uint32_t st = smem_lds + stage * STAGE;
-      const int64_t k0 = kt * BK;
+      const int64_t k0 = kt * KS;
       if constexpr (MODE == NT_BF16) {
         KMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, p.K);
         KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K, k0, p.K);
@@ -457,15 +462,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
         MNMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, m0, p.K);
         MNMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
       } else {
-        NVCodeLoader<BM, NW>::load(st, wid, ra, p.K, k0);
-        NVCodeLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K, k0);
-        // Scales: 64 rows (4 bytes each) per load, A rows first.
+        // Codes: 128 bytes (256 elements) per row, laid out like a K-major
+        // bf16 tile of 64 16-bit units per row.
+        KMajorLoader<BM, NW>::load(st, wid, ra, p.K / 4, k0 / 4, p.K / 4);
+        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K / 4, k0 / 4, p.K / 4);
+        // Scales: 16 bytes per row, 64 rows per load, A rows first.
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
           const int idx = wid + NW * i;
           const bool is_a = idx * 64 < BM;
           const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          dma4(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 256, (uint32_t)(row * (p.K / 16) + k0 / 16));
+          dma16(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(row * (p.K / 16) + k0 / 16));
         }
       }
     };
@@ -478,7 +485,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int64_t nk = (red + BK - 1) / BK;
+    const int64_t nk = (red + KS - 1) / KS;
+    // A wave whose rows all lie past the expert's end (the last row block
+    // of an expert is partly empty) skips its MFMAs; it still loads and
+    // takes part in every barrier.
+    int n_active = FM;
+    if (MODE != TN_BF16 && m_end - m0 <= wm * WTM) n_active = 0;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < nk) load_step(s, s);
@@ -488,74 +500,86 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       // steps' loads are outstanding; the barrier then makes every wave's
       // loads visible and frees the stage read in the previous step.
       const int64_t ahead = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
-      if (ahead >= 2)
-        wait_vmcnt<(S >= 4 ? 2 : 0) * NDMA>();
-      else if (ahead == 1)
-        wait_vmcnt<(S >= 3 ? 1 : 0) * NDMA>();
-      else
-        wait_vmcnt<0>();
+      wait_steps_ahead<S - 2, NDMA>((int)ahead);
       lds_barrier();
       if (kt + S - 1 < nk) load_step(kt + S - 1, (int)((kt + S - 1) % S));
 
       const uint8_t* st = smem + (int)(kt % S) * STAGE;
-      if constexpr (NV) {
-        NVFrag fa[FM], fb[FN];
+      // One step of MFMAs over the first NA fragment rows of this wave.
+      auto compute = [&](auto na_tag) {
+        constexpr int NA = decltype(na_tag)::value;
+        if constexpr (NA > 0) {
+          if constexpr (NV) {
+            // 64-element chunks of this stage inside K (K % 64 == 0).
+            const int64_t k_left = p.K - kt * KS;
+            const int nchunk = k_left >= KS ? KS / BK : (int)(k_left / BK);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = frag_nv(st, st + A_BYTES + B_BYTES, wm * WTM + i * 32, lane);
+            for (int c = 0; c < KS / BK; ++c) {
+              if (c < nchunk) {
+                NVFrag fa[NA], fb[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[j] = frag_nv(st + A_BYTES, st + A_BYTES + B_BYTES + BM * 4, wn * WTN + j * 32, lane);
-        // Operands of sub-step kk+1 are expanded while the MFMAs of kk run.
-        f16x8_t av[2][FM], bv[2][FN];
-        auto expand = [&](int kk, int buf) {
+                for (int i = 0; i < NA; ++i) fa[i] = frag_nv(st, st + A_BYTES + B_BYTES, wm * WTM + i * 32, c, lane);
 #pragma unroll
-          for (int i = 0; i < FM; ++i) av[buf][i] = nv_expand(fa[i], kk);
+                for (int j = 0; j < FN; ++j)
+                  fb[j] = frag_nv(st + A_BYTES, st + A_BYTES + B_BYTES + BM * 16, wn * WTN + j * 32, c, lane);
+                // Operands of sub-step kk+1 are expanded while the MFMAs of kk run.
+                f16x8_t av[2][NA], bv[2][FN];
+                auto expand = [&](int kk, int buf) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) bv[buf][j] = nv_expand(fb[j], kk);
-        };
-        expand(0, 0);
+                  for (int i = 0; i < NA; ++i) av[buf][i] = nv_expand(fa[i], kk);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          if (kk + 1 < BK / 16) expand(kk + 1, (kk + 1) & 1);
+                  for (int j = 0; j < FN; ++j) bv[buf][j] = nv_expand(fb[j], kk);
+                };
+                expand(0, 0);
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
+                for (int kk = 0; kk < BK / 16; ++kk) {
+                  if (kk + 1 < BK / 16) expand(kk + 1, (kk + 1) & 1);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
-          // ~9 VALU per expanded fragment (scale decode, 4 converts, 4 multiplies)
-          if (kk + 1 < BK / 16) interleave_mfma_valu<FM * FN, (9 * (FM + FN) + FM * FN - 1) / (FM * FN)>();
+                  for (int i = 0; i < NA; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                      acc[i][j] =
+                          __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+                  // ~9 VALU per expanded fragment (scale decode, 4 converts, 4 multiplies)
+                  if (kk + 1 < BK / 16) interleave_mfma_valu<NA * FN, (9 * (NA + FN) + NA * FN - 1) / (NA * FN)>();
+                }
+              }
+            }
+          } else {
+            // Fragments of sub-step kk+1 are read while the MFMAs of kk run.
+            bf16x8_t av[2][NA], bv[2][FN];
+            auto read_frags = [&](int kk, int buf) {
+#pragma unroll
+              for (int i = 0; i < NA; ++i)
+                av[buf][i] = MODE == TN_BF16 ? frag_mnmajor<BM>(st, wm * WTM + i * 32, kk, lane)
+                                             : frag_kmajor(st, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                bv[buf][j] = MODE == NT_BF16 ? frag_kmajor(st + A_BYTES, wn * WTN + j * 32, kk, lane)
+                                             : frag_mnmajor<BN>(st + A_BYTES, wn * WTN + j * 32, kk, lane);
+            };
+            // LDS reads per sub-step: one per K-major fragment, two per MN-major one.
+            constexpr int NRD = NA * (MODE == TN_BF16 ? 2 : 1) + FN * (MODE == NT_BF16 ? 1 : 2);
+            read_frags(0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk) {
+              if (kk + 1 < BK / 16) read_frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+              for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  acc[i][j] =
+                      __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+              if (kk + 1 < BK / 16)
+                interleave_mfma_ds<NA * FN, NRD>();
+              else
+                interleave_mfma_ds<NA * FN, 0>();
+            }
+          }
         }
-      } else {
-        // Fragments of sub-step kk+1 are read while the MFMAs of kk run.
-        bf16x8_t av[2][FM], bv[2][FN];
-        auto read_frags = [&](int kk, int buf) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            av[buf][i] = MODE == TN_BF16 ? frag_mnmajor<BM>(st, wm * WTM + i * 32, kk, lane)
-                                         : frag_kmajor(st, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bv[buf][j] = MODE == NT_BF16 ? frag_kmajor(st + A_BYTES, wn * WTN + j * 32, kk, lane)
-                                         : frag_mnmajor<BN>(st + A_BYTES, wn * WTN + j * 32, kk, lane);
-        };
-        // LDS reads per sub-step: one per K-major fragment, two per MN-major one.
-        constexpr int NRD = FM * (MODE == TN_BF16 ? 2 : 1) + FN * (MODE == NT_BF16 ? 1 : 2);
-        read_frags(0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          if (kk + 1 < BK / 16) read_frags(kk + 1, (kk + 1) & 1);
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
-          if (kk + 1 < BK / 16)
-            interleave_mfma_ds<FM * FN, NRD>();
-          else
-            interleave_mfma_ds<FM * FN, 0>();
-        }
-      }
+      };
+      if (n_active > 0) compute(IntConst<FM>{});
     }
 
     // Epilogue.  Lane layout of a 32x32 MFMA result (probed on the device):
@@ -632,10 +656,10 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   X(2, 256, 128, 2, 2, 3)        \
   X(3, 128, 256, 2, 2, 3)        \
   X(4, 128, 128, 2, 2, 4)        \
-  X(5, 256, 256, 2, 4, 4)        \
-  X(6, 256, 256, 4, 2, 4)        \
+  X(5, 256, 128, 4, 2, 2)        \
+  X(6, 128, 256, 2, 4, 2)        \
   X(7, 256, 256, 2, 2, 2)        \
-  X(8, 256, 256, 2, 2, 4)
+  X(8, 128, 128, 2, 2, 2)
 
 #ifdef NVFP4MOE_GEMM_FORCE_CONFIG
 constexpr int kForcedConfig = NVFP4MOE_GEMM_FORCE_CONFIG;
@@ -646,8 +670,8 @@ constexpr int kForcedConfig = -1;
 // Whether a configuration is valid for a layout: LDS within the 160 KiB of
 // a gfx950 CU, and whole loads per wave for NVFP4 tiles.
 constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s) {
-  return s * (mode == W4A4 ? (bm + bn) * 36 : (bm + bn) * BK * 2) <= 160 * 1024 &&
-         (mode != W4A4 || (bm % (32 * wm * wn) == 0 && bn % (32 * wm * wn) == 0 && (bm + bn) % (64 * wm * wn) == 0));
+  return s * (bm + bn) * (mode == W4A4 ? 144 : 128) <= 160 * 1024 &&
+         (mode != W4A4 || (bm + bn) % (64 * wm * wn) == 0);
 }
 
 template <int MODE>
@@ -672,8 +696,8 @@ int pick_config(int mode, const Params& p) {
   // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
   // 256 x 256 tiles on 8 waves; W4A4 with 4 LDS stages (its tiles are small).
   switch (mode) {
-    case W4A4: return 6;
-    default: return 0;
+    case W4A4: return 1;
+    default: return 1;
   }
 }
 
