@@ -66,8 +66,9 @@ def op_work(name, T, k, E, D, F):
     f1, f2 = gemm_flops(R, D, F)
     nv = lambda rows, cols: rows * cols * (0.5 + 1.0 / 16)  # noqa: E731  NVFP4 bytes per element
     table = {
-        "moe_permute": (0.0, T * D * 2 + R * D * 2 + R * 4 * 3),
-        "quantize_x": (0.0, R * D * 2 + nv(R, D)),
+        # metadata, X read once (its amax pass reads it once more), X_perm
+        # bf16 and its NVFP4 rows written once
+        "permute_quantize_x": (0.0, T * D * 2 + R * D * 2 + nv(R, D) + R * 4 * 3),
         "w4a4_gate_up": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
         "silu_gate_fwd": (0.0, R * 2 * F * 2 + R * F * 2),
         "quantize_h": (0.0, R * F * 2 + nv(R, F)),
@@ -81,12 +82,13 @@ def op_work(name, T, k, E, D, F):
         "bf16_tn_gate_up": (f1, R * 2 * F * 2 + R * D * 2 + E * 2 * F * D * 4),
         "unpermute_dx": (0.0, R * D * 2 + T * D * 2),
         "bf16_nt_gate_up_baseline": (f1, R * D * 2 + E * 2 * F * D * 2 + R * 2 * F * 2),
+        "quantize_x_perm_cold": (0.0, R * D * 2 + nv(R, D)),
     }
     return table[name]
 
 
 # Ops of the full-update step, in launch order (the PMC summary's rows).
-STEP_OPS = ["moe_permute", "quantize_x", "w4a4_gate_up", "silu_gate_fwd", "quantize_h", "w4a4_down", "unpermute",
+STEP_OPS = ["permute_quantize_x", "w4a4_gate_up", "silu_gate_fwd", "quantize_h", "w4a4_down", "unpermute",
             "gather_dy", "bf16_nn_down", "bf16_tn_down", "silu_gate_bwd", "bf16_nn_gate_up", "bf16_tn_gate_up",
             "unpermute_dx"]
 MARKER = "FillFunctor<int>"  # a one-element int fill between ops in --pmc-run
@@ -109,15 +111,15 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
     """The ops of one step, in launch order, as (name, thunk)."""
     E, k, T = buf.E, buf.k, buf.T
 
-    def permute():
-        meta_box["m"] = ops.moe_permute(inp["ids"], E, x=inp["x"], x_perm=buf.x_perm, amax_out=buf.amax[0:1],
-                                        workspace=buf.ws)
+    def permute_quantize():
+        # bf16 rows kept for the backward's weight gradient only
+        meta_box["m"] = ops.moe_permute_nvfp4(inp["ids"], E, inp["x"], x_perm=buf.x_perm if backward else None,
+                                              want_x_perm=backward, amax_out=buf.amax[0:1], q=buf.a1_q,
+                                              scales=buf.a1_s, gscale=buf.a1_g, workspace=buf.ws)
 
     m = lambda: meta_box["m"]  # noqa: E731
     seq = [
-        ("moe_permute", permute),
-        ("quantize_x", lambda: ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
-                                                  gscale=buf.a1_g)),
+        ("permute_quantize_x", permute_quantize),
         ("w4a4_gate_up", lambda: ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"],
                                                        wq_gu["g"], m()["offsets"], out=buf.y1)),
         ("silu_gate_fwd", lambda: ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])),
@@ -334,6 +336,22 @@ def main():
     torch.cuda.synchronize()
     per_op_extra = {"bf16_nt_gate_up_baseline": b0.elapsed_time(b1) / nrep}
 
+    # Standalone NVFP4 quantize of the permuted activations (R x D bf16,
+    # larger than the 256 MB Infinity Cache), cache flushed by a read of a
+    # 512 MiB buffer before each repetition; median.
+    flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    qts = []
+    for _ in range(7):
+        float(flush.sum())
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record()
+        ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s, gscale=buf.a1_g)
+        q1.record()
+        torch.cuda.synchronize()
+        qts.append(q0.elapsed_time(q1))
+    del flush
+    per_op_extra["quantize_x_perm_cold"] = sorted(qts)[len(qts) // 2]
+
     R = T * k
     f1, f2 = gemm_flops(R, D, F)
     step_flops = (f1 + f2) * (3 if backward else 1)
@@ -356,7 +374,7 @@ def main():
         kernels[name] = ent
 
     def roofline_of(name):
-        ms = per_op[name]
+        ms = per_op[name] if name in per_op else per_op_extra[name]
         fl, by = op_work(name, T, k, E, D, F)
         tr = traffic.get(name)
         tr_bytes = None if tr is None else round(tr["fetch"] + tr["write"])
@@ -398,7 +416,8 @@ def main():
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
                       "bf16_same_shape_tflops": bl.get("tflops"),
                       "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3) if w4 else None},
-        "quantize": roofline_of("quantize_x"),
+        "quantize": roofline_of("quantize_x_perm_cold"),
+        "permute_quantize": roofline_of("permute_quantize_x"),
         "cpu_baseline": cpu,
         "kernels": kernels,
         "weight_quantize": {"ms": round(wq_ms, 4), "gbs": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},

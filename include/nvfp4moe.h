@@ -142,6 +142,30 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x,
                 nvfp4moe_stream_t stream);
 
 /*
+ * moe_permute_nvfp4 -- moe_permute fused with the NVFP4 quantization of the
+ * gathered rows (token-wise path with contiguous layout, device-side
+ * metadata, amax reuse and op fusion: [JA], fourth paragraph).  Computes the
+ * same offsets/dest/src as moe_permute, optionally the bf16 rows x_perm, and
+ * q/scales/gscale equal to nvfp4_quantize(x_perm, groups = 1, amax) --
+ * bit for bit -- without reading x_perm back: each permuted row is encoded
+ * while it is gathered from x.
+ *   x        [T][D] bf16, 16-byte aligned; D % 16 == 0.
+ *   x_perm   [T*k][D] bf16 out, or NULL when only the NVFP4 rows are needed.
+ *   amax_in  fp32 [1] or NULL.  When NULL, max |x| over the T rows of x
+ *            (equal to that of x_perm: every token is routed) is computed
+ *            first and written to amax_out (then non-NULL).
+ *   q        [T*k][D/2], scales [T*k][D/16], gscale [1] out (see
+ *            nvfp4_quantize).  Rows past offsets[E] (invalid ids) are zeros.
+ *   offsets, dest, src, workspace, status: as for moe_permute.
+ * Errors: EINVAL (NULL, negative sizes, amax_in and amax_out both NULL),
+ * ESHAPE (D % 16, alignment, E > 4096, k > 64), EWORKSPACE.
+ */
+int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D,
+                      void* x_perm, const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales,
+                      float* gscale, int32_t* offsets, int32_t* dest, int32_t* src, void* workspace,
+                      size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream);
+
+/*
  * moe_gather -- out[p] = w[src[p]] * x[src[p] / k] for p < R (w = 1 when
  * topk_w is NULL); rows with src[p] < 0 are written as zeros.  With
  * topk_w == NULL any dtype is copied verbatim (NVFP4MOE_U8 row payloads,

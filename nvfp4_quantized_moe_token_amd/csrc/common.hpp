@@ -80,4 +80,7 @@ __device__ __forceinline__ void block_atomic_max(float* dst, float v) {
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);
 
+// max |x| per row-group (quantize.hip); amax_out is cleared first.
+int launch_amax(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out, hipStream_t st);
+
 }  // namespace nvfp4moe

@@ -16,7 +16,7 @@
 //                       assignment is a popcount, never an atomic: the
 //                       result does not depend on scheduling.
 // Out-of-range ids are skipped (dest = -1) and flagged in the status word.
-#include "common.hpp"
+#include "nvfp4_codec.hpp"
 
 namespace nvfp4moe {
 namespace {
@@ -307,6 +307,52 @@ int gather_dispatch(const void* x, int x_dtype, int64_t row_elems, const int32_t
   return NVFP4MOE_EINVAL;
 }
 
+// Gather fused with NVFP4 quantization of the gathered rows (token-wise
+// path with op fusion: "miniTE報告、NVFP4強化学習の安定性を検証", fourth
+// paragraph).  Thread-blocks walk the 16-element blocks b = p*bpr + j of the
+// permuted rows: each reads its 32 bytes from token src[p]/k, optionally
+// stores them to x_perm, and writes the block's codes and scale with the
+// same encoding as nvfp4_quantize on x_perm (so the result equals
+// quantize(permute(X)), which equals permute(quantize(X)) row by row).
+// Rows with src < 0 (past offsets[E]) are zeros.  X is read once per
+// assignment from cache instead of X_perm being re-read from HBM.
+template <int NT>
+__global__ __launch_bounds__(NT) void gather_quantize_kernel(const uint4* __restrict__ x, int64_t bpr,
+                                                             const int32_t* __restrict__ src, int k, int64_t R,
+                                                             uint4* __restrict__ x_perm, const float* __restrict__ amax,
+                                                             uint2* __restrict__ q, uint8_t* __restrict__ scales,
+                                                             float* __restrict__ gscale) {
+  const float g = global_scale(amax[0]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = g;
+  const int64_t nblk = R * bpr;
+  for (int64_t b = blockIdx.x * (int64_t)NT + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * NT) {
+    const int64_t p = b / bpr, j = b - p * bpr;
+    const int32_t s = src[p];
+    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+    if (s >= 0) {
+      const uint4* in = x + ((int64_t)(s / k) * bpr + j) * 2;
+      w0 = in[0];
+      w1 = in[1];
+    }
+    if (x_perm) {
+      x_perm[2 * b] = w0;
+      x_perm[2 * b + 1] = w1;
+    }
+    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(ws[i]);
+      v[2 * i + 1] = bf16_hi(ws[i]);
+    }
+    uint2 codes;
+    uint32_t S;
+    quantize_block(v, g, codes, S);
+    q[b] = codes;
+    scales[b] = (uint8_t)S;
+  }
+}
+
 // out[t] = sum_j w[t][j] * y[dest[t*k+j]], fp32 fma in ascending j.
 template <int IN, int OUT>
 __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restrict__ y, const int32_t* __restrict__ dest,
@@ -363,6 +409,21 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
 }  // namespace
 }  // namespace nvfp4moe
 
+namespace nvfp4moe {
+// Routing metadata for R assignments: histograms, scan, stable ranks, src
+// tail.  amax_cleared (nullable) is zeroed on the way.
+static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* amax_cleared, void* workspace,
+                           int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st) {
+  const int64_t chunks = cdiv(R, kChunk);
+  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
+  count_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, amax_cleared);
+  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets);
+  rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
+  src_tail_kernel<<<(unsigned)(cdiv(R, 256) < 1024 ? cdiv(R, 256) : 1024), 256, 0, st>>>(offsets, E, R, src);
+  return launch_status();
+}
+}  // namespace nvfp4moe
+
 using namespace nvfp4moe;
 
 extern "C" size_t moe_permute_workspace_size(int64_t T, int k, int E) {
@@ -391,18 +452,12 @@ extern "C" int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, con
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   hipStream_t st = as_stream(stream);
-  const int64_t chunks = cdiv(R, kChunk);
-  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
   if (R == 0) {
     fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
     if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
     return launch_status();
   }
-  count_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, x ? amax_out : nullptr);
-  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets);
-  rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
-  src_tail_kernel<<<(unsigned)(cdiv(R, 256) < 1024 ? cdiv(R, 256) : 1024), 256, 0, st>>>(offsets, E, R, src);
-  int rc = launch_status();
+  int rc = launch_metadata(topk_ids, R, E, x ? amax_out : nullptr, workspace, offsets, dest, src, status, st);
   if (rc != NVFP4MOE_OK) return rc;
   if (!x) {
     if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
@@ -451,5 +506,48 @@ extern "C" int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* des
     unpermute_kernel<NVFP4MOE_F32, NVFP4MOE_BF16><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
   else
     unpermute_kernel<NVFP4MOE_F32, NVFP4MOE_F32><<<grid, 256, 0, st>>>(y, dest, topk_w, T, k, D, o);
+  return launch_status();
+}
+
+extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D,
+                                 void* x_perm, const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales,
+                                 float* gscale, int32_t* offsets, int32_t* dest, int32_t* src, void* workspace,
+                                 size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || D < 0) return NVFP4MOE_EINVAL;
+  if (E > kMaxExperts || k > 64) return NVFP4MOE_ESHAPE;
+  if (!offsets || !gscale || (!amax_in && !amax_out)) return NVFP4MOE_EINVAL;
+  if (T > 0 && (!topk_ids || !dest || !src)) return NVFP4MOE_EINVAL;
+  if (T > 0 && D > 0 && (!x || !q || !scales)) return NVFP4MOE_EINVAL;
+  if (D % 16 != 0) return NVFP4MOE_ESHAPE;
+  if (T > 0 && D > 0 && (!aligned(x, 16) || !aligned(q, 8) || (x_perm && !aligned(x_perm, 16))))
+    return NVFP4MOE_ESHAPE;
+  if (!aligned(gscale, 4) || (amax_in && !aligned(amax_in, 4)) || (amax_out && !aligned(amax_out, 4)))
+    return NVFP4MOE_ESHAPE;
+  const int64_t R = T * k;
+  if (R > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  if (ws_bytes < moe_permute_workspace_size(T, k, E) || (R > 0 && !workspace)) return NVFP4MOE_EWORKSPACE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  hipStream_t st = as_stream(stream);
+  const float* amax = amax_in;
+  if (!amax_in) {
+    // The activation amax is taken once, over the T unpermuted rows.
+    const int rc = launch_amax(x, NVFP4MOE_BF16, T * D * 2 / 16, 1, amax_out, st);
+    if (rc != NVFP4MOE_OK) return rc;
+    amax = amax_out;
+  }
+  if (R == 0) {
+    fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
+  } else {
+    const int rc = launch_metadata(topk_ids, R, E, nullptr, workspace, offsets, dest, src, status, st);
+    if (rc != NVFP4MOE_OK) return rc;
+  }
+  // Launched even without rows: it also writes the global scale.
+  const int64_t bpr = D / 16, nblk = R * bpr;
+  int64_t grid = cdiv(nblk > 0 ? nblk : 1, 256);
+  if (grid > 256 * 16) grid = 256 * 16;
+  gather_quantize_kernel<256><<<(unsigned)grid, 256, 0, st>>>(
+      reinterpret_cast<const uint4*>(x), bpr, src, k, R, reinterpret_cast<uint4*>(x_perm), amax,
+      reinterpret_cast<uint2*>(q), scales, gscale);
   return launch_status();
 }

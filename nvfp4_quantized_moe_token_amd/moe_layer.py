@@ -4,10 +4,11 @@ orders the calls and owns the buffers).
 
 Forward ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph:
 contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
-  moe_permute (metadata + gather + amax of X)  ->  nvfp4_quantize(X_perm,
-  amax_in=amax_X)  ->  grouped_gemm_w4a4 (gate+up)  ->  silu_gate_fwd (+amax
-  of H)  ->  nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)
-  ->  moe_unpermute (routing-weighted combine).
+  moe_permute_nvfp4 (amax of X once, metadata, gather fused with the NVFP4
+  quantization of the gathered rows; the bf16 rows are kept only for the
+  backward)  ->  grouped_gemm_w4a4 (gate+up)  ->  silu_gate_fwd (+amax of H)
+  ->  nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)  ->
+  moe_unpermute (routing-weighted combine).
 Backward in BF16 (same page, first paragraph), no amax reduction at all:
   moe_gather(dY, weighted)  ->  NN dgrad / TN wgrad of the down projection
   ->  silu_gate_bwd  ->  NN dgrad / TN wgrad of gate+up  ->  moe_unpermute
@@ -54,11 +55,14 @@ class Buffers:
             self.dw_gu = e(E, 2 * F, D, dt=f32)
 
 
-def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
-    """W4A4 MoE forward; returns the routing metadata dict."""
+def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True):
+    """W4A4 MoE forward; returns the routing metadata dict.  The bf16
+    permuted rows (buf.x_perm) are written only when keep_x_perm (the BF16
+    backward's weight gradient needs them)."""
     E = buf.E
-    meta = ops.moe_permute(topk_ids, E, x=x, x_perm=buf.x_perm, amax_out=buf.amax[0:1], workspace=buf.ws)
-    ops.nvfp4_quantize(buf.x_perm, amax_in=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s, gscale=buf.a1_g)
+    meta = ops.moe_permute_nvfp4(topk_ids, E, x, x_perm=buf.x_perm if keep_x_perm else None,
+                                 want_x_perm=keep_x_perm, amax_out=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
+                                 gscale=buf.a1_g, workspace=buf.ws)
     ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], meta["offsets"],
                           out=buf.y1)
     ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])

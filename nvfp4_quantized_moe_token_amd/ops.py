@@ -98,6 +98,40 @@ def moe_permute(topk_ids, num_experts, x=None, x_perm=None, amax_out=None, want_
     return dict(offsets=offsets, dest=dest, src=src, x_perm=x_perm, amax=amax_out)
 
 
+def moe_permute_nvfp4(topk_ids, num_experts, x, x_perm=None, want_x_perm=True, amax_in=None, amax_out=None,
+                      q=None, scales=None, gscale=None, status=None, workspace=None):
+    """moe_permute fused with the NVFP4 quantization of the gathered rows.
+    Returns a dict with offsets, dest, src, x_perm (or None), q, scales,
+    gscale and amax."""
+    _dev(topk_ids, x, x_perm, amax_in, amax_out, q, scales, gscale, status)
+    T, k = topk_ids.shape
+    D = x.shape[1]
+    dev = x.device
+    R = T * k
+    lib = _lib.load()
+    offsets = torch.empty((num_experts + 1,), dtype=torch.int32, device=dev)
+    dest = torch.empty((R,), dtype=torch.int32, device=dev)
+    src = torch.empty((R,), dtype=torch.int32, device=dev)
+    if x_perm is None and want_x_perm:
+        x_perm = torch.empty((R, D), dtype=x.dtype, device=dev)
+    q = torch.empty((R, D // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((R, D // 16), dtype=torch.uint8, device=dev) if scales is None else scales
+    gscale = torch.empty((1,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    if amax_in is None and amax_out is None:
+        amax_out = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws_bytes = lib.moe_permute_workspace_size(T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("moe_permute_nvfp4 takes bf16 activations")
+    rc = lib.moe_permute_nvfp4(_ptr(topk_ids), T, k, num_experts, _ptr(x), D, _ptr(x_perm), _ptr(amax_in),
+                               _ptr(amax_out), _ptr(q), _ptr(scales), _ptr(gscale), _ptr(offsets), _ptr(dest),
+                               _ptr(src), _ptr(workspace), workspace.numel(), _ptr(status), _stream())
+    _check("moe_permute_nvfp4", rc)
+    return dict(offsets=offsets, dest=dest, src=src, x_perm=x_perm, q=q, scales=scales, gscale=gscale,
+                amax=amax_in if amax_in is not None else amax_out)
+
+
 def moe_gather(x, src, k, topk_w=None, out=None, out_dtype=None):
     """out[p] = w[src[p]] * x[src[p] // k] (a verbatim row copy when no weights)."""
     _dev(x, src, topk_w, out)

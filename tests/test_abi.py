@@ -94,6 +94,26 @@ def test_permute_validation(lib):
     assert p(FAKE, 100, 8, 128, FAKE, 2, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None) == -1  # amax of u8
 
 
+def test_permute_nvfp4_validation(lib):
+    f = lib.moe_permute_nvfp4
+    ws = lib.moe_permute_workspace_size(100, 8, 128)
+    ok = [FAKE, 100, 8, 128, FAKE, 2048, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None]
+    bad = list(ok); bad[2] = 0
+    assert f(*bad) == -1                       # k = 0
+    bad = list(ok); bad[7] = None; bad[8] = None
+    assert f(*bad) == -1                       # neither amax_in nor amax_out
+    bad = list(ok); bad[11] = None
+    assert f(*bad) == -1                       # gscale NULL
+    bad = list(ok); bad[5] = 2040
+    assert f(*bad) == -2                       # D % 16
+    bad = list(ok); bad[4] = FAKE + 8
+    assert f(*bad) == -2                       # x alignment
+    bad = list(ok); bad[3] = 5000
+    assert f(*bad) == -2                       # E too big
+    bad = list(ok); bad[16] = ws - 1
+    assert f(*bad) == -5                       # workspace too small
+
+
 def test_gather_unpermute_validation(lib):
     assert lib.moe_gather(FAKE, 1, 64, FAKE, None, 0, 10, FAKE, 1, None) == -1
     assert lib.moe_gather(FAKE, 2, 64, FAKE, FAKE, 8, 10, FAKE, 2, None) == -1  # weighted bytes

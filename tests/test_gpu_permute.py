@@ -172,3 +172,77 @@ def test_unpermute(weighted):
     assert_bf16_close(to_np(out), ref, scale=scale, what="unpermute bf16")
     err = np.abs(to_np(out32) - ref)
     assert (err <= 2.0 ** -21 * scale + 1e-30).all()
+
+
+@pytest.mark.parametrize("cfg", ["moe_4k", "moe_16k_skew", "moe_8k_update"])
+@pytest.mark.parametrize("with_x_perm", [True, False])
+def test_permute_nvfp4_matches_oracle(cfg, with_x_perm):
+    """Fused gather + quantize: metadata, x_perm, codes and scales bit-exact
+    against the oracle's quantize(permute(X)) with amax(X)."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.CONFIGS[cfg](weights=False)
+    E, k = d["E"], d["k"]
+    r = ops.moe_permute_nvfp4(to_gpu(d["topk_ids"], torch.int32), E, to_gpu(d["x"], torch.bfloat16),
+                              want_x_perm=with_x_perm)
+    torch.cuda.synchronize()
+    off, dest, src = _check_meta(d["topk_ids"], E, r)
+    amax = np.float32(np.abs(d["x"]).max())
+    assert to_np(r["amax"])[0] == amax
+    xp = moe.gather_rows(d["x"], src, k)
+    if with_x_perm:
+        np.testing.assert_array_equal(to_np(r["x_perm"]), xp)
+    else:
+        assert r["x_perm"] is None
+    # Sampled rows (the full 16k-token oracle quantization is slow): every
+    # expert's first and last row plus a seeded sample.
+    rng = np.random.default_rng(5)
+    rows = set(rng.choice(len(src), min(len(src), 3000), replace=False).tolist())
+    for e in range(E):
+        if off[e + 1] > off[e]:
+            rows.update([int(off[e]), int(off[e + 1]) - 1])
+    rows = np.array(sorted(rows))
+    q, s, g, _ = nvfp4.quantize(xp[rows], amax=[amax])
+    np.testing.assert_array_equal(to_np(r["q"])[rows], q)
+    np.testing.assert_array_equal(to_np(r["scales"])[rows], s)
+    assert to_np(r["gscale"])[0] == g[0]
+
+
+def test_permute_nvfp4_equals_unfused_path():
+    """moe_permute + nvfp4_quantize(amax_in) and the fused call agree bit for
+    bit, with a given amax (reuse) and with invalid ids present."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(9)
+    T, k, E, D = 700, 4, 9, 256
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[3, 1] = E + 2          # out of range: row past offsets[E]
+    ids[10, 0] = -1
+    x = workloads._bf16(rng.standard_normal((T, D)).astype(np.float32) * 3)
+    ids_g, x_g = to_gpu(ids, torch.int32), to_gpu(x, torch.bfloat16)
+    amax = to_gpu(np.array([np.abs(x).max() * 1.5], np.float32), torch.float32)  # a stale, larger amax
+    st1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = ops.moe_permute(ids_g, E, x=x_g, status=st1)
+    qa, sa, ga, _ = ops.nvfp4_quantize(a["x_perm"], amax_in=amax)
+    b = ops.moe_permute_nvfp4(ids_g, E, x_g, amax_in=amax, status=st2)
+    torch.cuda.synchronize()
+    for key in ("offsets", "dest", "src", "x_perm"):
+        np.testing.assert_array_equal(to_np(a[key]), to_np(b[key]))
+    np.testing.assert_array_equal(to_np(qa), to_np(b["q"]))
+    np.testing.assert_array_equal(to_np(sa), to_np(b["scales"]))
+    np.testing.assert_array_equal(to_np(ga), to_np(b["gscale"]))
+    assert to_np(st1)[0] == to_np(st2)[0] == 1
+    R_valid = int(to_np(b["offsets"])[-1])
+    assert (to_np(b["q"])[R_valid:] == 0).all() and (to_np(b["scales"])[R_valid:] == 0).all()
+
+
+def test_permute_nvfp4_zero_tokens():
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    ids = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    r = ops.moe_permute_nvfp4(ids, 16, x)
+    torch.cuda.synchronize()
+    assert (to_np(r["offsets"]) == 0).all()
+    assert to_np(r["amax"])[0] == 0.0 and to_np(r["gscale"])[0] == 1.0
