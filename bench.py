@@ -19,6 +19,7 @@ Prints one JSON line (N = 1).
 
     python bench.py [--steps K] [--warmup W] [--workload moe_8k_update]
     python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # HBM traffic summary
+    python bench.py --kernel-stats-summary DIR          # rocprofv3 --stats table
 """
 
 import argparse
@@ -189,6 +190,13 @@ def load_traffic():
     return out if digest == source_digest() else {}
 
 
+def short_name(n):
+    """Kernel name without namespace, return type and parameter list."""
+    n = n.replace("(anonymous namespace)::", "").replace("nvfp4moe::", "")
+    n = n[5:] if n.startswith("void ") else n
+    return n.split("(")[0].replace(" ", "")
+
+
 def pmc_summary(fetch_dir, write_dir):
     """Turn two rocprofv3 --pmc runs of `bench.py --pmc-run` (FETCH_SIZE,
     then WRITE_SIZE; counters in KiB per dispatch) into per-op HBM bytes of
@@ -215,7 +223,7 @@ def pmc_summary(fetch_dir, write_dir):
         out = []
         for j, name in enumerate(STEP_OPS):
             seg = rows[marks[j] + 1:marks[j + 1]]
-            out.append((name, sum(v for _, v in seg) * 1024.0, sorted({n.split("(")[0] for n, _ in seg})))
+            out.append((name, sum(v for _, v in seg) * 1024.0, sorted({short_name(n) for n, _ in seg})))
         return cal, out
 
     cal_f, fetch = per_op(read(fetch_dir, "FETCH_SIZE"))
@@ -231,6 +239,36 @@ def pmc_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+# Ops that launch the same kernel (one template instance per GEMM mode): the
+# roofline of a kernel averages over all of its launches in a step, as
+# rocprofv3's per-kernel statistics do.
+# Names as rocprofv3 prints them (first template argument = mode).
+KERNEL_OF_OP = {"w4a4_gate_up": "gemm_kernel<3,...> (W4A4)", "w4a4_down": "gemm_kernel<3,...> (W4A4)",
+                "bf16_nn_down": "gemm_kernel<1,...> (BF16 NN)", "bf16_nn_gate_up": "gemm_kernel<1,...> (BF16 NN)",
+                "bf16_tn_down": "gemm_kernel<2,...> (BF16 TN)", "bf16_tn_gate_up": "gemm_kernel<2,...> (BF16 TN)"}
+
+
+def kernel_stats_summary(d):
+    """Print the per-kernel table of a `rocprofv3 --kernel-trace --stats
+    --output-format csv` run (durations in microseconds)."""
+    import csv
+    paths = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    if not paths:
+        sys.exit("no *kernel_stats.csv under %s" % d)
+    rows = []
+    with open(paths[-1]) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+                         float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[2])
+    print("%-72s %6s %11s %10s %10s %10s %6s" % ("kernel", "calls", "total_us", "avg_us", "min_us", "max_us", "pct"))
+    for n, c, t, a, lo, hi, p in rows:
+        n = n.replace("(anonymous namespace)::", "")
+        n = n if len(n) <= 72 else n[:69] + "..."
+        print("%-72s %6d %11.1f %10.2f %10.2f %10.2f %6.2f" % (n, c, t, a, lo, hi, p))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,9 +279,13 @@ def main():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: steps only, then a 1 GiB calibration copy")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--kernel-stats-summary", metavar="DIR")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.kernel_stats_summary:
+        kernel_stats_summary(args.kernel_stats_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
@@ -387,7 +429,26 @@ def main():
         return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": tr_bytes, "ms": round(ms, 4)}
 
-    dominant = max(per_op, key=per_op.get)
+    def roofline_of_kernel(kname):
+        """Roofline of one kernel over its launches in a step: algorithmic
+        work per launch / average launch duration (rocprofv3's avg)."""
+        names = [o for o in STEP_OPS if KERNEL_OF_OP.get(o) == kname and o in per_op]
+        n = len(names)
+        ms = sum(per_op[o] for o in names) / n
+        fl = sum(op_work(o, T, k, E, D, F)[0] for o in names) / n
+        by = sum(op_work(o, T, k, E, D, F)[1] for o in names) / n
+        tr = [traffic.get(o) for o in names]
+        tr_bytes = None if None in tr else round(sum(t["fetch"] + t["write"] for t in tr) / n)
+        ach = fl / (ms * 1e-3) / 1e12
+        return {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": tr_bytes, "algorithmic_bytes": round(by), "avg_launch_ms": round(ms, 4)}
+
+    # Dominant kernel: the largest share of the step's time.
+    per_kernel = {}
+    for o, ms in per_op.items():
+        per_kernel[KERNEL_OF_OP.get(o, o)] = per_kernel.get(KERNEL_OF_OP.get(o, o), 0.0) + ms
+    dominant = max(per_kernel, key=per_kernel.get)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -412,7 +473,7 @@ def main():
                    "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "step_gflop": round(step_flops / 1e9, 1),
-        "roofline": roofline_of(dominant),
+        "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
                       "bf16_same_shape_tflops": bl.get("tflops"),
                       "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3) if w4 else None},
