@@ -46,12 +46,16 @@ def log(*a):
 
 
 def source_digest():
-    """sha256 over the HIP sources: recorded with PMC traffic so that a
-    changed kernel invalidates it."""
+    """sha256 over the HIP sources with comments and blank space removed:
+    recorded with PMC traffic so that a changed kernel invalidates it."""
+    import re
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "nvfp4_quantized_moe_token_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+        with open(p) as f:
+            code = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(os.path.basename(p).encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 
@@ -232,7 +236,11 @@ def pmc_summary(fetch_dir, write_dir):
     lines = ["# HBM traffic per op of one moe_8k_update step, from two rocprofv3 --pmc runs of",
              "# `bench.py --pmc-run` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the op's",
              "# kernels) scaled by the counters' reading of a plain %d-byte device copy:" % CALIB_BYTES,
-             "# fetch x%.4f, write x%.4f.  Bytes per launch; 'sources' fingerprints the HIP sources." % (sf, sw),
+             "# fetch x%.4f, write x%.4f.  Bytes per launch; 'sources' fingerprints the HIP sources (code, comments removed)." % (sf, sw),
+             "# commands: cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+             "-d $REPO/gpurun_out/pmc_fetch -o run -- python $REPO/bench.py --pmc-run --steps 2 --warmup 1",
+             "#   (the same with WRITE_SIZE into $REPO/gpurun_out/pmc_write), then",
+             "#   python $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write",
              "sources %s" % source_digest()]
     for (name, fb, kn), (_, wb, _) in zip(fetch, write):
         lines.append("op %s fetch %.0f write %.0f kernels %s" % (name, fb * sf, wb * sw, ";".join(kn)))

@@ -26,10 +26,11 @@
 //  * MN-major bf16 tiles (64 k x columns, as stored in HBM): rows of the
 //    reduction index, chunks XOR-swizzled by (row mod 4); fragments are
 //    read transposed with ds_read_b64_tr_b16 (two per fragment).
-//  * NVFP4 tiles (rows x 64 k): 32 bytes of codes per row (halves swizzled)
-//    and the row's 4 scale bytes.  Lane half h of an MFMA takes the 32 codes
-//    k in [32h, 32h+32) of the step, 8 per MFMA, for A and B alike (a fixed
-//    permutation of the reduction order), so one ds_read_b128 feeds 4 MFMAs.
+//  * NVFP4 tiles (rows x 256 k): 128 bytes of codes per row, swizzled like
+//    the K-major bf16 rows, and the row's 16 scale bytes.  In each 64-k
+//    group, lane half h of an MFMA takes the 32 codes k in [32h, 32h+32),
+//    8 per MFMA, for A and B alike (a fixed permutation of the reduction
+//    order), so one ds_read_b128 feeds 4 MFMAs.
 //
 // Scheduling.  The host knows only the total row count, so the kernel is
 // persistent: the grid is (CUs x resident workgroups), rounded to a multiple
