@@ -1,8 +1,9 @@
 """Benchmark of the NVFP4 token-wise MoE hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the MoE layer forward
-on the NVFP4 token-wise path (permute + amax, quantize, grouped W4A4 GEMM
-gate+up, SiLU gate + amax, requantize, grouped W4A4 GEMM down, unpermute)
+on the NVFP4 token-wise path (amax + permute fused with the quantize, grouped
+W4A4 GEMM gate+up with the SiLU gate + amax in its epilogue, requantize,
+grouped W4A4 GEMM down, unpermute)
 followed by its BF16 backward (weighted gather, grouped NN/TN GEMMs for both
 projections, SiLU-gate backward, unpermute).  Default workload: the
 Qwen3-30B-A3B-shaped full update at 8192 tokens (d_model 2048, 128 experts,
@@ -11,9 +12,10 @@ weight quantization runs once per optimizer step and is timed separately.
 
 Per-op times are HIP events recorded inside the timed steps, on the stream
 the library launches on (torch's current stream).  Beside the step, the
-BF16 grouped GEMM runs on the gate+up shape of the W4A4 one (the baseline
-the W4A4 GEMM is compared with), and the CPU oracle runs on a bounded
-sample of the same workload.
+plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped GEMM on
+the same shape and routing (the baseline the W4A4 GEMM is compared with) are
+timed alone, and the CPU oracle runs on a bounded sample of the same
+workload.
 
 Prints one JSON line (N = 1).
 
@@ -75,7 +77,8 @@ def op_work(name, T, k, E, D, F):
         # bf16 and its NVFP4 rows written once
         "permute_quantize_x": (0.0, T * D * 2 + R * D * 2 + nv(R, D) + R * 4 * 3),
         "w4a4_gate_up": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
-        "silu_gate_fwd": (0.0, R * 2 * F * 2 + R * F * 2),
+        # with the SiLU gate in the epilogue: Y1 (kept for the backward) and H written
+        "w4a4_gate_up_silu": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2 + R * F * 2),
         "quantize_h": (0.0, R * F * 2 + nv(R, F)),
         "w4a4_down": (f2, nv(R, F) + nv(E * D, F) + R * D * 2),
         "unpermute": (0.0, R * D * 2 + T * D * 2 + R * 4),
@@ -93,7 +96,7 @@ def op_work(name, T, k, E, D, F):
 
 
 # Ops of the full-update step, in launch order (the PMC summary's rows).
-STEP_OPS = ["permute_quantize_x", "w4a4_gate_up", "silu_gate_fwd", "quantize_h", "w4a4_down", "unpermute",
+STEP_OPS = ["permute_quantize_x", "w4a4_gate_up_silu", "quantize_h", "w4a4_down", "unpermute",
             "gather_dy", "bf16_nn_down", "bf16_tn_down", "silu_gate_bwd", "bf16_nn_gate_up", "bf16_tn_gate_up",
             "unpermute_dx"]
 MARKER = "FillFunctor<int>"  # a one-element int fill between ops in --pmc-run
@@ -125,9 +128,9 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
     m = lambda: meta_box["m"]  # noqa: E731
     seq = [
         ("permute_quantize_x", permute_quantize),
-        ("w4a4_gate_up", lambda: ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"],
-                                                       wq_gu["g"], m()["offsets"], out=buf.y1)),
-        ("silu_gate_fwd", lambda: ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])),
+        ("w4a4_gate_up_silu", lambda: ops.grouped_gemm_w4a4_silu_gate(
+            buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], m()["offsets"],
+            y1=buf.y1 if backward else None, want_y1=backward, h=buf.h, amax_out=buf.amax[1:2])),
         ("quantize_h", lambda: ops.nvfp4_quantize(buf.h, amax_in=buf.amax[1:2], q=buf.a2_q, scales=buf.a2_s,
                                                   gscale=buf.a2_g)),
         ("w4a4_down", lambda: ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"],
@@ -251,7 +254,7 @@ def pmc_summary(fetch_dir, write_dir):
 # roofline of a kernel averages over all of its launches in a step, as
 # rocprofv3's per-kernel statistics do.
 # Names as rocprofv3 prints them (first template argument = mode).
-KERNEL_OF_OP = {"w4a4_gate_up": "gemm_kernel<3,...> (W4A4)", "w4a4_down": "gemm_kernel<3,...> (W4A4)",
+KERNEL_OF_OP = {"w4a4_gate_up_silu": "gemm_kernel<4,...> (W4A4 + SiLU gate)", "w4a4_down": "gemm_kernel<3,...> (W4A4)",
                 "bf16_nn_down": "gemm_kernel<1,...> (BF16 NN)", "bf16_nn_gate_up": "gemm_kernel<1,...> (BF16 NN)",
                 "bf16_tn_down": "gemm_kernel<2,...> (BF16 TN)", "bf16_tn_gate_up": "gemm_kernel<2,...> (BF16 TN)"}
 
@@ -371,20 +374,28 @@ def main():
             per_op.setdefault(n0, []).append(e0.elapsed_time(e1))
     per_op = {n: sum(v) / len(v) for n, v in per_op.items()}
 
-    # BF16 grouped GEMM on the gate+up shape of the W4A4 GEMM (same routing).
+    # The plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped
+    # GEMM on the same shape and routing, each timed alone.
     offs = meta_box["m"]["offsets"]
+    y1w = torch.empty_like(buf.y1)
     y1b = torch.empty_like(buf.y1)
-    base = lambda: ops.grouped_gemm_bf16(ops.NT, buf.x_perm, inp["w_gu"], offs, out=y1b)  # noqa: E731
-    for _ in range(3):
-        base()
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    side = {
+        "w4a4_gate_up": lambda: ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"],
+                                                      wq_gu["g"], offs, out=y1w),
+        "bf16_nt_gate_up_baseline": lambda: ops.grouped_gemm_bf16(ops.NT, buf.x_perm, inp["w_gu"], offs, out=y1b),
+    }
+    per_op_extra = {}
     nrep = max(5, min(args.steps, 20))
-    b0.record()
-    for _ in range(nrep):
-        base()
-    b1.record()
-    torch.cuda.synchronize()
-    per_op_extra = {"bf16_nt_gate_up_baseline": b0.elapsed_time(b1) / nrep}
+    for name, fn in side.items():
+        for _ in range(3):
+            fn()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(nrep):
+            fn()
+        b1.record()
+        torch.cuda.synchronize()
+        per_op_extra[name] = b0.elapsed_time(b1) / nrep
 
     # Standalone NVFP4 quantize of the permuted activations (R x D bf16,
     # larger than the 256 MB Infinity Cache), cache flushed by a read of a
@@ -462,7 +473,7 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline()
 
-    w4 = kernels.get("w4a4_gate_up", {})
+    w4 = kernels["w4a4_gate_up"]
     bl = kernels["bf16_nt_gate_up_baseline"]
     res = {
         "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
@@ -484,7 +495,7 @@ def main():
         "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
                       "bf16_same_shape_tflops": bl.get("tflops"),
-                      "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3) if w4 else None},
+                      "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3)},
         "quantize": roofline_of("quantize_x_perm_cold"),
         "permute_quantize": roofline_of("permute_quantize_x"),
         "cpu_baseline": cpu,

@@ -73,6 +73,7 @@ typedef struct ihipStream_t* nvfp4moe_stream_t; /* == hipStream_t */
 
 /* W4A4 GEMM epilogues */
 #define NVFP4MOE_EPI_NONE 0
+#define NVFP4MOE_EPI_SILU_GATE 1 /* c receives H = silu(gate) * up, see below */
 
 /* ABI version of this header; returned by nvfp4moe_abi_version(). */
 #define NVFP4MOE_ABI_VERSION 1
@@ -202,15 +203,40 @@ int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const fl
  *   c [M_total][N] of c_dtype (F32/BF16)
  * K % 64 == 0 (every 64-element step holds whole 16-blocks and 4-byte
  * aligned scale words), N % 32 == 0; a_q, b_q, c 16-byte aligned, a_s, b_s
- * 4-byte aligned.  epilogue must be NVFP4MOE_EPI_NONE.  workspace may be
- * NULL (none needed).  Errors: EINVAL (NULL, negative, bad enum), ESHAPE
- * (the shape and alignment rules above).
+ * 4-byte aligned.  workspace may be NULL (none needed).
+ * epilogue NVFP4MOE_EPI_NONE: c as above.
+ * epilogue NVFP4MOE_EPI_SILU_GATE (the gate+up projection, B_e = [gate rows
+ * 0..F-1; up rows F..2F-1] with N = 2F): c receives only H [M_total][F]
+ * bf16 (c_dtype must be BF16), the SiLU gate of the bf16-rounded C exactly as
+ * silu_gate_fwd computes it, and amax_out[0] (may be NULL) = max |H|
+ * ([JA] fourth paragraph: op fusion, amax reuse).  N % 256 == 0.
+ * Errors: EINVAL (NULL, negative, bad enum), ESHAPE (the shape and
+ * alignment rules above).
  */
 int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
                       const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                       const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
                       void* c, int c_dtype, int epilogue, float* amax_out, void* workspace,
                       size_t ws_bytes, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_w4a4_silu_gate -- the gate+up W4A4 GEMM with the SiLU gate
+ * and the amax of its output in the epilogue ([JA] fourth paragraph: op
+ * fusion, amax reuse): the result equals grouped_gemm_w4a4 (N = 2F, bf16 C)
+ * followed by silu_gate_fwd, bit for bit, without re-reading Y1.
+ *   operands as grouped_gemm_w4a4 with N = 2F (B_e = [gate; up] rows)
+ *   y1 [M_total][2F] bf16 or NULL: Y1 is stored only when given (the BF16
+ *      backward needs it)
+ *   h  [M_total][F] bf16: H = silu(G) * U of the bf16 Y1, fp32 math
+ *   amax_out [1] fp32 or NULL: max |H| over the stored bf16 values
+ * F % 128 == 0, K % 64 == 0; y1, h 16-byte aligned.  Errors as
+ * grouped_gemm_w4a4.
+ */
+int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                const int32_t* expert_offsets, int E, int64_t M_total, int64_t F,
+                                int64_t K, void* y1, void* h, float* amax_out,
+                                nvfp4moe_stream_t stream);
 
 /*
  * grouped_gemm_bf16 -- grouped BF16 GEMM, fp32 accumulation (the BF16

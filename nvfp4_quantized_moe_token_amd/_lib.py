@@ -26,6 +26,8 @@ SIGNATURES = {
     "moe_unpermute": (c_int, [c_vp, c_int, c_vp, c_vp, c_i64, c_int, c_i64, c_vp, c_int, c_vp]),
     "grouped_gemm_w4a4": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
                                   c_vp, c_int, c_int, c_vp, c_vp, c_size, c_vp]),
+    "grouped_gemm_w4a4_silu_gate": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
+                                            c_vp, c_vp, c_vp, c_vp]),
     "grouped_gemm_bf16": (c_int, [c_int, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_int,
                                   c_vp, c_size, c_vp]),
     "silu_gate_fwd": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
@@ -36,7 +38,7 @@ SIGNATURES = {
 OK, EINVAL, ESHAPE, EARCH, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5
 F32, BF16, U8 = 0, 1, 2
 NT, NN, TN = 0, 1, 2
-EPI_NONE = 0
+EPI_NONE, EPI_SILU_GATE = 0, 1
 ABI_VERSION = 1
 STATUS_BAD_EXPERT = 1
 

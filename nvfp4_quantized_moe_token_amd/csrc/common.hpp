@@ -39,15 +39,23 @@ constexpr int kStreamBlocks = 256 * 8;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16 bits, round to nearest even (finite inputs): the gfx950
+// conversion instruction v_cvt_pk_bf16_f32, two values per instruction.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// SiLU gate of one element pair, fp32: silu(g) * u with silu(g) = g / (1 + e^-g)
+// evaluated as g * rcp(1 + e^-g) (hardware exp2 and reciprocal, about 1 ulp
+// each).  Shared by the standalone SiLU-gate kernels and the fused GEMM
+// epilogue so that both produce the same bits.
+__device__ __forceinline__ float sigmoid_f32(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_gate(float g, float u) { return g * sigmoid_f32(g) * u; }
 
 // Non-negative floats order like their bit patterns: max-reduce |x| with
 // unsigned integer atomics.

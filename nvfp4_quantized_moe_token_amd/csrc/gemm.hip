@@ -59,7 +59,9 @@ constexpr int NV_KS = 256;                   // reduction elements per NVFP4 sta
 constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
-enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3 };
+// W4A4_SILU: the W4A4 gate+up GEMM with the SiLU-gate epilogue.
+enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4 };
+constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU; }
 
 struct Params {
   const void* a;       // NT/NN/TN: bf16 A; W4A4: packed codes of A
@@ -76,6 +78,8 @@ struct Params {
   int accumulate;
   int n_tiles;         // tiles along N
   int k_tiles_tn;      // TN: tiles along K (rows of C_e)
+  void* h;             // W4A4_SILU: H [M][N/2] bf16 (c = Y1 or NULL)
+  float* amax;         // W4A4_SILU: max |H| (cleared before the launch), or NULL
 };
 
 // ---- small device helpers ----
@@ -189,14 +193,23 @@ __device__ bool find_row_block(const int32_t* __restrict__ off, int E, int64_t M
 // layout.  Offsets are relative to a range-checked operand region: offsets
 // at or past its end, or marked kOOB, read as zeros.
 
+// Gate+up tiles of the SiLU-gate epilogue: tile row r (of 256) is expert row
+// gate_f * ((r / 32) % 2) + j0 + 32 * (r / 64) + r % 32, so 32-row granules
+// alternate gate and up rows of the same 32 features; each wave's pair of
+// adjacent 32-column MFMA blocks then holds matching gate and up columns.
+__device__ __forceinline__ int64_t gate_up_row(int r, int64_t gate_f, int64_t j0) {
+  return ((r >> 5) & 1) * gate_f + j0 + ((r >> 6) << 5) + (r & 31);
+}
+
 // K-major bf16 tile of ROWS rows x 64 k; row r of the tile is row r of the
-// region, element k0 + k.  `ld` is the row pitch in elements.
+// region (or gate_up_row(r) when gate_f > 0), element k0 + k.  `ld` is the
+// row pitch in elements.
 template <int ROWS, int NW>
 struct KMajorLoader {
   static_assert(ROWS % (8 * NW) == 0, "K-major tile: rows per wave");
   static constexpr int N_INSTR = ROWS / (8 * NW);
   __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
-                                              int64_t k0, int64_t K) {
+                                              int64_t k0, int64_t K, int64_t gate_f = 0, int64_t j0 = 0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < N_INSTR; ++i) {
@@ -204,7 +217,8 @@ struct KMajorLoader {
       const int row = idx * 8 + (lane >> 3);
       const int c = (lane & 7) ^ kswz(row);
       const int64_t k = k0 + c * 8;
-      const uint32_t voff = k < K ? (uint32_t)((row * ld + k) * 2) : kOOB;
+      const int64_t grow = gate_f > 0 ? gate_up_row(row, gate_f, j0) : row;
+      const uint32_t voff = k < K ? (uint32_t)((grow * ld + k) * 2) : kOOB;
       dma16(r, lds + idx * 1024, voff);
     }
   }
@@ -332,7 +346,7 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // Wave-wide loads per pipeline step of one operand tile (A side or B side).
 template <int MODE, bool A_SIDE, int ROWS, int NW>
 constexpr int loads_per_wave() {
-  if constexpr (MODE == W4A4)
+  if constexpr (is_nv(MODE))
     return KMajorLoader<ROWS, NW>::N_INSTR;
   else if constexpr ((A_SIDE && MODE == TN_BF16) || (!A_SIDE && MODE != NT_BF16))
     return MNMajorLoader<ROWS, NW>::N_INSTR;
@@ -351,7 +365,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");
-  constexpr bool NV = MODE == W4A4;
+  constexpr bool NV = is_nv(MODE);
+  constexpr bool SILU = MODE == W4A4_SILU;
   // Reduction elements per pipeline stage: 64 for bf16 (128-byte rows);
   // 256 for NVFP4, so that each row brings a whole 128-byte line of codes
   // and 16 bytes of scales per stage.
@@ -444,11 +459,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
     } else if constexpr (MODE == TN_BF16) {
       rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
     } else {
-      const int64_t nv = p.N - n0 < BN ? p.N - n0 : BN;
-      const int64_t brow = (int64_t)expert * p.N + n0;
+      // SiLU-gate tiles gather gate and up rows: the region is the expert.
+      const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
+      const int64_t brow = (int64_t)expert * p.N + (SILU ? 0 : n0);
       rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
       rsb = make_rsrc(p.bs + brow * (p.K / 16), nv * (p.K / 16));
     }
+    const int64_t gate_f = SILU ? p.N / 2 : 0;
+    const int64_t j0 = n0 / 2;
 
     auto load_step = [&](int64_t kt, int stage) {
       const uint32_t st = smem_lds + stage * STAGE;
@@ -466,14 +484,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
         // bf16 tile of 64 16-bit units per row.
         KMajorLoader<BM, NW>::load(st, wid, ra, p.K / 4, k0 / 4, p.K / 4);
-        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K / 4, k0 / 4, p.K / 4);
+        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K / 4, k0 / 4, p.K / 4, gate_f, j0);
         // Scales: 16 bytes per row, 64 rows per load, A rows first.
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
           const int idx = wid + NW * i;
           const bool is_a = idx * 64 < BM;
           const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          dma16(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(row * (p.K / 16) + k0 / 16));
+          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0) : row;
+          dma16(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
         }
       }
     };
@@ -540,7 +559,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
                       acc[i][j] =
-                          __builtin_amdgcn_mfma_f32_32x32x16_f16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+                          __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[kk & 1][j], av[kk & 1][i], acc[i][j], 0, 0, 0);
                   // ~9 VALU per expanded fragment (scale decode, 4 converts, 4 multiplies)
                   if (kk + 1 < BK / 16) interleave_mfma_valu<NA * FN, (9 * (NA + FN) + NA * FN - 1) / (NA * FN)>();
                 }
@@ -571,7 +590,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                   acc[i][j] =
-                      __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1][i], bv[kk & 1][j], acc[i][j], 0, 0, 0);
+                      __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[kk & 1][j], av[kk & 1][i], acc[i][j], 0, 0, 0);
               if (kk + 1 < BK / 16)
                 interleave_mfma_ds<NA * FN, NRD>();
               else
@@ -583,33 +602,86 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       if (n_active > 0) compute(IntConst<FM>{});
     }
 
-    // Epilogue.  Lane layout of a 32x32 MFMA result (probed on the device):
-    // register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // Epilogue.  Register r of lane l of a 32x32 MFMA result holds result row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32 (probed on the device).  The
+    // MFMAs take the B fragment as their first operand, so the result is the
+    // transposed tile: lane l holds output row l%32 and, for g = 0..3, the
+    // four consecutive output columns 8*g + 4*(l/32) + 0..3 in registers
+    // 4g..4g+3 -- one 8-byte (bf16) or 16-byte (fp32) store each.
     float alpha = 1.0f;
-    if (MODE == W4A4) alpha = p.ag[0] * p.bg[expert];
+    if (NV) alpha = p.ag[0] * p.bg[expert];
     const int64_t ldc = p.N;
     float* C32 = reinterpret_cast<float*>(p.c);
     uint16_t* C16 = reinterpret_cast<uint16_t*>(p.c);
     const int64_t cbase = MODE == TN_BF16 ? (int64_t)expert * p.K * p.N : 0;
+    if constexpr (SILU) {
+      static_assert(BN == 256 && WTN % 64 == 0, "SiLU-gate tiles");
+      // SiLU gate on the tile: block pair (2jj, 2jj+1) holds gate and up of
+      // the same features.  Y1 is rounded to bf16 first, so H is the SiLU
+      // gate of the stored Y1, as the standalone kernel computes it.
+      uint16_t* Hp = reinterpret_cast<uint16_t*>(p.h);
+      const int64_t F = p.N / 2;
+      float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (row >= m_end) continue;
+#pragma unroll
+        for (int jj = 0; jj < FN / 2; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t f = j0 + wn * (WTN / 2) + jj * 32 + 8 * g + 4 * (lane >> 5);
+            const f32x16_t& ga = acc[i][2 * jj];
+            const f32x16_t& ua = acc[i][2 * jj + 1];
+            const uint32_t g01 = pack_bf16x2(ga[4 * g] * alpha, ga[4 * g + 1] * alpha);
+            const uint32_t g23 = pack_bf16x2(ga[4 * g + 2] * alpha, ga[4 * g + 3] * alpha);
+            const uint32_t u01 = pack_bf16x2(ua[4 * g] * alpha, ua[4 * g + 1] * alpha);
+            const uint32_t u23 = pack_bf16x2(ua[4 * g + 2] * alpha, ua[4 * g + 3] * alpha);
+            if (C16) {
+              *reinterpret_cast<uint2*>(C16 + row * ldc + f) = make_uint2(g01, g23);
+              *reinterpret_cast<uint2*>(C16 + row * ldc + F + f) = make_uint2(u01, u23);
+            }
+            const uint32_t h01 = pack_bf16x2(silu_gate(bf16_lo(g01), bf16_lo(u01)), silu_gate(bf16_hi(g01), bf16_hi(u01)));
+            const uint32_t h23 = pack_bf16x2(silu_gate(bf16_lo(g23), bf16_lo(u23)), silu_gate(bf16_hi(g23), bf16_hi(u23)));
+            *reinterpret_cast<uint2*>(Hp + row * F + f) = make_uint2(h01, h23);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(h01)), fabsf(bf16_hi(h01))),
+                               fmaxf(fabsf(bf16_lo(h23)), fabsf(bf16_hi(h23)))));
+          }
+      }
+      if (p.amax) {
+        m = wave_max(m);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(m));
+      }
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+      if (row >= m_end) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
-        if (col >= p.N) continue;
+        if (n0 + wn * WTN + j * 32 >= p.N) continue;  // N % 32 == 0: whole blocks
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row >= m_end) continue;
-          const float v = acc[i][j][r] * alpha;
-          const int64_t idx = cbase + row * ldc + col;
+        for (int g = 0; g < 4; ++g) {
+          const int64_t idx = cbase + row * ldc + n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const f32x16_t& a = acc[i][j];
+          float4 v = make_float4(a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha, a[4 * g + 3] * alpha);
           if (p.c_f32) {
-            C32[idx] = p.accumulate ? C32[idx] + v : v;
+            float4* dst = reinterpret_cast<float4*>(C32 + idx);
+            if (p.accumulate) {
+              const float4 o = *dst;
+              v.x += o.x;
+              v.y += o.y;
+              v.z += o.z;
+              v.w += o.w;
+            }
+            *dst = v;
           } else {
-            C16[idx] = (uint16_t)f32_to_bf16_rne(v);
+            *reinterpret_cast<uint2*>(C16 + idx) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
           }
         }
       }
+    }
   }
 }
 
@@ -669,10 +741,12 @@ constexpr int kForcedConfig = -1;
 #endif
 
 // Whether a configuration is valid for a layout: LDS within the 160 KiB of
-// a gfx950 CU, and whole loads per wave for NVFP4 tiles.
+// a gfx950 CU, whole loads per wave for NVFP4 tiles, and for the SiLU-gate
+// epilogue 256-column tiles whose wave halves are multiples of 64 columns.
 constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s) {
-  return s * (bm + bn) * (mode == W4A4 ? 144 : 128) <= 160 * 1024 &&
-         (mode != W4A4 || (bm + bn) % (64 * wm * wn) == 0);
+  return s * (bm + bn) * (is_nv(mode) ? 144 : 128) <= 160 * 1024 &&
+         (!is_nv(mode) || (bm + bn) % (64 * wm * wn) == 0) &&
+         (mode != W4A4_SILU || (bn == 256 && (bn / wn) % 64 == 0));
 }
 
 template <int MODE>
@@ -697,7 +771,8 @@ int pick_config(int mode, const Params& p) {
   // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
   // 256 x 256 tiles on 8 waves; W4A4 with 4 LDS stages (its tiles are small).
   switch (mode) {
-    case W4A4: return 1;
+    case W4A4:
+    case W4A4_SILU: return 1;
     default: return 1;
   }
 }
@@ -708,6 +783,7 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case NT_BF16: return launch_mode<NT_BF16>(cfg, p, st);
     case NN_BF16: return launch_mode<NN_BF16>(cfg, p, st);
     case TN_BF16: return launch_mode<TN_BF16>(cfg, p, st);
+    case W4A4_SILU: return launch_mode<W4A4_SILU>(cfg, p, st);
     default: return launch_mode<W4A4>(cfg, p, st);
   }
 }
@@ -717,25 +793,26 @@ int launch(int mode, const Params& p, hipStream_t st) {
 
 using namespace nvfp4moe;
 
-extern "C" int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q,
-                                 const uint8_t* b_s, const float* b_g, const int32_t* expert_offsets, int E,
-                                 int64_t M_total, int64_t N, int64_t K, void* c, int c_dtype, int epilogue,
-                                 float* amax_out, void* workspace, size_t ws_bytes, nvfp4moe_stream_t stream) {
-  (void)amax_out;
-  (void)workspace;
-  (void)ws_bytes;
+namespace {
+
+// Shared by both W4A4 entry points.  silu: c = Y1 (NULL: not stored), h = H.
+int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q, const uint8_t* b_s,
+               const float* b_g, const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
+               void* c, int c_dtype, int silu, void* h, float* amax_out, hipStream_t st) {
   if (E < 1 || M_total < 0 || N < 0 || K < 0) return NVFP4MOE_EINVAL;
   if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
-  if (epilogue != NVFP4MOE_EPI_NONE) return NVFP4MOE_EINVAL;
+  if (silu && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
   if (!expert_offsets || !a_g || !b_g) return NVFP4MOE_EINVAL;
-  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || !c)) return NVFP4MOE_EINVAL;
+  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h : !c))) return NVFP4MOE_EINVAL;
   if (K % 64 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (silu && N % 256 != 0) return NVFP4MOE_ESHAPE;
   if (M_total > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
-      !aligned(c, 16))
+      !aligned(c, 16) || !aligned(h, 16))
     return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
-  if (M_total == 0 || N == 0) return NVFP4MOE_OK;
+  if (silu && amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+  if (M_total == 0 || N == 0) return launch_status();
   Params p = {};
   p.a = a_q;
   p.b = b_q;
@@ -750,7 +827,35 @@ extern "C" int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const f
   p.K = K;
   p.E = E;
   p.c_f32 = c_dtype == NVFP4MOE_F32;
-  return launch(W4A4, p, as_stream(stream));
+  p.h = h;
+  p.amax = amax_out;
+  return launch(silu ? W4A4_SILU : W4A4, p, st);
+}
+
+}  // namespace
+
+extern "C" int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q,
+                                 const uint8_t* b_s, const float* b_g, const int32_t* expert_offsets, int E,
+                                 int64_t M_total, int64_t N, int64_t K, void* c, int c_dtype, int epilogue,
+                                 float* amax_out, void* workspace, size_t ws_bytes, nvfp4moe_stream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (epilogue == NVFP4MOE_EPI_NONE)
+    return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, N, K, c, c_dtype, 0, nullptr,
+                      nullptr, as_stream(stream));
+  if (epilogue == NVFP4MOE_EPI_SILU_GATE)
+    return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, N, K, nullptr, c_dtype, 1, c,
+                      amax_out, as_stream(stream));
+  return NVFP4MOE_EINVAL;
+}
+
+extern "C" int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                           const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                           const int32_t* expert_offsets, int E, int64_t M_total, int64_t F,
+                                           int64_t K, void* y1, void* h, float* amax_out, nvfp4moe_stream_t stream) {
+  if (F < 0) return NVFP4MOE_EINVAL;
+  return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h,
+                    amax_out, as_stream(stream));
 }
 
 extern "C" int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* expert_offsets, int E,

@@ -7,8 +7,6 @@
 namespace nvfp4moe {
 namespace {
 
-__device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
-
 __global__ __launch_bounds__(256) void silu_fwd_kernel(const uint16_t* __restrict__ y1, int64_t R, int64_t F,
                                                        uint16_t* __restrict__ h, float* __restrict__ amax_out) {
   const int64_t n8 = F / 8;
@@ -23,8 +21,8 @@ __global__ __launch_bounds__(256) void silu_fwd_kernel(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float g0 = bf16_lo(g[j]), g1 = bf16_hi(g[j]);
-      const float h0 = g0 * sigmoid(g0) * bf16_lo(u[j]);
-      const float h1 = g1 * sigmoid(g1) * bf16_hi(u[j]);
+      const float h0 = silu_gate(g0, bf16_lo(u[j]));
+      const float h1 = silu_gate(g1, bf16_hi(u[j]));
       o[j] = pack_bf16x2(h0, h1);
       m = fmaxf(m, fmaxf(fabsf(bf16_lo(o[j])), fabsf(bf16_hi(o[j]))));
     }
@@ -51,7 +49,7 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const uint16_t* __restric
       float rg[2], ru[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const float sg = sigmoid(gg[q]);
+        const float sg = sigmoid_f32(gg[q]);
         const float dsilu = sg * (1.0f + gg[q] * (1.0f - sg));
         rg[q] = dd[q] * uu[q] * dsilu;
         ru[q] = dd[q] * gg[q] * sg;

@@ -6,9 +6,11 @@ Forward ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragra
 contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
   moe_permute_nvfp4 (amax of X once, metadata, gather fused with the NVFP4
   quantization of the gathered rows; the bf16 rows are kept only for the
-  backward)  ->  grouped_gemm_w4a4 (gate+up)  ->  silu_gate_fwd (+amax of H)
-  ->  nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)  ->
-  moe_unpermute (routing-weighted combine).
+  backward)  ->  grouped_gemm_w4a4_silu_gate (gate+up with the SiLU gate and
+  the amax of H in its epilogue; Y1 is stored only for the backward)  ->
+  nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)  ->
+  moe_unpermute (routing-weighted combine).  When F is not a multiple of 128
+  the gate+up GEMM and silu_gate_fwd run as two launches.
 Backward in BF16 (same page, first paragraph), no amax reduction at all:
   moe_gather(dY, weighted)  ->  NN dgrad / TN wgrad of the down projection
   ->  silu_gate_bwd  ->  NN dgrad / TN wgrad of gate+up  ->  moe_unpermute
@@ -55,17 +57,22 @@ class Buffers:
             self.dw_gu = e(E, 2 * F, D, dt=f32)
 
 
-def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True):
+def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=True):
     """W4A4 MoE forward; returns the routing metadata dict.  The bf16
-    permuted rows (buf.x_perm) are written only when keep_x_perm (the BF16
-    backward's weight gradient needs them)."""
+    permuted rows (buf.x_perm) and Y1 (buf.y1) are written only when
+    keep_x_perm (the BF16 backward needs them)."""
     E = buf.E
     meta = ops.moe_permute_nvfp4(topk_ids, E, x, x_perm=buf.x_perm if keep_x_perm else None,
                                  want_x_perm=keep_x_perm, amax_out=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
                                  gscale=buf.a1_g, workspace=buf.ws)
-    ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], meta["offsets"],
-                          out=buf.y1)
-    ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])
+    wgu = (wq_gu["q"], wq_gu["s"], wq_gu["g"])
+    if fuse_silu and buf.F % 128 == 0:
+        ops.grouped_gemm_w4a4_silu_gate(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"],
+                                        y1=buf.y1 if keep_x_perm else None, want_y1=keep_x_perm, h=buf.h,
+                                        amax_out=buf.amax[1:2])
+    else:
+        ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"], out=buf.y1)
+        ops.silu_gate_fwd(buf.y1, h=buf.h, amax_out=buf.amax[1:2])
     ops.nvfp4_quantize(buf.h, amax_in=buf.amax[1:2], q=buf.a2_q, scales=buf.a2_s, gscale=buf.a2_g)
     ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"], wq_dn["g"], meta["offsets"],
                           out=buf.y2)

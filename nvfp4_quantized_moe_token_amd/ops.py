@@ -170,6 +170,28 @@ def grouped_gemm_w4a4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out=None, out_dtype
     return out
 
 
+def grouped_gemm_w4a4_silu_gate(a_q, a_s, a_g, b_q, b_s, b_g, offsets, y1=None, want_y1=True, h=None,
+                                amax_out=None, want_amax=True):
+    """Gate+up W4A4 GEMM with the SiLU gate (and amax of H) in its epilogue.
+    B_e = [gate; up] rows.  Returns (y1 or None, h, amax or None)."""
+    _dev(a_q, a_s, a_g, b_q, b_s, b_g, offsets, y1, h, amax_out)
+    M = a_q.shape[0]
+    K = a_q.shape[1] * 2
+    E, N = b_q.shape[0], b_q.shape[1]
+    F = N // 2
+    dev = a_q.device
+    if y1 is None and want_y1:
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev) if h is None else h
+    if amax_out is None and want_amax:
+        amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rc = _lib.load().grouped_gemm_w4a4_silu_gate(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g),
+                                                 _ptr(offsets), E, M, F, K, _ptr(y1), _ptr(h), _ptr(amax_out),
+                                                 _stream())
+    _check("grouped_gemm_w4a4_silu_gate", rc)
+    return y1, h, amax_out
+
+
 def grouped_gemm_bf16(layout, a, b, offsets, num_experts=None, out=None, out_dtype=torch.float32, accumulate=False):
     """Grouped BF16 GEMM; layout NT / NN / TN as in the C header."""
     _dev(a, b, offsets, out)

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
-              "grouped_gemm_w4a4", "grouped_gemm_bf16", "silu_gate_fwd", "silu_gate_bwd",
+              "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "silu_gate_fwd",
+              "silu_gate_bwd", "moe_permute_nvfp4",
               "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
         assert n in names
 
@@ -128,8 +129,12 @@ def test_gemm_validation(lib):
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None, None, 0, None]
     bad = list(args); bad[12] = 9
     assert g(*bad) == -1                       # dtype
+    bad = list(args); bad[13] = 2
+    assert g(*bad) == -1                       # unknown epilogue
     bad = list(args); bad[13] = 1
-    assert g(*bad) == -1                       # epilogue
+    assert g(*bad) == -1                       # SiLU-gate epilogue needs a bf16 H
+    bad = list(args); bad[13] = 1; bad[12] = 1
+    assert g(*bad) == -2                       # SiLU-gate epilogue: N % 256
     bad = list(args); bad[10] = 48
     assert g(*bad) == -2                       # K % 64
     bad = list(args); bad[10] = 96
@@ -143,6 +148,23 @@ def test_gemm_validation(lib):
     assert b(0, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 1, 1, None, 0, None) == -1  # accumulate bf16
     assert b(1, FAKE, FAKE, FAKE, 4, 64, 64, 48, FAKE, 0, 0, None, 0, None) == -2
     assert b(2, FAKE + 8, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None, 0, None) == -2
+
+
+def test_gemm_silu_gate_validation(lib):
+    g = lib.grouped_gemm_w4a4_silu_gate
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 64, FAKE, FAKE, None, None]
+    bad = list(args); bad[12] = None
+    assert g(*bad) == -1                       # H is required
+    bad = list(args); bad[9] = -1
+    assert g(*bad) == -1                       # F < 0
+    bad = list(args); bad[9] = 96
+    assert g(*bad) == -2                       # F % 128
+    bad = list(args); bad[10] = 96
+    assert g(*bad) == -2                       # K % 64
+    bad = list(args); bad[11] = FAKE + 8
+    assert g(*bad) == -2                       # Y1 alignment
+    bad = list(args); bad[12] = FAKE + 2
+    assert g(*bad) == -2                       # H alignment
 
 
 def test_silu_validation(lib):
