@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.0   # dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_GHZ = 2.4        # the clock the published MFMA peaks assume
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_moe_8k_update.txt")
 CALIB_BYTES = 1 << 30       # the plain copy that calibrates the traffic counters
 
@@ -193,7 +194,9 @@ def load_traffic():
             if len(parts) >= 2 and parts[0] == "sources":
                 digest = parts[1]
             elif len(parts) >= 7 and parts[0] == "op":
-                out[parts[1]] = dict(fetch=float(parts[3]), write=float(parts[5]))
+                out.setdefault(parts[1], {}).update(fetch=float(parts[3]), write=float(parts[5]))
+            elif len(parts) == 3 and parts[0] == "clock":
+                out.setdefault(parts[1], {})["clock_ghz"] = float(parts[2])
     return out if digest == source_digest() else {}
 
 
@@ -204,7 +207,7 @@ def short_name(n):
     return n.split("(")[0].replace(" ", "")
 
 
-def pmc_summary(fetch_dir, write_dir):
+def pmc_summary(fetch_dir, write_dir, clock_dir=None):
     """Turn two rocprofv3 --pmc runs of `bench.py --pmc-run` (FETCH_SIZE,
     then WRITE_SIZE; counters in KiB per dispatch) into per-op HBM bytes of
     the last step, scaled by what the counters read for a plain 1 GiB copy.
@@ -212,8 +215,8 @@ def pmc_summary(fetch_dir, write_dir):
     so an op's dispatches are the ones between two markers."""
     import csv
 
-    def read(d, counter):
-        rows = {}
+    def read(d, counter, with_ns=False):
+        rows, ns = {}, {}
         for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
             with open(p) as f:
                 for r in csv.DictReader(f):
@@ -221,6 +224,9 @@ def pmc_summary(fetch_dir, write_dir):
                         i = int(r["Dispatch_Id"])
                         v = rows.get(i, (r["Kernel_Name"], 0.0))[1] + float(r["Counter_Value"])
                         rows[i] = (r["Kernel_Name"], v)
+                        ns[i] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        if with_ns:
+            return [(rows[i][0], rows[i][1], ns[i]) for i in sorted(rows)]
         return [rows[i] for i in sorted(rows)]
 
     def per_op(rows):
@@ -242,11 +248,25 @@ def pmc_summary(fetch_dir, write_dir):
              "# fetch x%.4f, write x%.4f.  Bytes per launch; 'sources' fingerprints the HIP sources (code, comments removed)." % (sf, sw),
              "# commands: cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
              "-d $REPO/gpurun_out/pmc_fetch -o run -- python $REPO/bench.py --pmc-run --steps 2 --warmup 1",
-             "#   (the same with WRITE_SIZE into $REPO/gpurun_out/pmc_write), then",
-             "#   python $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write",
+             "#   (the same with WRITE_SIZE into $REPO/gpurun_out/pmc_write and with GRBM_GUI_ACTIVE into",
+             "#   $REPO/gpurun_out/pmc_clock), then python $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch",
+             "#   $REPO/gpurun_out/pmc_write $REPO/gpurun_out/pmc_clock",
              "sources %s" % source_digest()]
     for (name, fb, kn), (_, wb, _) in zip(fetch, write):
         lines.append("op %s fetch %.0f write %.0f kernels %s" % (name, fb * sf, wb * sw, ";".join(kn)))
+    if clock_dir:
+        # GRBM_GUI_ACTIVE counts GPU-busy cycles summed over the 8 XCDs; per
+        # op, cycles / 8 / the dispatches' own duration is the shader clock
+        # the op ran at.
+        rows = read(clock_dir, "GRBM_GUI_ACTIVE", with_ns=True)
+        marks = [i for i, r in enumerate(rows) if MARKER in r[0]][-(len(STEP_OPS) + 1):]
+        lines.append("# sustained shader clock per op: GRBM_GUI_ACTIVE / 8 XCDs / dispatch time "
+                     "(a third --pmc run with GRBM_GUI_ACTIVE)")
+        for j, name in enumerate(STEP_OPS):
+            seg = [r for r in rows[marks[j] + 1:marks[j + 1]] if r[2] > 0]
+            cyc, ns = sum(r[1] for r in seg), sum(r[2] for r in seg)
+            if ns > 0:
+                lines.append("clock %s %.3f" % (name, cyc / 8.0 / ns))
     print("\n".join(lines))
 
 
@@ -289,7 +309,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: steps only, then a 1 GiB calibration copy")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="FETCH_SIZE and WRITE_SIZE run directories, optionally a GRBM_GUI_ACTIVE one")
     ap.add_argument("--kernel-stats-summary", metavar="DIR")
     args = ap.parse_args()
     if args.pmc_summary:
@@ -429,21 +450,43 @@ def main():
                 ent["frac_fp4_mfma_peak"] = round(ent["tflops"] / PEAK_FP4_TFLOPS, 4)
         ent["gbs"] = round(by / (ms * 1e-3) / 1e9, 1)
         ent["frac_hbm_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
-        if name in traffic:
-            ent["hbm_bytes_measured"] = traffic[name]["fetch"] + traffic[name]["write"]
+        tr = traffic.get(name, {})
+        if "fetch" in tr:
+            ent["hbm_bytes_measured"] = tr["fetch"] + tr["write"]
             ent["hbm_bytes_algorithmic"] = by
+        if "clock_ghz" in tr:
+            ent["sustained_clock_ghz"] = tr["clock_ghz"]
+            if fl:
+                ent["frac_bf16_peak_at_sustained_clock"] = round(
+                    ent["tflops"] / (PEAK_BF16_TFLOPS * tr["clock_ghz"] / PEAK_CLOCK_GHZ), 4)
         kernels[name] = ent
+
+    def traffic_bytes(names):
+        tr = [traffic.get(o, {}) for o in names]
+        if not all("fetch" in t for t in tr):
+            return None
+        return round(sum(t["fetch"] + t["write"] for t in tr) / len(names))
+
+    def clock_fields(names, ach):
+        """Sustained clock of the ops (time-weighted) and the fraction of the
+        bf16 MFMA peak scaled to that clock."""
+        tr = [traffic.get(o, {}) for o in names]
+        if not names or not all("clock_ghz" in t for t in tr):
+            return {}
+        w = [per_op.get(o, per_op_extra.get(o, 0.0)) for o in names]
+        clk = sum(t["clock_ghz"] * wi for t, wi in zip(tr, w)) / sum(w)
+        return {"sustained_clock_ghz": round(clk, 3),
+                "frac_at_sustained_clock": round(ach / (PEAK_BF16_TFLOPS * clk / PEAK_CLOCK_GHZ), 4)}
 
     def roofline_of(name):
         ms = per_op[name] if name in per_op else per_op_extra[name]
         fl, by = op_work(name, T, k, E, D, F)
-        tr = traffic.get(name)
-        tr_bytes = None if tr is None else round(tr["fetch"] + tr["write"])
+        tr_bytes = traffic_bytes([name])
         if fl:
             ach = fl / (ms * 1e-3) / 1e12
             return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": tr_bytes,
-                    "algorithmic_bytes": by, "ms": round(ms, 4)}
+                    "algorithmic_bytes": by, "ms": round(ms, 4), **clock_fields([name], ach)}
         ach = by / (ms * 1e-3) / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": tr_bytes, "ms": round(ms, 4)}
@@ -456,12 +499,11 @@ def main():
         ms = sum(per_op[o] for o in names) / n
         fl = sum(op_work(o, T, k, E, D, F)[0] for o in names) / n
         by = sum(op_work(o, T, k, E, D, F)[1] for o in names) / n
-        tr = [traffic.get(o) for o in names]
-        tr_bytes = None if None in tr else round(sum(t["fetch"] + t["write"] for t in tr) / n)
         ach = fl / (ms * 1e-3) / 1e12
         return {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": tr_bytes, "algorithmic_bytes": round(by), "avg_launch_ms": round(ms, 4)}
+                "traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "avg_launch_ms": round(ms, 4),
+                **clock_fields(names, ach)}
 
     # Dominant kernel: the largest share of the step's time.
     per_kernel = {}
