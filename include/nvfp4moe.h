@@ -210,8 +210,8 @@ int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const fl
  * bf16 (c_dtype must be BF16), the SiLU gate of the bf16-rounded C exactly as
  * silu_gate_fwd computes it, and amax_out[0] (may be NULL) = max |H|
  * ([JA] fourth paragraph: op fusion, amax reuse).  N % 256 == 0.
- * Errors: EINVAL (NULL, negative, bad enum), ESHAPE (the shape and
- * alignment rules above).
+ * M_total, N, K < 2^31.  Errors: EINVAL (NULL, negative, bad enum), ESHAPE
+ * (the shape and alignment rules above).
  */
 int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
                       const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
@@ -251,7 +251,8 @@ int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const fl
  * beyond offsets[E] are not written (NT/NN).  K % 32 == 0 and N % 32 == 0
  * (TN: K % 32 == 0, N % 32 == 0; M_e arbitrary); 16-byte aligned pointers.
  * Operands are read through 32-bit buffer offsets: NN needs K*N*2 < 2^31,
- * TN needs M_total*K*2 and M_total*N*2 < 2^31 (else ESHAPE).
+ * TN needs M_total*K*2 and M_total*N*2 < 2^31; M_total, N, K < 2^31 (else
+ * ESHAPE).
  * workspace may be NULL.
  */
 int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* expert_offsets,

@@ -112,8 +112,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // address lds + size*l (lds wave-uniform).  Issued as inline assembly so the
 // compiler does not make every later LDS read wait for it: the kernel keeps
 // the count of its own loads (s_waitcnt vmcnt) and orders LDS with barriers.
+// `lds` goes through readfirstlane: under register pressure the compiler may
+// hold a uniform value in a vector register, which the scalar operand cannot
+// take (a no-op when it is already scalar).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(
+                   __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(r)
                : "memory", "m0");
 }
 // K-major bf16 tile: chunk c (8 elements) of row r at byte r*128 + 16*(c ^ kswz(r)).
@@ -360,7 +365,7 @@ struct IntConst {
 };
 // ---- the kernel ----
 
-template <int MODE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
@@ -654,6 +659,71 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       }
       continue;
     }
+    // The wave's results leave through a private LDS region (the stage ring
+    // is free once every wave is past its last step): each 32-row block is
+    // written in the register layout above and read back by rows, so that
+    // every global store instruction writes whole 128-byte lines of
+    // consecutive rows (16 bytes per lane) instead of 32 partial lines.
+    // (The W4A4 kernel stores directly: staging costs it register spills.)
+    constexpr int REGION = 32 * WTN * 4;  // one 32-row block in fp32
+    if constexpr (MODE != W4A4 && NW * REGION <= S * STAGE && WTN % 32 == 0) {
+      lds_barrier();
+      uint8_t* reg = smem + wid * REGION;
+      const int q = lane & 31, h = lane >> 5;
+      const int64_t col0 = n0 + wn * WTN;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t row0 = m0 + wm * WTM + i * 32;
+        if constexpr (OUT32) {
+          constexpr int CH = WTN / 4;  // 16-byte chunks per row
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x16_t& a = acc[i][j];
+              const int ch = j * 8 + 2 * g + h;
+              *reinterpret_cast<float4*>(reg + q * (WTN * 4) + ((ch ^ (q & (CH - 1))) << 4)) =
+                  make_float4(a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha, a[4 * g + 3] * alpha);
+            }
+#pragma unroll 2
+          for (int t = 0; t < 32 * CH / 64; ++t) {
+            const int r = t * (64 / CH) + lane / CH, ch = lane % CH;
+            float4 v = *reinterpret_cast<const float4*>(reg + r * (WTN * 4) + ((ch ^ (r & (CH - 1))) << 4));
+            const int64_t row = row0 + r, col = col0 + ch * 4;
+            if (row < m_end && col < p.N) {
+              float4* dst = reinterpret_cast<float4*>(C32 + cbase + row * ldc + col);
+              if (p.accumulate) {
+                const float4 o = *dst;
+                v.x += o.x;
+                v.y += o.y;
+                v.z += o.z;
+                v.w += o.w;
+              }
+              *dst = v;
+            }
+          }
+        } else {
+          constexpr int CH = WTN / 8;  // 16-byte chunks (8 bf16) per row
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x16_t& a = acc[i][j];
+              const int ch = j * 4 + g;
+              *reinterpret_cast<uint2*>(reg + q * (WTN * 2) + ((ch ^ (q & (CH - 1))) << 4) + 8 * h) =
+                  make_uint2(pack_bf16x2(a[4 * g] * alpha, a[4 * g + 1] * alpha),
+                             pack_bf16x2(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha));
+            }
+#pragma unroll 2
+          for (int t = 0; t < 32 * CH / 64; ++t) {
+            const int r = t * (64 / CH) + lane / CH, ch = lane % CH;
+            const uint4 v = *reinterpret_cast<const uint4*>(reg + r * (WTN * 2) + ((ch ^ (r & (CH - 1))) << 4));
+            const int64_t row = row0 + r, col = col0 + ch * 8;
+            if (row < m_end && col < p.N) *reinterpret_cast<uint4*>(C16 + cbase + row * ldc + col) = v;
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
@@ -666,7 +736,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
           const int64_t idx = cbase + row * ldc + n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
           const f32x16_t& a = acc[i][j];
           float4 v = make_float4(a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha, a[4 * g + 3] * alpha);
-          if (p.c_f32) {
+          if constexpr (OUT32) {
             float4* dst = reinterpret_cast<float4*>(C32 + idx);
             if (p.accumulate) {
               const float4 o = *dst;
@@ -682,17 +752,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
         }
       }
     }
+    }
   }
 }
 
 // Resident workgroups per CU of one kernel instantiation (cached; the same on
 // every gfx950 device).
-template <int MODE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
 int resident_per_cu() {
   static int cached = 0;
   if (cached > 0) return cached;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel<MODE, BM, BN, WM, WN, S>, WM * WN * 64, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel<MODE, BM, BN, WM, WN, S, OUT32>, WM * WN * 64,
+                                                   0) !=
           hipSuccess ||
       occ < 1)
     occ = 1;
@@ -700,7 +772,7 @@ int resident_per_cu() {
   return occ;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int S>
+template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
 int launch_cfg(const Params& p0, hipStream_t st) {
   Params p = p0;
   p.n_tiles = (int)cdiv(p.N, BN);
@@ -713,16 +785,17 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   }
   if (upper <= 0) return NVFP4MOE_OK;
   if (upper > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
-  int64_t grid = (int64_t)device_cu_count() * resident_per_cu<MODE, BM, BN, WM, WN, S>();
+  int64_t grid = (int64_t)device_cu_count() * resident_per_cu<MODE, BM, BN, WM, WN, S, OUT32>();
   if (grid > upper) grid = upper;
   grid = cdiv(grid, 8) * 8;  // whole XCD rounds
-  gemm_kernel<MODE, BM, BN, WM, WN, S><<<(unsigned)grid, WM * WN * 64, 0, st>>>(p);
+  gemm_kernel<MODE, BM, BN, WM, WN, S, OUT32><<<(unsigned)grid, WM * WN * 64, 0, st>>>(p);
   return launch_status();
 }
 
 // Tile configurations: (BM, BN, waves along M, waves along N, LDS stages).
-// A build for tuning sweeps may force one with -DNVFP4MOE_GEMM_FORCE_CONFIG=<i>
-// (then only that one is compiled).
+// Only the configuration pick_config chooses (kDefaultConfig) is compiled; a
+// build for tuning sweeps may force another with
+// -DNVFP4MOE_GEMM_FORCE_CONFIG=<i>.
 #define NVFP4MOE_GEMM_CONFIGS(X) \
   X(0, 256, 256, 2, 4, 2)        \
   X(1, 256, 256, 4, 2, 2)        \
@@ -734,11 +807,15 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   X(7, 256, 256, 2, 2, 2)        \
   X(8, 128, 128, 2, 2, 2)
 
+// Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
+// 256 x 256 tiles on 8 waves (4 x 2) with two LDS stages, for every layout.
+constexpr int kDefaultConfig = 1;
 #ifdef NVFP4MOE_GEMM_FORCE_CONFIG
 constexpr int kForcedConfig = NVFP4MOE_GEMM_FORCE_CONFIG;
 #else
 constexpr int kForcedConfig = -1;
 #endif
+constexpr int kBuiltConfig = kForcedConfig >= 0 ? kForcedConfig : kDefaultConfig;
 
 // Whether a configuration is valid for a layout: LDS within the 160 KiB of
 // a gfx950 CU, whole loads per wave for NVFP4 tiles, and for the SiLU-gate
@@ -754,8 +831,13 @@ int launch_mode(int cfg, const Params& p, hipStream_t st) {
   switch (cfg) {
 #define NVFP4MOE_CASE(I, BM_, BN_, WM_, WN_, S_)                                               \
   case I:                                                                                      \
-    if constexpr ((kForcedConfig < 0 || kForcedConfig == I) && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_)) \
-      return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_>(p, st);                                  \
+    if constexpr (kBuiltConfig == I && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_)) {                  \
+      if (p.c_f32) {                                                                           \
+        if constexpr (MODE != W4A4_SILU) return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, true>(p, st); \
+      } else {                                                                                 \
+        return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, false>(p, st);                         \
+      }                                                                                        \
+    }                                                                                          \
     break;
     NVFP4MOE_GEMM_CONFIGS(NVFP4MOE_CASE)
 #undef NVFP4MOE_CASE
@@ -764,17 +846,11 @@ int launch_mode(int cfg, const Params& p, hipStream_t st) {
   return NVFP4MOE_ESHAPE;
 }
 
-// Tile configuration per layout and shape.
+// Tile configuration per layout and shape (one for all, see kDefaultConfig).
 int pick_config(int mode, const Params& p) {
+  (void)mode;
   (void)p;
-  if (kForcedConfig >= 0) return kForcedConfig;
-  // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
-  // 256 x 256 tiles on 8 waves; W4A4 with 4 LDS stages (its tiles are small).
-  switch (mode) {
-    case W4A4:
-    case W4A4_SILU: return 1;
-    default: return 1;
-  }
+  return kBuiltConfig;
 }
 
 int launch(int mode, const Params& p, hipStream_t st) {
@@ -806,7 +882,8 @@ int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const u
   if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h : !c))) return NVFP4MOE_EINVAL;
   if (K % 64 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
   if (silu && N % 256 != 0) return NVFP4MOE_ESHAPE;
-  if (M_total > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+  if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) ||
+      !aligned(a_s, 4) || !aligned(b_s, 4) ||
       !aligned(c, 16) || !aligned(h, 16))
     return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
@@ -872,7 +949,9 @@ extern "C" int grouped_gemm_bf16(int layout, const void* a, const void* b, const
   const bool has_out = layout == NVFP4MOE_TN ? (K > 0 && N > 0) : (M_total > 0 && N > 0);
   if (has_out && (!c || (M_total > 0 && (!a || !b)))) return NVFP4MOE_EINVAL;
   if (K % 32 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
-  if (M_total > 0x7FFFFFFFLL || !aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return NVFP4MOE_ESHAPE;
+  if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a, 16) || !aligned(b, 16) ||
+      !aligned(c, 16))
+    return NVFP4MOE_ESHAPE;
   // Buffer offsets are 32-bit: one expert's operand must stay below 2 GiB.
   if (layout == NVFP4MOE_NN && K * N * 2 >= (1LL << 31)) return NVFP4MOE_ESHAPE;
   if (layout == NVFP4MOE_TN && (M_total * K * 2 >= (1LL << 31) || M_total * N * 2 >= (1LL << 31)))
