@@ -261,7 +261,8 @@ def pmc_summary(fetch_dir, write_dir, clock_dir=None):
         rows = read(clock_dir, "GRBM_GUI_ACTIVE", with_ns=True)
         marks = [i for i, r in enumerate(rows) if MARKER in r[0]][-(len(STEP_OPS) + 1):]
         lines.append("# sustained shader clock per op: GRBM_GUI_ACTIVE / 8 XCDs / dispatch time "
-                     "(a third --pmc run with GRBM_GUI_ACTIVE)")
+                     "(a third --pmc run with GRBM_GUI_ACTIVE); meaningful for the GEMMs (hundreds of us),")
+        lines.append("# while short kernels read high (the counter window is wider than the kernel)")
         for j, name in enumerate(STEP_OPS):
             seg = [r for r in rows[marks[j] + 1:marks[j + 1]] if r[2] > 0]
             cyc, ns = sum(r[1] for r in seg), sum(r[2] for r in seg)
