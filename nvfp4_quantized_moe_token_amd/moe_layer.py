@@ -12,9 +12,9 @@ contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
   moe_unpermute (routing-weighted combine).  When F is not a multiple of 128
   the gate+up GEMM and silu_gate_fwd run as two launches.
 Backward in BF16 (same page, first paragraph), no amax reduction at all:
-  moe_gather(dY, weighted)  ->  NN dgrad / TN wgrad of the down projection
-  ->  silu_gate_bwd  ->  NN dgrad / TN wgrad of gate+up  ->  moe_unpermute
-  (unweighted sum back to tokens).
+  moe_gather(dY, weighted)  ->  NN dgrad of the down projection  ->
+  silu_gate_bwd  ->  TN wgrad of the down projection  ->  NN dgrad of gate+up
+  ->  moe_unpermute (unweighted sum back to tokens)  ->  TN wgrad of gate+up.
 """
 
 import torch
@@ -81,12 +81,14 @@ def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=
 
 
 def backward(dy, topk_w, w_gu, w_dn, meta, buf):
-    """BF16 backward of ``forward`` (weight gradients in fp32)."""
+    """BF16 backward of ``forward`` (weight gradients in fp32).  Each
+    elementwise consumer runs right after its producer, before a weight-
+    gradient GEMM streams its fp32 output through the caches."""
     ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
     off = meta["offsets"]
     ops.grouped_gemm_bf16(ops.NN, buf.dy2, w_dn, off, out=buf.dh)
-    ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, off, out=buf.dw_dn)
     ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
+    ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, off, out=buf.dw_dn)
     ops.grouped_gemm_bf16(ops.NN, buf.dy1, w_gu, off, out=buf.dx_perm)
-    ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, off, out=buf.dw_gu)
     ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
+    ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, off, out=buf.dw_gu)
