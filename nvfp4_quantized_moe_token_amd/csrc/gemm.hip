@@ -286,17 +286,19 @@ __device__ __forceinline__ bf16x8_t frag_mnmajor(const uint8_t* tile, int base, 
 
 // NVFP4 fragment of 64-element chunk c of a stage: the lane's 32 codes (row
 // base + lane % 32, k in [64c + 32h, 64c + 32h + 32), h = lane / 32) and its
-// two block scales.  Code rows are 128 bytes (16-byte units swizzled like
-// the K-major bf16 tile), scale rows 16 bytes.
+// two block scales, decoded E4M3 -> fp16 (exact) by one packed conversion.
+// Code rows are 128 bytes (16-byte units swizzled like the K-major bf16
+// tile), scale rows 16 bytes.
 struct NVFrag {
   uint4 q;
-  uint32_t s;  // low byte: block 4c+2h, next byte: block 4c+2h+1
+  f16x2_t sc;  // scales of blocks 4c+2h (x) and 4c+2h+1 (y)
 };
 __device__ __forceinline__ NVFrag frag_nv(const uint8_t* codes, const uint8_t* scales, int base, int c, int lane) {
   const int row = base + (lane & 31), h = lane >> 5;
   NVFrag f;
   f.q = *reinterpret_cast<const uint4*>(codes + row * 128 + (((2 * c + h) ^ kswz(row)) << 4));
-  f.s = *reinterpret_cast<const uint16_t*>(scales + row * 16 + 4 * c + 2 * h);
+  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales + row * 16 + 4 * c + 2 * h);
+  f.sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s2, 1.0f, false);
   return f;
 }
 __device__ __forceinline__ uint32_t nv_pair(uint32_t w, f16x2_t sc, int sel) {
@@ -313,8 +315,7 @@ __device__ __forceinline__ uint32_t nv_pair(uint32_t w, f16x2_t sc, int sel) {
 // MFMA operand kk (k = 32h + 8kk + 0..7): 8 codes expanded exactly to fp16.
 __device__ __forceinline__ f16x8_t nv_expand(const NVFrag& f, int kk) {
   const uint32_t w = kk == 0 ? f.q.x : kk == 1 ? f.q.y : kk == 2 ? f.q.z : f.q.w;
-  const _Float16 s =
-      (_Float16)(kk < 2 ? __builtin_amdgcn_cvt_f32_fp8((int)f.s, 0) : __builtin_amdgcn_cvt_f32_fp8((int)f.s, 1));
+  const _Float16 s = kk < 2 ? f.sc.x : f.sc.y;
   const f16x2_t sc = {s, s};
   uint4 o;
   o.x = nv_pair(w, sc, 0);
@@ -565,8 +566,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
                     for (int j = 0; j < FN; ++j)
                       acc[i][j] =
                           __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[kk & 1][j], av[kk & 1][i], acc[i][j], 0, 0, 0);
-                  // ~9 VALU per expanded fragment (scale decode, 4 converts, 4 multiplies)
-                  if (kk + 1 < BK / 16) interleave_mfma_valu<NA * FN, (9 * (NA + FN) + NA * FN - 1) / (NA * FN)>();
+                  // ~8 VALU per expanded fragment (4 converts, 4 multiplies)
+                  if (kk + 1 < BK / 16) interleave_mfma_valu<NA * FN, (8 * (NA + FN) + NA * FN - 1) / (NA * FN)>();
                 }
               }
             }
