@@ -1,0 +1,146 @@
+"""Full-size parity of the step the benchmark times (the MoE layer full
+update: 8192 tokens, d_model 2048, 128 experts, top-8, FFN 768), launched
+exactly as bench.py launches it (moe_layer.forward / backward on full-size
+buffers).  Every stage is checked against the oracle fed with the GPU's own
+stored input of that stage, on what the oracle can afford at this size:
+the whole routing metadata, and for four experts (the first, the largest,
+the last and a seeded one) the first and last row of every 256-row tile plus
+seeded rows; two experts' weight gradients on seeded elements; seeded
+tokens of the two combines.  Integer outputs are compared bit for bit,
+GEMMs within |C - C_ref| <= 1e-3 * sum|a*b| (+ bf16 output rounding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _helpers import assert_bf16_close, assert_gemm_close, gpu, require_gpu, to_gpu, to_np
+from oracle import gemm, moe, nvfp4
+from oracle.layer import quantize_weights
+
+pytestmark = gpu
+
+
+@pytest.fixture(scope="module")
+def step():
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer
+    d = workloads.moe_8k_update()
+    T, k, E, D, F = d["T"], d["k"], d["E"], d["D"], d["F"]
+    dev = torch.device("cuda:0")
+    x, w_gu, w_dn, dy = (to_gpu(d[n], torch.bfloat16) for n in ("x", "w_gu", "w_dn", "dy"))
+    ids, tw = to_gpu(d["topk_ids"], torch.int32), to_gpu(d["topk_w"], torch.float32)
+    wq_gu = moe_layer.quantize_expert_weights(w_gu)
+    wq_dn = moe_layer.quantize_expert_weights(w_dn)
+    buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=True)
+    meta = moe_layer.forward(x, ids, tw, wq_gu, wq_dn, buf)
+    moe_layer.backward(dy, tw, w_gu, w_dn, meta, buf)
+    torch.cuda.synchronize()
+    off = to_np(meta["offsets"]).astype(np.int64)
+    counts = np.diff(off)
+    rng = np.random.default_rng(7)
+    experts = sorted({0, int(counts.argmax()), E - 1, int(rng.integers(1, E - 1))})
+    rows = []
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        for t0 in range(lo, hi, 256):
+            rows += [t0, min(t0 + 255, hi - 1)]
+        rows += rng.integers(lo, hi, 6).tolist()
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    return dict(d=d, meta=meta, buf=buf, wq_gu=wq_gu, wq_dn=wq_dn, off=off, rows=rows, experts=experts, rng=rng)
+
+
+def _rows(t, rows):
+    return to_np(t[torch.from_numpy(rows).to(t.device)])
+
+
+def test_metadata_and_fused_permute_quantize(step):
+    d, meta, buf, rows = step["d"], step["meta"], step["buf"], step["rows"]
+    off, dest, src = moe.permute_metadata(d["topk_ids"], d["E"])
+    np.testing.assert_array_equal(to_np(meta["offsets"]), off)
+    np.testing.assert_array_equal(to_np(meta["dest"]), dest)
+    np.testing.assert_array_equal(to_np(meta["src"]), src)
+    amax = to_np(buf.amax)
+    assert amax[0] == np.abs(d["x"]).max()
+    xr = d["x"][src[rows] // d["k"]]
+    np.testing.assert_array_equal(_rows(buf.x_perm, rows), xr)
+    q, s, g, _ = nvfp4.quantize(xr, amax=[amax[0]])
+    np.testing.assert_array_equal(_rows(buf.a1_q, rows), q)
+    np.testing.assert_array_equal(_rows(buf.a1_s, rows), s)
+    assert to_np(buf.a1_g)[0] == g[0]
+
+
+def test_gate_up_silu_requantize_down_combine(step):
+    d, meta, buf, rows, off = step["d"], step["meta"], step["buf"], step["rows"], step["off"]
+    wq_gu, wq_dn = step["wq_gu"], step["wq_dn"]
+    wg = (to_np(wq_gu["q"]), to_np(wq_gu["s"]), to_np(wq_gu["g"]))
+    wd = (to_np(wq_dn["q"]), to_np(wq_dn["s"]), to_np(wq_dn["g"]))
+    a1 = (to_np(buf.a1_q), to_np(buf.a1_s), to_np(buf.a1_g))
+    y1_ref, ab1 = gemm.grouped_gemm_w4a4(*a1, *wg, off, rows=rows)
+    y1 = _rows(buf.y1, rows)
+    assert_gemm_close(y1, y1_ref, ab1, bf16_out=True, what="gate+up (fused epilogue)")
+    h = _rows(buf.h, rows)
+    assert_bf16_close(h, moe.silu_gate_fwd(y1), what="fused SiLU gate")
+    amax = to_np(buf.amax)
+    assert amax[1] == np.abs(to_np(buf.h)).max()
+    q2, s2, g2, _ = nvfp4.quantize(h, amax=[amax[1]])
+    np.testing.assert_array_equal(_rows(buf.a2_q, rows), q2)
+    np.testing.assert_array_equal(_rows(buf.a2_s, rows), s2)
+    a2 = (to_np(buf.a2_q), to_np(buf.a2_s), to_np(buf.a2_g))
+    y2_ref, ab2 = gemm.grouped_gemm_w4a4(*a2, *wd, off, rows=rows)
+    assert_gemm_close(_rows(buf.y2, rows), y2_ref, ab2, bf16_out=True, what="down")
+    # combine: seeded tokens, from the GPU's own Y2 rows
+    k = d["k"]
+    dest = to_np(meta["dest"])
+    toks = np.sort(step["rng"].choice(d["T"], 32, replace=False))
+    sub = dest.reshape(-1, k)[toks].reshape(-1)
+    y2s = _rows(buf.y2, sub)
+    local = np.arange(sub.size, dtype=np.int64)
+    ref = moe.unpermute(y2s, local, k, d["topk_w"][toks])
+    bound = moe.unpermute_absbound(y2s, local, k, d["topk_w"][toks])
+    assert_bf16_close(_rows(buf.out, toks), ref, scale=bound, what="combine")
+
+
+def test_backward(step):
+    d, meta, buf, rows, off = step["d"], step["meta"], step["buf"], step["rows"], step["off"]
+    k, F = d["k"], d["F"]
+    src = to_np(meta["src"])
+    dy2 = _rows(buf.dy2, rows)
+    assert_bf16_close(dy2, moe.gather_rows(d["dy"], src[rows], k, d["topk_w"]), what="dY2")
+    expert_of = np.searchsorted(off, rows, side="right") - 1
+    dh = _rows(buf.dh, rows)
+    for i, (r, e) in enumerate(zip(rows, expert_of)):
+        ref, ab = gemm.grouped_gemm_bf16("NN", dy2[i:i + 1], d["w_dn"][e:e + 1], [0, 1])
+        assert_gemm_close(dh[i:i + 1], ref, ab, bf16_out=True, what="dH row %d" % r)
+    y1 = _rows(buf.y1, rows)
+    dy1 = _rows(buf.dy1, rows)
+    dy1_ref = moe.silu_gate_bwd(y1, dh)
+    scale = np.abs(dy1_ref) + 1e-3 * np.abs(np.concatenate([dh, dh], axis=1)) * (np.abs(y1) + 1)
+    assert_bf16_close(dy1, dy1_ref, scale=scale, what="dY1")
+    dxp = _rows(buf.dx_perm, rows)
+    for i, (r, e) in enumerate(zip(rows, expert_of)):
+        ref, ab = gemm.grouped_gemm_bf16("NN", dy1[i:i + 1], d["w_gu"][e:e + 1], [0, 1])
+        assert_gemm_close(dxp[i:i + 1], ref, ab, bf16_out=True, what="dX_perm row %d" % r)
+    # weight gradients of two experts, seeded elements, over all their rows
+    rng = step["rng"]
+    for e in (step["experts"][0], step["experts"][-1]):
+        lo, hi = int(off[e]), int(off[e + 1])
+        er = np.arange(lo, hi, dtype=np.int64)
+        dy2_e, h_e = _rows(buf.dy2, er), _rows(buf.h, er)
+        dy1_e, xp_e = _rows(buf.dy1, er), _rows(buf.x_perm, er)
+        for name, a, b, dw in (("dW_dn", dy2_e, h_e, buf.dw_dn), ("dW_gu", dy1_e, xp_e, buf.dw_gu)):
+            ii = rng.integers(0, a.shape[1], 64)
+            jj = rng.integers(0, b.shape[1], 64)
+            ref = np.einsum("ri,ri->i", a[:, ii].astype(np.float64), b[:, jj].astype(np.float64))
+            ab = np.einsum("ri,ri->i", np.abs(a[:, ii]).astype(np.float64), np.abs(b[:, jj]).astype(np.float64))
+            got = to_np(dw[e])[ii, jj]
+            assert_gemm_close(got, ref, ab, what="%s expert %d" % (name, e))
+    # dX combine: seeded tokens, from the GPU's own dX_perm rows
+    dest = to_np(meta["dest"])
+    toks = np.sort(rng.choice(d["T"], 32, replace=False))
+    sub = dest.reshape(-1, k)[toks].reshape(-1)
+    dxs = _rows(buf.dx_perm, sub)
+    local = np.arange(sub.size, dtype=np.int64)
+    ref = moe.unpermute(dxs, local, k, None)
+    bound = moe.unpermute_absbound(dxs, local, k, None)
+    assert_bf16_close(_rows(buf.dx, toks), ref, scale=bound, what="dX")
