@@ -55,6 +55,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int BK = 64;                       // reduction elements per MFMA group / bf16 stage
+#ifndef NVFP4MOE_GEMM_NMAJOR
+#define NVFP4MOE_GEMM_NMAJOR 1
+#endif
+constexpr bool kNMajor = NVFP4MOE_GEMM_NMAJOR;  // tile order within an expert (find_tile)
 constexpr int NV_KS = 256;                   // reduction elements per NVFP4 stage
 constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
@@ -157,10 +161,15 @@ __device__ int count_row_blocks(const int32_t* __restrict__ off, int E, int64_t 
 
 // Map row block `slot` to (expert, first row, end row) by a prefix sum of
 // per-expert block counts.  Runs on one whole wave; false past the last block.
-template <int BM>
-__device__ bool find_row_block(const int32_t* __restrict__ off, int E, int64_t M, int64_t slot, int& e_out,
-                               int64_t& r0, int64_t& r1) {
+// Tile L of the row-grouped layouts: its expert, row range and n-tile.  The
+// tiles of one expert are numbered n-tile-major when NMAJOR (the expert's
+// row blocks that share a weight panel are neighbours, so they run side by
+// side on one XCD), row-block-major otherwise.
+template <int BM, bool NMAJOR>
+__device__ bool find_tile(const int32_t* __restrict__ off, int E, int64_t M, int64_t L, int n_tiles, int& e_out,
+                          int64_t& r0, int64_t& r1, int& n_out) {
   const int lane = threadIdx.x & 63;
+  const int64_t slot = L / n_tiles;  // the expert's tiles span its row blocks x n_tiles
   int64_t running = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
@@ -182,7 +191,18 @@ __device__ bool find_row_block(const int32_t* __restrict__ off, int E, int64_t M
       const int srcl = __ffsll((unsigned long long)mask) - 1;
       e_out = __shfl(e, srcl, 64);
       const int lo_s = __shfl(lo, srcl, 64), hi_s = __shfl(hi, srcl, 64), ex = __shfl(incl - cnt, srcl, 64);
-      r0 = lo_s + (slot - running - ex) * BM;
+      const int cnt_s = __shfl(cnt, srcl, 64);
+      const int64_t rb0 = running + ex;  // the expert's first row block
+      int64_t rb;
+      if (NMAJOR) {
+        const int64_t t = L - rb0 * n_tiles;
+        n_out = (int)(t / cnt_s);
+        rb = t % cnt_s;
+      } else {
+        n_out = (int)(L % n_tiles);
+        rb = slot - rb0;
+      }
+      r0 = lo_s + rb * BM;
       r1 = r0 + BM < hi_s ? r0 + BM : hi_s;
       return true;
     }
@@ -390,7 +410,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
   static_assert(S >= 2 && S <= 8 && NDMA * (S - 2) <= 63, "pipeline depth");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
-  __shared__ int64_t s_tile[4];
+  __shared__ int64_t s_tile[5];  // tile lookup: expert, rows, -, n-tile; [3]: row-block count
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void_t*)smem;  // LDS byte address
@@ -429,13 +449,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       red = hi - lo;
     } else {
       if (wid == 0) {
-        int e = -1;
+        int e = -1, nt = 0;
         int64_t r0 = 0, r1 = 0;
-        const bool ok = find_row_block<BM>(p.offsets, p.E, p.M, L / p.n_tiles, e, r0, r1);
+        const bool ok = find_tile<BM, kNMajor>(p.offsets, p.E, p.M, L, p.n_tiles, e, r0, r1, nt);
         if (lane == 0) {
           s_tile[0] = ok ? e : -1;
           s_tile[1] = r0;
           s_tile[2] = r1;
+          s_tile[4] = nt;
         }
       }
       lds_barrier();
@@ -443,7 +464,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       expert = (int)s_tile[0];
       m0 = s_tile[1];
       m_end = s_tile[2];
-      n0 = (L % p.n_tiles) * BN;
+      n0 = s_tile[4] * BN;
       red = p.K;
     }
 
