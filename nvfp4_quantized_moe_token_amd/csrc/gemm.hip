@@ -127,6 +127,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, ui
 }
 // K-major bf16 tile: chunk c (8 elements) of row r at byte r*128 + 16*(c ^ kswz(r)).
 __device__ __forceinline__ int kswz(int r) { return (r ^ (r >> 3)) & 7; }
+// Swizzle of a K-major tile with ROWB-byte rows (128: kswz; 64: (r / 2) % 4),
+// conflict-free for 16-byte reads of the same chunk in 8 consecutive rows.
+template <int ROWB>
+__device__ __forceinline__ int rswz(int r) {
+  if constexpr (ROWB == 128) return kswz(r);
+  else return (r >> 1) & 3;
+}
 // MN-major bf16 tile: chunk c of reduction row k at byte k*rowbytes + 16*(c ^ mswz(k)).
 // Any 4 consecutive rows k = 4i..4i+3 then put a transposed read's 32- and
 // 64-byte row segments on disjoint banks.
@@ -226,21 +233,23 @@ __device__ __forceinline__ int64_t gate_up_row(int r, int64_t gate_f, int64_t j0
   return ((r >> 5) & 1) * gate_f + j0 + ((r >> 6) << 5) + (r & 31);
 }
 
-// K-major bf16 tile of ROWS rows x 64 k; row r of the tile is row r of the
-// region (or gate_up_row(r) when gate_f > 0), element k0 + k.  `ld` is the
-// row pitch in elements.
-template <int ROWS, int NW>
+// K-major bf16 tile of ROWS rows x ROWB/2 k; row r of the tile is row r of
+// the region (or gate_up_row(r) when gate_f > 0), element k0 + k.  `ld` is
+// the row pitch in elements.
+template <int ROWS, int NW, int ROWB = 128>
 struct KMajorLoader {
-  static_assert(ROWS % (8 * NW) == 0, "K-major tile: rows per wave");
-  static constexpr int N_INSTR = ROWS / (8 * NW);
+  static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;   // rows per 1 KiB load
+  static_assert(ROWS % (RPL * NW) == 0, "K-major tile: rows per wave");
+  static constexpr int N_INSTR = ROWS / (RPL * NW);
   __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
                                               int64_t k0, int64_t K, int64_t gate_f = 0, int64_t j0 = 0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < N_INSTR; ++i) {
       const int idx = wid + NW * i;
-      const int row = idx * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ kswz(row);
+      const int row = idx * RPL + lane / CPR;
+      const int c = (lane % CPR) ^ rswz<ROWB>(row);
       const int64_t k = k0 + c * 8;
       const int64_t grow = gate_f > 0 ? gate_up_row(row, gate_f, j0) : row;
       const uint32_t voff = k < K ? (uint32_t)((grow * ld + k) * 2) : kOOB;
@@ -249,15 +258,15 @@ struct KMajorLoader {
   }
 };
 
-// MN-major bf16 tile of 64 reduction rows x COLS columns; reduction row kr
+// MN-major bf16 tile of KR reduction rows x COLS columns; reduction row kr
 // is region row (row0 + kr), column n0 + n; `ld` is the row pitch.
-template <int COLS, int NW>
+template <int COLS, int NW, int KR = 64>
 struct MNMajorLoader {
   static_assert(COLS == 128 || COLS == 256, "MN-major tile width");
   static constexpr int CPR = COLS / 8;  // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;  // rows per 1 KiB load
-  static_assert((64 / RPI) % NW == 0, "MN-major tile: loads per wave");
-  static constexpr int N_INSTR = 64 / RPI / NW;
+  static_assert((KR / RPI) % NW == 0, "MN-major tile: loads per wave");
+  static constexpr int N_INSTR = KR / RPI / NW;
   __device__ __forceinline__ static void load(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
                                               int64_t row0, int64_t n0, int64_t ncols) {
     const int lane = threadIdx.x & 63;
@@ -275,11 +284,13 @@ struct MNMajorLoader {
 
 // ---- fragment readers (LDS -> MFMA operands) ----
 
-// K-major bf16 fragment: rows base + (lane % 32), k = 16*kk + 8*(lane/32) + 0..7.
+// K-major bf16 fragment (ROWB-byte rows): rows base + (lane % 32),
+// k = 16*kk + 8*(lane/32) + 0..7.
+template <int ROWB>
 __device__ __forceinline__ bf16x8_t frag_kmajor(const uint8_t* tile, int base, int kk, int lane) {
   const int row = base + (lane & 31);
   const int c = kk * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8_t*>(tile + row * 128 + ((c ^ kswz(row)) << 4));
+  return *reinterpret_cast<const bf16x8_t*>(tile + row * ROWB + ((c ^ rswz<ROWB>(row)) << 4));
 }
 
 // MN-major bf16 fragment through two transposed reads: column base +
@@ -370,14 +381,14 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 }
 
 // Wave-wide loads per pipeline step of one operand tile (A side or B side).
-template <int MODE, bool A_SIDE, int ROWS, int NW>
+template <int MODE, bool A_SIDE, int ROWS, int NW, int BKB>
 constexpr int loads_per_wave() {
   if constexpr (is_nv(MODE))
     return KMajorLoader<ROWS, NW>::N_INSTR;
   else if constexpr ((A_SIDE && MODE == TN_BF16) || (!A_SIDE && MODE != NT_BF16))
-    return MNMajorLoader<ROWS, NW>::N_INSTR;
+    return MNMajorLoader<ROWS, NW, BKB>::N_INSTR;
   else
-    return KMajorLoader<ROWS, NW>::N_INSTR;
+    return KMajorLoader<ROWS, NW, BKB * 2>::N_INSTR;
 }
 
 template <int N>
@@ -386,8 +397,10 @@ struct IntConst {
 };
 // ---- the kernel ----
 
-template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
+// Two waves per SIMD (at most 256 VGPRs each): one 8-wave workgroup, or two
+// 4-wave workgroups per CU (then stated, so the compiler keeps to 256).
+template <int MODE, int BM, int BN, int WM, int WN, int S, int BKB, bool OUT32>
+__global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 ? 2 : 1) void gemm_kernel(Params p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");
@@ -396,16 +409,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
   // Reduction elements per pipeline stage: 64 for bf16 (128-byte rows);
   // 256 for NVFP4, so that each row brings a whole 128-byte line of codes
   // and 16 bytes of scales per stage.
-  constexpr int KS = NV ? NV_KS : BK;
-  constexpr int A_BYTES = BM * 128;
-  constexpr int B_BYTES = BN * 128;
+  // bf16 stages hold BKB reduction elements (64: 128-byte K-major rows; 32:
+  // 64-byte rows, for deeper rings in the same LDS).
+  static_assert(!NV || BKB == 64, "NVFP4 stages use 128-byte code rows");
+  constexpr int KS = NV ? NV_KS : BKB;
+  constexpr int A_BYTES = BM * BKB * 2;
+  constexpr int B_BYTES = BN * BKB * 2;
   constexpr int SC_BYTES = NV ? (BM + BN) * 16 : 0;  // A scales then B scales
   constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   static_assert(!NV || (BM + BN) % (64 * NW) == 0, "NVFP4 scales: rows per wave");
   constexpr int SC_INSTR = NV ? (BM + BN) / (64 * NW) : 0;
   // Per-wave loads per step, for the vmcnt waits.
-  constexpr int A_INSTR = loads_per_wave<MODE, true, BM, NW>();
-  constexpr int B_INSTR = loads_per_wave<MODE, false, BN, NW>();
+  constexpr int A_INSTR = loads_per_wave<MODE, true, BM, NW, BKB>();
+  constexpr int B_INSTR = loads_per_wave<MODE, false, BN, NW, BKB>();
   constexpr int NDMA = A_INSTR + B_INSTR + SC_INSTR;
   static_assert(S >= 2 && S <= 8 && NDMA * (S - 2) <= 63, "pipeline depth");
 
@@ -499,14 +515,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
       const uint32_t st = smem_lds + stage * STAGE;
       const int64_t k0 = kt * KS;
       if constexpr (MODE == NT_BF16) {
-        KMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, p.K);
-        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K, k0, p.K);
+        KMajorLoader<BM, NW, BKB * 2>::load(st, wid, ra, p.K, k0, p.K);
+        KMajorLoader<BN, NW, BKB * 2>::load(st + A_BYTES, wid, rb, p.K, k0, p.K);
       } else if constexpr (MODE == NN_BF16) {
-        KMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, p.K);
-        MNMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+        KMajorLoader<BM, NW, BKB * 2>::load(st, wid, ra, p.K, k0, p.K);
+        MNMajorLoader<BN, NW, BKB>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
       } else if constexpr (MODE == TN_BF16) {
-        MNMajorLoader<BM, NW>::load(st, wid, ra, p.K, k0, m0, p.K);
-        MNMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+        MNMajorLoader<BM, NW, BKB>::load(st, wid, ra, p.K, k0, m0, p.K);
+        MNMajorLoader<BN, NW, BKB>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
       } else {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
         // bf16 tile of 64 16-bit units per row.
@@ -599,10 +615,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 #pragma unroll
               for (int i = 0; i < NA; ++i)
                 av[buf][i] = MODE == TN_BF16 ? frag_mnmajor<BM>(st, wm * WTM + i * 32, kk, lane)
-                                             : frag_kmajor(st, wm * WTM + i * 32, kk, lane);
+                                             : frag_kmajor<BKB * 2>(st, wm * WTM + i * 32, kk, lane);
 #pragma unroll
               for (int j = 0; j < FN; ++j)
-                bv[buf][j] = MODE == NT_BF16 ? frag_kmajor(st + A_BYTES, wn * WTN + j * 32, kk, lane)
+                bv[buf][j] = MODE == NT_BF16 ? frag_kmajor<BKB * 2>(st + A_BYTES, wn * WTN + j * 32, kk, lane)
                                              : frag_mnmajor<BN>(st + A_BYTES, wn * WTN + j * 32, kk, lane);
             };
             // LDS reads per sub-step: one per K-major fragment, two per MN-major one.
@@ -610,15 +626,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
             read_frags(0, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-              if (kk + 1 < BK / 16) read_frags(kk + 1, (kk + 1) & 1);
+            for (int kk = 0; kk < BKB / 16; ++kk) {
+              if (kk + 1 < BKB / 16) read_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
               for (int i = 0; i < NA; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                   acc[i][j] =
                       __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[kk & 1][j], av[kk & 1][i], acc[i][j], 0, 0, 0);
-              if (kk + 1 < BK / 16)
+              if (kk + 1 < BKB / 16)
                 interleave_mfma_ds<NA * FN, NRD>();
               else
                 interleave_mfma_ds<NA * FN, 0>();
@@ -780,12 +796,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(Params p) {
 
 // Resident workgroups per CU of one kernel instantiation (cached; the same on
 // every gfx950 device).
-template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
+template <int MODE, int BM, int BN, int WM, int WN, int S, int BKB, bool OUT32>
 int resident_per_cu() {
   static int cached = 0;
   if (cached > 0) return cached;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel<MODE, BM, BN, WM, WN, S, OUT32>, WM * WN * 64,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_kernel<MODE, BM, BN, WM, WN, S, BKB, OUT32>, WM * WN * 64,
                                                    0) !=
           hipSuccess ||
       occ < 1)
@@ -794,7 +810,7 @@ int resident_per_cu() {
   return occ;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int S, bool OUT32>
+template <int MODE, int BM, int BN, int WM, int WN, int S, int BKB, bool OUT32>
 int launch_cfg(const Params& p0, hipStream_t st) {
   Params p = p0;
   p.n_tiles = (int)cdiv(p.N, BN);
@@ -807,43 +823,64 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   }
   if (upper <= 0) return NVFP4MOE_OK;
   if (upper > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
-  int64_t grid = (int64_t)device_cu_count() * resident_per_cu<MODE, BM, BN, WM, WN, S, OUT32>();
+  int64_t grid = (int64_t)device_cu_count() * resident_per_cu<MODE, BM, BN, WM, WN, S, BKB, OUT32>();
   if (grid > upper) grid = upper;
   grid = cdiv(grid, 8) * 8;  // whole XCD rounds
-  gemm_kernel<MODE, BM, BN, WM, WN, S, OUT32><<<(unsigned)grid, WM * WN * 64, 0, st>>>(p);
+  gemm_kernel<MODE, BM, BN, WM, WN, S, BKB, OUT32><<<(unsigned)grid, WM * WN * 64, 0, st>>>(p);
   return launch_status();
 }
 
-// Tile configurations: (BM, BN, waves along M, waves along N, LDS stages).
-// Only the configuration pick_config chooses (kDefaultConfig) is compiled; a
-// build for tuning sweeps may force another with
+// Tile configurations: (BM, BN, waves along M, waves along N, LDS stages,
+// reduction elements per bf16 stage).
+// Only the configuration pick_config chooses for each layout is compiled; a
+// build for tuning sweeps may force one for all layouts with
 // -DNVFP4MOE_GEMM_FORCE_CONFIG=<i>.
 #define NVFP4MOE_GEMM_CONFIGS(X) \
-  X(0, 256, 256, 2, 4, 2)        \
-  X(1, 256, 256, 4, 2, 2)        \
-  X(2, 256, 128, 2, 2, 3)        \
-  X(3, 128, 256, 2, 2, 3)        \
-  X(4, 128, 128, 2, 2, 4)        \
-  X(5, 256, 128, 4, 2, 2)        \
-  X(6, 128, 256, 2, 4, 2)        \
-  X(7, 256, 256, 2, 2, 2)        \
-  X(8, 128, 128, 2, 2, 2)
+  X(0, 256, 256, 2, 4, 2, 64)    \
+  X(1, 256, 256, 4, 2, 2, 64)    \
+  X(2, 256, 128, 2, 2, 3, 64)    \
+  X(3, 128, 256, 2, 2, 3, 64)    \
+  X(4, 128, 128, 2, 2, 4, 64)    \
+  X(5, 256, 128, 4, 2, 2, 64)    \
+  X(6, 128, 256, 2, 4, 2, 64)    \
+  X(7, 256, 256, 2, 2, 2, 64)    \
+  X(8, 128, 128, 2, 2, 2, 64)    \
+  X(9, 256, 256, 4, 2, 4, 32)    \
+  X(10, 256, 128, 4, 1, 3, 32)   \
+  X(11, 128, 256, 2, 2, 3, 32)   \
+  X(12, 256, 256, 4, 2, 3, 32)
 
 // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
-// 256 x 256 tiles on 8 waves (4 x 2) with two LDS stages, for every layout.
-constexpr int kDefaultConfig = 1;
+// 256 x 256 tiles on 8 waves (4 x 2); two 64-k stages for the NT and W4A4
+// GEMMs, four 32-k stages (a longer prefetch in the same LDS) for NN and TN,
+// whose MN-major operands come through transposed LDS reads (NN -9..-12%,
+// TN -2..-4% against two 64-k stages).  Two 4-wave workgroups per CU
+// (config 10), to overlap one's epilogue with the other's loop, was slower.
+constexpr int default_config(int mode) { return mode == NN_BF16 || mode == TN_BF16 ? 9 : 1; }
 #ifdef NVFP4MOE_GEMM_FORCE_CONFIG
 constexpr int kForcedConfig = NVFP4MOE_GEMM_FORCE_CONFIG;
 #else
 constexpr int kForcedConfig = -1;
 #endif
-constexpr int kBuiltConfig = kForcedConfig >= 0 ? kForcedConfig : kDefaultConfig;
+constexpr int built_config(int mode) { return kForcedConfig >= 0 ? kForcedConfig : default_config(mode); }
 
 // Whether a configuration is valid for a layout: LDS within the 160 KiB of
-// a gfx950 CU, whole loads per wave for NVFP4 tiles, and for the SiLU-gate
-// epilogue 256-column tiles whose wave halves are multiples of 64 columns.
-constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s) {
-  return s * (bm + bn) * (is_nv(mode) ? 144 : 128) <= 160 * 1024 &&
+// a gfx950 CU, whole loads per wave, NVFP4 stages of 64-element chunks, and
+// for the SiLU-gate epilogue 256-column tiles whose wave halves are
+// multiples of 64 columns.
+constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s, int bkb) {
+  const int nw = wm * wn;
+  if (is_nv(mode) && bkb != 64) return false;
+  if (!is_nv(mode)) {
+    // whole K-major loads (512 / bkb rows each) and MN-major loads (512 / cols rows each) per wave
+    const bool kmaj_a = mode != TN_BF16, kmaj_b = mode == NT_BF16;
+    if (kmaj_a && bm % ((512 / bkb) * nw) != 0) return false;
+    if (kmaj_b && bn % ((512 / bkb) * nw) != 0) return false;
+    if (!kmaj_a && (bm != 128 && bm != 256 || (bkb / (512 / bm)) % nw != 0)) return false;
+    if (!kmaj_b && (bn != 128 && bn != 256 || (bkb / (512 / bn)) % nw != 0)) return false;
+    if ((bm / wm) % 32 != 0 || (bn / wn) % 32 != 0) return false;
+  }
+  return s * (bm + bn) * (is_nv(mode) ? 144 : bkb * 2) <= 160 * 1024 &&
          (!is_nv(mode) || (bm + bn) % (64 * wm * wn) == 0) &&
          (mode != W4A4_SILU || (bn == 256 && (bn / wn) % 64 == 0));
 }
@@ -851,13 +888,13 @@ constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s) {
 template <int MODE>
 int launch_mode(int cfg, const Params& p, hipStream_t st) {
   switch (cfg) {
-#define NVFP4MOE_CASE(I, BM_, BN_, WM_, WN_, S_)                                               \
+#define NVFP4MOE_CASE(I, BM_, BN_, WM_, WN_, S_, BK_)                                          \
   case I:                                                                                      \
-    if constexpr (kBuiltConfig == I && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_)) {                  \
+    if constexpr (built_config(MODE) == I && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_, BK_)) {       \
       if (p.c_f32) {                                                                           \
-        if constexpr (MODE != W4A4_SILU) return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, true>(p, st); \
+        if constexpr (MODE != W4A4_SILU) return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, BK_, true>(p, st); \
       } else {                                                                                 \
-        return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, false>(p, st);                         \
+        return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, BK_, false>(p, st);                    \
       }                                                                                        \
     }                                                                                          \
     break;
@@ -868,11 +905,10 @@ int launch_mode(int cfg, const Params& p, hipStream_t st) {
   return NVFP4MOE_ESHAPE;
 }
 
-// Tile configuration per layout and shape (one for all, see kDefaultConfig).
+// Tile configuration per layout (see default_config).
 int pick_config(int mode, const Params& p) {
-  (void)mode;
   (void)p;
-  return kBuiltConfig;
+  return built_config(mode);
 }
 
 int launch(int mode, const Params& p, hipStream_t st) {
