@@ -16,7 +16,7 @@ import torch
 import workloads
 from _helpers import assert_bf16_close, assert_gemm_close, gpu, require_gpu, to_gpu, to_np
 from oracle import gemm, moe, nvfp4
-from oracle.layer import quantize_weights
+from oracle.layer import bf16_round
 
 pytestmark = gpu
 
@@ -144,3 +144,76 @@ def test_backward(step):
     ref = moe.unpermute(dxs, local, k, None)
     bound = moe.unpermute_absbound(dxs, local, k, None)
     assert_bf16_close(_rows(buf.dx, toks), ref, scale=bound, what="dX")
+
+
+@pytest.mark.parametrize("cfg", ["moe_4k", "moe_16k_skew"])
+def test_forward_only_workloads(cfg):
+    """The forward-only workloads as bench.py --workload runs them (no bf16
+    X_perm, no stored Y1): routing metadata in full, sampled rows of every
+    stage for the largest expert and three seeded non-empty ones, seeded
+    tokens of the combine."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer
+    d = workloads.CONFIGS[cfg]()
+    T, k, E, D, F = d["T"], d["k"], d["E"], d["D"], d["F"]
+    dev = torch.device("cuda:0")
+    x = to_gpu(d["x"], torch.bfloat16)
+    ids, tw = to_gpu(d["topk_ids"], torch.int32), to_gpu(d["topk_w"], torch.float32)
+    wq_gu = moe_layer.quantize_expert_weights(to_gpu(d["w_gu"], torch.bfloat16))
+    wq_dn = moe_layer.quantize_expert_weights(to_gpu(d["w_dn"], torch.bfloat16))
+    buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=False)
+    meta = moe_layer.forward(x, ids, tw, wq_gu, wq_dn, buf, keep_x_perm=False)
+    torch.cuda.synchronize()
+    off, dest, src = moe.permute_metadata(d["topk_ids"], E)
+    np.testing.assert_array_equal(to_np(meta["offsets"]), off)
+    np.testing.assert_array_equal(to_np(meta["dest"]), dest)
+    counts = np.diff(off)
+    rng = np.random.default_rng(3)
+    nz = np.nonzero(counts)[0]
+    experts = sorted({int(counts.argmax())} | set(rng.choice(nz, 3, replace=False).tolist()))
+    rows = []
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        for t0 in range(lo, hi, 256):
+            rows += [t0, min(t0 + 255, hi - 1)]
+        rows += rng.integers(lo, hi, 6).tolist()
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    amax = to_np(buf.amax)
+    assert amax[0] == np.abs(d["x"]).max()
+    q, s, g, _ = nvfp4.quantize(d["x"][src[rows] // k], amax=[amax[0]])
+    np.testing.assert_array_equal(_rows(buf.a1_q, rows), q)
+    np.testing.assert_array_equal(_rows(buf.a1_s, rows), s)
+    wg = (to_np(wq_gu["q"]), to_np(wq_gu["s"]), to_np(wq_gu["g"]))
+    wd = (to_np(wq_dn["q"]), to_np(wq_dn["s"]), to_np(wq_dn["g"]))
+    a1 = (to_np(buf.a1_q), to_np(buf.a1_s), to_np(buf.a1_g))
+    y1_ref, ab1 = gemm.grouped_gemm_w4a4(*a1, *wg, off, rows=rows)
+    # Y1 is not stored on this path: H is checked against the oracle's SiLU
+    # gate of the oracle's Y1 rounded to bf16, within the GEMM tolerance
+    # carried through the gate.
+    h = _rows(buf.h, rows)
+    y1_bf = bf16_round(y1_ref.astype(np.float32))
+    h_ref = moe.silu_gate_fwd(y1_bf)
+    Fh = h_ref.shape[1]
+    g_ab, u_ab = ab1[:, :Fh], ab1[:, Fh:]
+    gv, uv = y1_bf[:, :Fh].astype(np.float64), y1_bf[:, Fh:].astype(np.float64)
+    # |d silu(g) u| <= (1.1 |u| dg + |silu(g)| du) with dg, du the Y1 errors
+    dg = 1e-3 * g_ab + 2.0 ** -8 * (np.abs(gv) + 1e-3 * g_ab)
+    du = 1e-3 * u_ab + 2.0 ** -8 * (np.abs(uv) + 1e-3 * u_ab)
+    tol = 1.1 * np.abs(uv) * dg + np.abs(moe.silu(gv)) * du + 2.0 ** -8 * np.abs(h_ref) + 1e-30
+    err = np.abs(h.astype(np.float64) - h_ref)
+    assert (err <= tol).all(), "H: %d of %d out of tolerance" % (int((err > tol).sum()), err.size)
+    amax_h = to_np(buf.amax)[1]
+    assert amax_h == np.abs(to_np(buf.h)).max()
+    q2, s2, _, _ = nvfp4.quantize(h, amax=[amax_h])
+    np.testing.assert_array_equal(_rows(buf.a2_q, rows), q2)
+    np.testing.assert_array_equal(_rows(buf.a2_s, rows), s2)
+    a2 = (to_np(buf.a2_q), to_np(buf.a2_s), to_np(buf.a2_g))
+    y2_ref, ab2 = gemm.grouped_gemm_w4a4(*a2, *wd, off, rows=rows)
+    assert_gemm_close(_rows(buf.y2, rows), y2_ref, ab2, bf16_out=True, what="%s down" % cfg)
+    toks = np.sort(rng.choice(T, 32, replace=False))
+    sub = dest.reshape(-1, k)[toks].reshape(-1)
+    y2s = _rows(buf.y2, sub.astype(np.int64))
+    local = np.arange(sub.size, dtype=np.int64)
+    ref = moe.unpermute(y2s, local, k, d["topk_w"][toks])
+    bound = moe.unpermute_absbound(y2s, local, k, d["topk_w"][toks])
+    assert_bf16_close(_rows(buf.out, toks), ref, scale=bound, what="%s combine" % cfg)
