@@ -154,6 +154,39 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
     return seq
 
 
+# With --overlap, the weight-gradient GEMMs run on a second stream, each
+# after the op whose output it reads; nothing in the step reads dW, and the
+# main stream joins the second one at the end of the step.  The step is then
+# faster, but kernels that share the GPU report inflated durations, so the
+# default keeps the step serial for per-kernel rooflines.
+WGRAD_DEPS = {"bf16_tn_down": "gather_dy", "bf16_tn_gate_up": "silu_gate_bwd"}
+
+
+def run_step(torch, seq, wstream, timed):
+    """Enqueue one step; returns [(op, start event, end event)], each pair on
+    the stream the op runs on."""
+    main = torch.cuda.current_stream()
+    done, out, last_w = {}, [], None
+    for name, fn in seq:
+        on_w = wstream is not None and name in WGRAD_DEPS
+        st = wstream if on_w else main
+        with torch.cuda.stream(st):
+            if on_w:
+                st.wait_event(done[WGRAD_DEPS[name]])
+            e0 = torch.cuda.Event(enable_timing=timed)
+            e0.record(st)
+            fn()
+            e1 = torch.cuda.Event(enable_timing=timed)
+            e1.record(st)
+        done[name] = e1
+        if on_w:
+            last_w = e1
+        out.append((name, e0, e1))
+    if last_w is not None:
+        main.wait_event(last_w)
+    return out
+
+
 def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the same workload:
     4096 tokens routed top-8 over 64 experts (512 rows per expert, the
@@ -308,6 +341,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe_8k_update", choices=["moe_8k_update", "moe_4k", "moe_16k_skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="weight-gradient GEMMs on a second stream (per-op times then overlap)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: steps only, then a 1 GiB calibration copy")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
@@ -350,10 +385,10 @@ def main():
     buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=backward)
     meta_box = {}
     seq = step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward)
+    wstream = torch.cuda.Stream() if (args.overlap and backward) else None
     log("warmup", args.warmup)
     for _ in range(args.warmup):
-        for _, fn in seq:
-            fn()
+        run_step(torch, seq, wstream, False)
     torch.cuda.synchronize()
 
     if args.pmc_run:
@@ -371,29 +406,20 @@ def main():
         log("pmc run done")
         return
 
-    # Timed steps; every op is bracketed by HIP events on the launch stream.
-    log("timed steps", args.steps)
+    # Timed steps; every op is bracketed by HIP events on its launch stream.
+    log("timed steps", args.steps, "(weight gradients on a second stream)" if wstream is not None else "")
     marks = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        evs = []
-        for name, fn in seq:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            evs.append((name, e))
-            fn()
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        evs.append(("__end__", e))
-        marks.append(evs)
+        marks.append(run_step(torch, seq, wstream, True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     per_op = {}
     for evs in marks:
-        for (n0, e0), (_, e1) in zip(evs[:-1], evs[1:]):
-            per_op.setdefault(n0, []).append(e0.elapsed_time(e1))
+        for n, e0, e1 in evs:
+            per_op.setdefault(n, []).append(e0.elapsed_time(e1))
     per_op = {n: sum(v) / len(v) for n, v in per_op.items()}
 
     # The plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped
@@ -534,7 +560,8 @@ def main():
         "dtype": "fp16+bf16 mfma, fp32 acc" if backward else "fp16 mfma, fp32 acc",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "d_model": D, "experts": E, "top_k": k, "ffn": F,
-                   "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)"},
+                   "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)",
+                   "wgrad_stream": wstream is not None},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "step_gflop": round(step_flops / 1e9, 1),
         "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),

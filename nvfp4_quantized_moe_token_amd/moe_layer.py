@@ -80,15 +80,39 @@ def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=
     return meta
 
 
-def backward(dy, topk_w, w_gu, w_dn, meta, buf):
+def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None):
     """BF16 backward of ``forward`` (weight gradients in fp32).  Each
     elementwise consumer runs right after its producer, before a weight-
-    gradient GEMM streams its fp32 output through the caches."""
-    ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
+    gradient GEMM streams its fp32 output through the caches.
+
+    With ``wgrad_stream`` (a torch stream) the two weight-gradient GEMMs run
+    there, each after the op whose output it reads, overlapping the rest of
+    the backward; the current stream waits for them before returning, so the
+    caller's next step cannot overwrite their inputs early."""
+    main = torch.cuda.current_stream()
     off = meta["offsets"]
+
+    def wgrad(a, b, out):
+        if wgrad_stream is None:
+            ops.grouped_gemm_bf16(ops.TN, a, b, off, out=out)
+            return
+        ready = torch.cuda.Event()
+        ready.record(main)
+        wgrad_stream.wait_event(ready)
+        with torch.cuda.stream(wgrad_stream):
+            ops.grouped_gemm_bf16(ops.TN, a, b, off, out=out)
+
+    ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
+    if wgrad_stream is not None:
+        wgrad(buf.dy2, buf.h, buf.dw_dn)
     ops.grouped_gemm_bf16(ops.NN, buf.dy2, w_dn, off, out=buf.dh)
     ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
-    ops.grouped_gemm_bf16(ops.TN, buf.dy2, buf.h, off, out=buf.dw_dn)
+    if wgrad_stream is None:
+        wgrad(buf.dy2, buf.h, buf.dw_dn)
     ops.grouped_gemm_bf16(ops.NN, buf.dy1, w_gu, off, out=buf.dx_perm)
     ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
-    ops.grouped_gemm_bf16(ops.TN, buf.dy1, buf.x_perm, off, out=buf.dw_gu)
+    wgrad(buf.dy1, buf.x_perm, buf.dw_gu)
+    if wgrad_stream is not None:
+        done = torch.cuda.Event()
+        done.record(wgrad_stream)
+        main.wait_event(done)

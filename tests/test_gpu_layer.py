@@ -90,6 +90,25 @@ def test_layer_stagewise(T, k, E, D, F):
     assert_bf16_close(to_np(buf.dx), dx_ref, scale=moe.unpermute_absbound(dxp, dest, k, None), what="dX")
 
 
+def test_backward_with_wgrad_stream_matches_serial():
+    # The weight-gradient GEMMs on a second stream give the same bits as the
+    # serial backward (same kernels, only the order of independent launches).
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer
+    d, meta, buf, wq_gu, wq_dn = _run(256, 8, 16, 256, 128)
+    ref = {n: getattr(buf, n).clone() for n in ("dy2", "dh", "dy1", "dx_perm", "dx", "dw_dn", "dw_gu")}
+    for n in ref:
+        getattr(buf, n).fill_(7.0)
+    dy, tw = to_gpu(d["dy"], torch.bfloat16), to_gpu(d["topk_w"], torch.float32)
+    w_gu, w_dn = to_gpu(d["w_gu"], torch.bfloat16), to_gpu(d["w_dn"], torch.bfloat16)
+    moe_layer.backward(dy, tw, w_gu, w_dn, meta, buf, wgrad_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for n, t in ref.items():
+        got = getattr(buf, n)
+        assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                           t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)), n
+
+
 def test_silu_extremes():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
