@@ -400,7 +400,7 @@ struct IntConst {
 // Two waves per SIMD (at most 256 VGPRs each): one 8-wave workgroup, or two
 // 4-wave workgroups per CU (then stated, so the compiler keeps to 256).
 template <int MODE, int BM, int BN, int WM, int WN, int S, int BKB, bool OUT32>
-__global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 ? 2 : 1) void gemm_kernel(Params p) {
+__global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <= 64 * 128 ? 2 : 1) void gemm_kernel(Params p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");

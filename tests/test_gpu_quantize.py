@@ -135,6 +135,35 @@ def test_grouped_expert_weights():
     _assert_same(w.reshape(E * N, K), torch.bfloat16, groups=E)
 
 
+def test_expert_weights_full_size_sampled():
+    # Expert weights at the MoE down-projection shape [128, 2048, 768] (403 MB
+    # of bf16), one global scale per expert, amax computed by the library.
+    # Every expert's first and last rows and a seeded sample of others are
+    # checked against the oracle with that expert's amax.
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    E, N, K = 128, 2048, 768
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    w = (torch.randn(E, N, K, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    w[7] *= 64.0
+    w[70] = 0.0
+    q, s, g, a = ops.nvfp4_quantize(w.view(E * N, K), groups=E)
+    torch.cuda.synchronize()
+    want_amax = w.float().abs().amax(dim=(1, 2))
+    assert torch.equal(a, want_amax)
+    rng = np.random.default_rng(6)
+    q3, s3 = q.view(E, N, K // 2), s.view(E, N, K // 16)
+    for e in range(E):
+        rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 2)]))
+        xe = to_np(w[e, torch.as_tensor(rows, device="cuda")].float())
+        rq, rs, rg, _ = nvfp4.quantize(xe, amax=[np.float32(want_amax[e].item())])
+        idx = torch.as_tensor(rows, device="cuda")
+        np.testing.assert_array_equal(to_np(q3[e, idx]), rq)
+        np.testing.assert_array_equal(to_np(s3[e, idx]), rs)
+        assert to_np(g[e:e + 1]).view(np.uint32)[0] == rg.view(np.uint32)[0], e
+
+
 def test_empty_and_single_block():
     require_gpu()
     _assert_same(np.zeros((0, 64), np.float32), torch.float32)
