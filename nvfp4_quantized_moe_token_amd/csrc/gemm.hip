@@ -446,6 +446,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   const int xcd = blockIdx.x & 7;
   const int64_t t_end = total * (xcd + 1) / 8, t_step = gridDim.x >> 3;
 
+  float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
   for (int64_t L = total * xcd / 8 + (blockIdx.x >> 3); L < t_end; L += t_step) {
     int expert;
     int64_t m0, m_end;  // output rows (row-grouped) or C_e rows (TN)
@@ -691,10 +692,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
                                fmaxf(fabsf(bf16_lo(h23)), fabsf(bf16_hi(h23)))));
           }
       }
-      if (p.amax) {
-        m = wave_max(m);
-        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(m));
-      }
+      silu_amax = fmaxf(silu_amax, m);
       continue;
     }
     // The wave's results leave through a private LDS region (the stage ring
@@ -702,9 +700,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // written in the register layout above and read back by rows, so that
     // every global store instruction writes whole 128-byte lines of
     // consecutive rows (16 bytes per lane) instead of 32 partial lines.
-    // (The W4A4 kernel stores directly: staging costs it register spills.)
     constexpr int REGION = 32 * WTN * 4;  // one 32-row block in fp32
-    if constexpr (MODE != W4A4 && NW * REGION <= S * STAGE && WTN % 32 == 0) {
+    if constexpr (NW * REGION <= S * STAGE && WTN % 32 == 0) {
       lds_barrier();
       uint8_t* reg = smem + wid * REGION;
       const int q = lane & 31, h = lane >> 5;
@@ -790,6 +787,22 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
       }
     }
+    }
+  }
+  // W4A4_SILU: one atomic per workgroup for the amax of H (every wave of the
+  // workgroup leaves the tile loop together).
+  if constexpr (SILU) {
+    if (p.amax) {
+      __shared__ float red[NW];
+      const float m = wave_max(silu_amax);
+      if (lane == 0) red[wid] = m;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float v = red[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) v = fmaxf(v, red[i]);
+        atomicMax(reinterpret_cast<unsigned int*>(p.amax), __float_as_uint(v));
+      }
     }
   }
 }
