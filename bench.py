@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.0   # dense fp4 MFMA
 PEAK_HBM_GBS = 8000.0
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP/byte where the two ceilings meet
 PEAK_CLOCK_GHZ = 2.4        # the clock the published MFMA peaks assume
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_moe_8k_update.txt")
 CALIB_BYTES = 1 << 30       # the plain copy that calibrates the traffic counters
@@ -552,17 +553,28 @@ def main():
 
     def roofline_of_kernel(kname):
         """Roofline of one kernel over its launches in a step: algorithmic
-        work per launch / average launch duration (rocprofv3's avg)."""
+        work per launch / average launch duration (rocprofv3's avg).  The
+        bound is the lower ceiling: HBM when the kernel's algorithmic
+        FLOP/byte is below the ridge point (bf16 MFMA peak / HBM peak), the
+        MFMA otherwise; the other ceiling's fraction is reported beside it."""
         names = [o for o in STEP_OPS if KERNEL_OF_OP.get(o) == kname and o in per_op]
         n = len(names)
         ms = sum(per_op[o] for o in names) / n
         fl = sum(op_work(o, T, k, E, D, F)[0] for o in names) / n
         by = sum(op_work(o, T, k, E, D, F)[1] for o in names) / n
-        ach = fl / (ms * 1e-3) / 1e12
-        return {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(ach, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "avg_launch_ms": round(ms, 4),
-                **clock_fields(names, ach)}
+        tfl = fl / (ms * 1e-3) / 1e12
+        gbs = by / (ms * 1e-3) / 1e9
+        common = {"traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "algorithmic_flops": round(fl),
+                  "flop_per_byte": round(fl / by, 1), "ridge_flop_per_byte": round(RIDGE, 1),
+                  "avg_launch_ms": round(ms, 4)}
+        if fl / by < RIDGE:
+            return {"kernel": kname, "ops": names, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), **common,
+                    "mfma_tflops": round(tfl, 1), "mfma_frac": round(tfl / PEAK_BF16_TFLOPS, 4),
+                    **{"mfma_" + key: v for key, v in clock_fields(names, tfl).items()}}
+        return {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(tfl, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tfl / PEAK_BF16_TFLOPS, 4), **common,
+                "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), **clock_fields(names, tfl)}
 
     # Dominant kernel: the largest share of the step's time.
     per_kernel = {}
