@@ -337,12 +337,92 @@ def kernel_stats_summary(d):
         print("%-72s %6d %11.1f %10.2f %10.2f %10.2f %6.2f" % (n, c, t, a, lo, hi, p))
 
 
+def bench_dense(args):
+    """The dense special case on the Qwen3-4B up-projection shape
+    (X [4096, 2560], W [9728, 2560], one expert with offsets [0, M]): NVFP4
+    quantize of X (amax computed, cache flushed) and of W, the W4A4 GEMM to
+    bf16, and this build's BF16 NT GEMM on the same shape.  One JSON line;
+    `value` is the W4A4 GEMM's TFLOP/s (median of the timed repetitions)."""
+    import numpy as np
+    import torch
+    import workloads
+    from nvfp4_quantized_moe_token_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = workloads.qwen3_4b_up()
+    x = torch.from_numpy(np.ascontiguousarray(d["x"])).to(dev).to(torch.bfloat16)
+    w = torch.from_numpy(np.ascontiguousarray(d["w"])).to(dev).to(torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[0]
+    offs = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps, cold=False):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            if cold:
+                flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    xq = ops.nvfp4_quantize(x)
+    wq = ops.nvfp4_quantize(w)
+    y4 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    yb = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    reps = max(5, args.steps)
+    ms_qx = timed(lambda: ops.nvfp4_quantize(x, amax_out=xq[3], q=xq[0], scales=xq[1], gscale=xq[2]), 7, cold=True)
+    ms_qw = timed(lambda: ops.nvfp4_quantize(w, amax_out=wq[3], q=wq[0], scales=wq[1], gscale=wq[2]), 7, cold=True)
+    wq3 = (wq[0].view(1, N, K // 2), wq[1].view(1, N, K // 16), wq[2])
+    ms_w4 = timed(lambda: ops.grouped_gemm_w4a4(xq[0], xq[1], xq[2], *wq3, offs, out=y4), reps)
+    ms_bf = timed(lambda: ops.grouped_gemm_bf16(ops.NT, x, w.view(1, N, K), offs, out=yb), reps)
+    fl = 2.0 * M * N * K
+    nvb = lambda r, c: r * c // 2 + r * c // 16  # noqa: E731
+
+    def gemm_obj(ms, name, in_bytes):
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 4),
+                "algorithmic_bytes": in_bytes + M * N * 2}
+
+    def quant_obj(ms, rows):
+        # the amax pass reads the tensor once more: 2 + 2 + 0.5625 B per element
+        by = rows * K * 2 * 2 + nvb(rows, K)
+        gbs = by / (ms * 1e-3) / 1e9
+        return {"kernel": "amax + quantize (cold)", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4), "algorithmic_bytes": by}
+
+    w4 = gemm_obj(ms_w4, "grouped_gemm_w4a4 (E=1)", nvb(M, K) + nvb(N, K))
+    bf = gemm_obj(ms_bf, "grouped_gemm_bf16 NT (E=1)", (M + N) * K * 2)
+    res = {
+        "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
+        "value": w4["achieved"], "unit": "TFLOP/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(ms_w4, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 mfma, fp32 acc", "data": "synthetic",
+        "config": {"workload": "qwen3_4b_up", "M": M, "N": N, "K": K, "parallelism": "none (1 GPU)"},
+        "w4a4_gemm": {**w4, "frac_fp4_peak": round(w4["achieved"] / PEAK_FP4_TFLOPS, 4),
+                      "speedup_vs_bf16": round(ms_bf / ms_w4, 3)},
+        "bf16_gemm": bf,
+        "quantize_x": quant_obj(ms_qx, M),
+        "quantize_w": quant_obj(ms_qw, N),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe_8k_update", choices=["moe_8k_update", "moe_4k", "moe_16k_skew"])
+    ap.add_argument("--workload", default="moe_8k_update",
+                    choices=["moe_8k_update", "moe_4k", "moe_16k_skew", "qwen3_4b_up"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap", action="store_true",
                     help="weight-gradient GEMMs on a second stream (per-op times then overlap)")
@@ -362,6 +442,10 @@ def main():
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
               "(sharding is described, not built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "qwen3_4b_up":
+        bench_dense(args)
+        return
 
     import torch
     from nvfp4_quantized_moe_token_amd import moe_layer, ops
