@@ -666,31 +666,59 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       uint16_t* Hp = reinterpret_cast<uint16_t*>(p.h);
       const int64_t F = p.N / 2;
       float m = 0.0f;
+      // Gate, up and H of each 32-row block leave through a private LDS
+      // region of the wave (three 32 x FW bf16 parts, 16-byte chunks
+      // XOR-swizzled by row), read back by rows: every global store then
+      // writes 16 bytes per lane and whole 128-byte lines.
+      constexpr int FW = WTN / 2;                // features per wave
+      constexpr int CH = FW / 8;                 // 16-byte chunks per row and part
+      constexpr int PART = 32 * FW * 2;
+      static_assert(NW * 3 * PART <= S * STAGE && (CH & (CH - 1)) == 0 && 64 % CH == 0, "SiLU staging");
+      lds_barrier();  // the stage ring is free: every wave is past its last step
+      uint8_t* reg = smem + wid * 3 * PART;
+      const int q = lane & 31, hh = lane >> 5;
+      const int64_t f0 = j0 + wn * FW;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (row >= m_end) continue;
+        const int64_t row0 = m0 + wm * WTM + i * 32;
+        const bool valid = row0 + q < m_end;
 #pragma unroll
         for (int jj = 0; jj < FN / 2; ++jj)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int64_t f = j0 + wn * (WTN / 2) + jj * 32 + 8 * g + 4 * (lane >> 5);
             const f32x16_t& ga = acc[i][2 * jj];
             const f32x16_t& ua = acc[i][2 * jj + 1];
             const uint32_t g01 = pack_bf16x2(ga[4 * g] * alpha, ga[4 * g + 1] * alpha);
             const uint32_t g23 = pack_bf16x2(ga[4 * g + 2] * alpha, ga[4 * g + 3] * alpha);
             const uint32_t u01 = pack_bf16x2(ua[4 * g] * alpha, ua[4 * g + 1] * alpha);
             const uint32_t u23 = pack_bf16x2(ua[4 * g + 2] * alpha, ua[4 * g + 3] * alpha);
-            if (C16) {
-              *reinterpret_cast<uint2*>(C16 + row * ldc + f) = make_uint2(g01, g23);
-              *reinterpret_cast<uint2*>(C16 + row * ldc + F + f) = make_uint2(u01, u23);
-            }
             const uint32_t h01 = pack_bf16x2(silu_gate(bf16_lo(g01), bf16_lo(u01)), silu_gate(bf16_hi(g01), bf16_hi(u01)));
             const uint32_t h23 = pack_bf16x2(silu_gate(bf16_lo(g23), bf16_lo(u23)), silu_gate(bf16_hi(g23), bf16_hi(u23)));
-            *reinterpret_cast<uint2*>(Hp + row * F + f) = make_uint2(h01, h23);
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(h01)), fabsf(bf16_hi(h01))),
-                               fmaxf(fabsf(bf16_lo(h23)), fabsf(bf16_hi(h23)))));
+            // features jj*32 + 8g + 4hh .. +3: chunk jj*4 + g, half hh
+            const int off = q * (FW * 2) + (((jj * 4 + g) ^ (q & (CH - 1))) << 4) + 8 * hh;
+            *reinterpret_cast<uint2*>(reg + off) = make_uint2(g01, g23);
+            *reinterpret_cast<uint2*>(reg + PART + off) = make_uint2(u01, u23);
+            *reinterpret_cast<uint2*>(reg + 2 * PART + off) = make_uint2(h01, h23);
+            if (valid)
+              m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(h01)), fabsf(bf16_hi(h01))),
+                                 fmaxf(fabsf(bf16_lo(h23)), fabsf(bf16_hi(h23)))));
           }
+#pragma unroll
+        for (int t = 0; t < 32 * CH / 64; ++t) {
+          const int r = t * (64 / CH) + lane / CH, ch = lane % CH;
+          const int off = r * (FW * 2) + ((ch ^ (r & (CH - 1))) << 4);
+          const int64_t row = row0 + r, f = f0 + ch * 8;
+          const uint4 vg = *reinterpret_cast<const uint4*>(reg + off);
+          const uint4 vu = *reinterpret_cast<const uint4*>(reg + PART + off);
+          const uint4 vh = *reinterpret_cast<const uint4*>(reg + 2 * PART + off);
+          if (row < m_end) {
+            if (C16) {
+              *reinterpret_cast<uint4*>(C16 + row * ldc + f) = vg;
+              *reinterpret_cast<uint4*>(C16 + row * ldc + F + f) = vu;
+            }
+            *reinterpret_cast<uint4*>(Hp + row * F + f) = vh;
+          }
+        }
       }
       silu_amax = fmaxf(silu_amax, m);
       continue;
