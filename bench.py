@@ -68,16 +68,17 @@ def gemm_flops(R, D, F):
     return 2.0 * R * (2 * F) * D, 2.0 * R * D * F
 
 
-def op_work(name, T, k, E, D, F):
+def op_work(name, T, k, E, D, F, backward=True):
     """(flops, algorithmic HBM bytes) of one launch of each op of the step:
     every operand read once and every result written once."""
     R = T * k
     f1, f2 = gemm_flops(R, D, F)
     nv = lambda rows, cols: rows * cols * (0.5 + 1.0 / 16)  # noqa: E731  NVFP4 bytes per element
     table = {
-        # metadata, X read once (its amax pass reads it once more), X_perm
-        # bf16 and its NVFP4 rows written once
-        "permute_quantize_x": (0.0, T * D * 2 + R * D * 2 + nv(R, D) + R * 4 * 3),
+        # metadata, X read once (its amax pass reads it once more), the NVFP4
+        # rows of X_perm written once, and its bf16 copy when the backward
+        # keeps one (the full update)
+        "permute_quantize_x": (0.0, T * D * 2 + nv(R, D) + R * 4 * 3 + (R * D * 2 if backward else 0)),
         "w4a4_gate_up": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
         # with the SiLU gate in the epilogue: Y1 (kept for the backward) and H written
         "w4a4_gate_up_silu": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2 + R * F * 2),
@@ -89,6 +90,7 @@ def op_work(name, T, k, E, D, F):
         "bf16_tn_down": (f2, R * D * 2 + R * F * 2 + E * D * F * 4),
         "silu_gate_bwd": (0.0, R * 2 * F * 2 + R * F * 2 + R * 2 * F * 2),
         "bf16_nn_gate_up": (f1, R * 2 * F * 2 + E * 2 * F * D * 2 + R * D * 2),
+        # dY1 and X_perm read once, fp32 dW written once
         "bf16_tn_gate_up": (f1, R * 2 * F * 2 + R * D * 2 + E * 2 * F * D * 4),
         "unpermute_dx": (0.0, R * D * 2 + T * D * 2),
         "bf16_nt_gate_up_baseline": (f1, R * D * 2 + E * 2 * F * D * 2 + R * 2 * F * 2),
@@ -518,8 +520,12 @@ def main():
     per_op = {n: sum(v) / len(v) for n, v in per_op.items()}
 
     # The plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped
-    # GEMM on the same shape and routing, each timed alone.
+    # GEMM on the same shape and routing, each timed alone; the latter and
+    # the standalone quantize below read the bf16 X_perm, written here once
+    # (the forward-only workloads do not keep it).
     offs = meta_box["m"]["offsets"]
+    ops.moe_permute_nvfp4(inp["ids"], E, inp["x"], x_perm=buf.x_perm, want_x_perm=True, amax_out=buf.amax[0:1],
+                          q=buf.a1_q, scales=buf.a1_s, gscale=buf.a1_g, workspace=buf.ws)
     y1w = torch.empty_like(buf.y1)
     y1b = torch.empty_like(buf.y1)
     side = {
@@ -585,7 +591,7 @@ def main():
     traffic = load_traffic()
     kernels = {}
     for name, ms in list(per_op.items()) + list(per_op_extra.items()):
-        fl, by = op_work(name, T, k, E, D, F)
+        fl, by = op_work(name, T, k, E, D, F, backward)
         ent = {"ms": round(ms, 4)}
         if fl:
             ent["tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
@@ -624,7 +630,7 @@ def main():
 
     def roofline_of(name):
         ms = per_op[name] if name in per_op else per_op_extra[name]
-        fl, by = op_work(name, T, k, E, D, F)
+        fl, by = op_work(name, T, k, E, D, F, backward)
         tr_bytes = traffic_bytes([name])
         if fl:
             ach = fl / (ms * 1e-3) / 1e12
@@ -644,8 +650,8 @@ def main():
         names = [o for o in STEP_OPS if KERNEL_OF_OP.get(o) == kname and o in per_op]
         n = len(names)
         ms = sum(per_op[o] for o in names) / n
-        fl = sum(op_work(o, T, k, E, D, F)[0] for o in names) / n
-        by = sum(op_work(o, T, k, E, D, F)[1] for o in names) / n
+        fl = sum(op_work(o, T, k, E, D, F, backward)[0] for o in names) / n
+        by = sum(op_work(o, T, k, E, D, F, backward)[1] for o in names) / n
         tfl = fl / (ms * 1e-3) / 1e12
         gbs = by / (ms * 1e-3) / 1e9
         common = {"traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "algorithmic_flops": round(fl),

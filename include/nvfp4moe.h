@@ -260,6 +260,29 @@ int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* e
                       int accumulate, void* workspace, size_t ws_bytes, nvfp4moe_stream_t stream);
 
 /*
+ * grouped_gemm_bf16_tn_gather -- the NVFP4MOE_TN weight gradient with B's
+ * rows gathered from the unpermuted tokens, so that the permuted copy of
+ * the activations (contiguous layout, [JA] fourth paragraph) need not be
+ * kept for the BF16 backward ([JA] first paragraph):
+ *   c_e = sum over rows r of expert e of a[r]^T b[b_src[r] / k]
+ * (rows with b_src[r] < 0 contribute nothing).  With b_src = the src array
+ * of moe_permute and b = the [T][N] tokens, this equals NVFP4MOE_TN on the
+ * permuted rows bit for bit.
+ *   a      [M_total][K] bf16 (permuted rows, e.g. the gradient of Y1).
+ *   b      [b_rows][N] bf16 (e.g. the T unpermuted tokens).
+ *   b_src  [M_total] int32, device; k >= 1.  b_src[r] / k must be < b_rows
+ *          (a larger index reads zeros or other rows of b; never outside it).
+ *   c      [E][K][N], F32 or BF16; accumulate as for grouped_gemm_bf16.
+ * K % 32 == 0, N % 32 == 0; 16-byte aligned a, b, c; 4-byte aligned b_src;
+ * M_total*K*2 and b_rows*N*2 < 2^31 (else ESHAPE).  EINVAL for NULL
+ * pointers with work to do, k < 1, negative sizes or a bad dtype.
+ */
+int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,
+                                int64_t b_rows, const int32_t* expert_offsets, int E, int64_t M_total,
+                                int64_t N, int64_t K, void* c, int c_dtype, int accumulate,
+                                nvfp4moe_stream_t stream);
+
+/*
  * silu_gate_fwd -- H[r][f] = silu(Y1[r][f]) * Y1[r][F+f] (gate half first),
  * fp32 math, bf16 out (RNE), and amax_out[0] = max |H| over the stored bf16
  * values, ready for amax reuse by the next quantization ([JA] fourth

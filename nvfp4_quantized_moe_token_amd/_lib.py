@@ -30,6 +30,8 @@ SIGNATURES = {
                                             c_vp, c_vp, c_vp, c_vp]),
     "grouped_gemm_bf16": (c_int, [c_int, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_int,
                                   c_vp, c_size, c_vp]),
+    "grouped_gemm_bf16_tn_gather": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_i64, c_i64, c_i64,
+                                            c_vp, c_int, c_int, c_vp]),
     "silu_gate_fwd": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
     "silu_gate_bwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
 }

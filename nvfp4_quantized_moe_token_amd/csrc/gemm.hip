@@ -84,6 +84,10 @@ struct Params {
   int k_tiles_tn;      // TN: tiles along K (rows of C_e)
   void* h;             // W4A4_SILU: H [M][N/2] bf16 (c = Y1 or NULL)
   float* amax;         // W4A4_SILU: max |H| (cleared before the launch), or NULL
+  const int32_t* bsrc; // TN with gathered B: B row of reduction row r is bsrc[r] / bk (none if < 0)
+  int bk;
+  int bk_shift;        // log2(bk) when bk is a power of two, else -1
+  int64_t b_rows;      // TN with gathered B: rows of B
 };
 
 // ---- small device helpers ----
@@ -122,6 +126,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(
                    __builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+// The same with 4 bytes per lane: lane l's word lands at lds + 4*l (probed).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
                "v"(voff), "s"(r)
                : "memory", "m0");
 }
@@ -280,6 +290,25 @@ struct MNMajorLoader {
       dma16(r, lds + idx * 1024, voff);
     }
   }
+  // The same tile with each reduction row taken from its own row of the
+  // region: load i's two rows (lanes 0..31 and 32..63) are src_rows[i][0..1],
+  // a negative row reading as zeros.
+  __device__ __forceinline__ static void load_rows(uint32_t lds, int wid, __amdgpu_buffer_rsrc_t r, int64_t ld,
+                                                   const int32_t (&src_rows)[N_INSTR][2], int64_t n0,
+                                                   int64_t ncols) {
+    static_assert(RPI == 2, "gathered MN-major rows: two reduction rows per load");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const int kr = idx * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ mswz(kr);
+      const int64_t n = n0 + c * 8;
+      const int32_t row = lane < CPR ? src_rows[i][0] : src_rows[i][1];
+      const uint32_t voff = n < ncols && row >= 0 ? (uint32_t)(((int64_t)row * ld + n) * 2) : kOOB;
+      dma16(r, lds + idx * 1024, voff);
+    }
+  }
 };
 
 // ---- fragment readers (LDS -> MFMA operands) ----
@@ -422,11 +451,17 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   // Per-wave loads per step, for the vmcnt waits.
   constexpr int A_INSTR = loads_per_wave<MODE, true, BM, NW, BKB>();
   constexpr int B_INSTR = loads_per_wave<MODE, false, BN, NW, BKB>();
-  constexpr int NDMA = A_INSTR + B_INSTR + SC_INSTR;
+  // TN: one 4-byte load per step of the gathered-B row indices (out of
+  // range, i.e. nothing, when B is not gathered), so the count is fixed.
+  constexpr int NIDX = MODE == TN_BF16 ? 1 : 0;
+  constexpr int NDMA = A_INSTR + B_INSTR + SC_INSTR + NIDX;
   static_assert(S >= 2 && S <= 8 && NDMA * (S - 2) <= 63, "pipeline depth");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
   __shared__ int64_t s_tile[5];  // tile lookup: expert, rows, -, n-tile; [3]: row-block count
+  // TN with gathered B: per wave and ring slot, the bsrc entries of the
+  // wave's B rows of that step (4 used of each 256-byte landing area).
+  __shared__ __attribute__((aligned(256))) int32_t gidx[MODE == TN_BF16 ? NW * S * 64 : 1];
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void_t*)smem;  // LDS byte address
@@ -501,7 +536,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     } else if constexpr (MODE == NN_BF16) {
       rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)expert * p.K * p.N, p.K * p.N * 2);
     } else if constexpr (MODE == TN_BF16) {
-      rb = make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
+      rb = p.bsrc ? make_rsrc(p.b, p.b_rows * p.N * 2)
+                  : make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
     } else {
       // SiLU-gate tiles gather gate and up rows: the region is the expert.
       const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
@@ -512,6 +548,17 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     const int64_t gate_f = SILU ? p.N / 2 : 0;
     const int64_t j0 = n0 / 2;
 
+    // TN: bsrc entries of this wave's B rows of step s (rows (wid + NW i) * 2
+    // + h, lane 2i + h) into ring slot s % S; out of range when B is not
+    // gathered or past the expert's rows.
+    using BLoad = MNMajorLoader<BN, NW, BKB>;
+    const __amdgpu_buffer_rsrc_t rix = make_rsrc(p.bsrc, p.bsrc ? p.M * 4 : 0);
+    auto index_load = [&](int64_t s) {
+      const int i = lane >> 1, h = lane & 1;
+      const int64_t rr = s * BKB + (wid + NW * i) * 2 + h;
+      const uint32_t voff = lane < 2 * BLoad::N_INSTR && rr < red ? (uint32_t)((lo + rr) * 4) : kOOB;
+      dma4(rix, (uint32_t)(uintptr_t)(const lds_void_t*)gidx + (wid * S + (int)(s % S)) * 256, voff);
+    };
     auto load_step = [&](int64_t kt, int stage) {
       const uint32_t st = smem_lds + stage * STAGE;
       const int64_t k0 = kt * KS;
@@ -523,7 +570,22 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         MNMajorLoader<BN, NW, BKB>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
       } else if constexpr (MODE == TN_BF16) {
         MNMajorLoader<BM, NW, BKB>::load(st, wid, ra, p.K, k0, m0, p.K);
-        MNMajorLoader<BN, NW, BKB>::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+        if (p.bsrc) {
+          const int32_t* ix = gidx + (wid * S + (int)(kt % S)) * 64;
+          int32_t rows[BLoad::N_INSTR][2];
+#pragma unroll
+          for (int i = 0; i < BLoad::N_INSTR; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int32_t v = ix[2 * i + h];
+              const int32_t t = p.bk_shift >= 0 ? v >> p.bk_shift : v / p.bk;
+              rows[i][h] = k0 + (wid + NW * i) * 2 + h < red && v >= 0 ? t : -1;
+            }
+          BLoad::load_rows(st + A_BYTES, wid, rb, p.N, rows, n0, p.N);
+        } else {
+          BLoad::load(st + A_BYTES, wid, rb, p.N, k0, n0, p.N);
+        }
+        index_load(kt + S - 1);
       } else {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
         // bf16 tile of 64 16-bit units per row.
@@ -555,6 +617,12 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // takes part in every barrier.
     int n_active = FM;
     if (MODE != TN_BF16 && m_end - m0 <= wm * WTM) n_active = 0;
+    if (MODE == TN_BF16 && p.bsrc) {
+      // Row indices of the first S - 1 steps (the wave's own LDS area).
+#pragma unroll
+      for (int s = 0; s < S - 1; ++s) index_load(s);
+      wait_vmcnt<0>();
+    }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < nk) load_step(s, s);
@@ -1032,6 +1100,46 @@ extern "C" int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_
   if (F < 0) return NVFP4MOE_EINVAL;
   return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h,
                     amax_out, as_stream(stream));
+}
+
+extern "C" int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,
+                                           int64_t b_rows, const int32_t* expert_offsets, int E, int64_t M_total,
+                                           int64_t N, int64_t K, void* c, int c_dtype, int accumulate,
+                                           nvfp4moe_stream_t stream) {
+  if (E < 1 || M_total < 0 || N < 0 || K < 0 || k < 1 || b_rows < 0) return NVFP4MOE_EINVAL;
+  if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return NVFP4MOE_EINVAL;
+  if (accumulate && c_dtype != NVFP4MOE_F32) return NVFP4MOE_EINVAL;
+  if (!expert_offsets) return NVFP4MOE_EINVAL;
+  const bool has_out = K > 0 && N > 0;
+  if (has_out && (!c || (M_total > 0 && (!a || !b_src || (b_rows > 0 && !b))))) return NVFP4MOE_EINVAL;
+  if (K % 32 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a, 16) || !aligned(b, 16) ||
+      !aligned(c, 16) || !aligned(b_src, 4))
+    return NVFP4MOE_ESHAPE;
+  // Buffer offsets are 32-bit: A and B must each stay below 2 GiB.
+  if (M_total * K * 2 >= (1LL << 31) || b_rows * N * 2 >= (1LL << 31)) return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (!has_out) return NVFP4MOE_OK;
+  Params p = {};
+  p.a = a;
+  p.b = b;
+  p.offsets = expert_offsets;
+  p.c = c;
+  p.M = M_total;
+  p.N = N;
+  p.K = K;
+  p.E = E;
+  p.c_f32 = c_dtype == NVFP4MOE_F32;
+  p.accumulate = accumulate;
+  // b_src is never read when no expert has rows; a NULL B with b_rows = 0
+  // leaves every gathered row out of range (zeros).
+  p.bsrc = b_src;
+  p.bk = k;
+  p.bk_shift = (k & (k - 1)) == 0 ? __builtin_ctz((unsigned)k) : -1;
+  p.b_rows = b_rows;
+  return launch(TN_BF16, p, as_stream(stream));
 }
 
 extern "C" int grouped_gemm_bf16(int layout, const void* a, const void* b, const int32_t* expert_offsets, int E,

@@ -5,8 +5,8 @@ orders the calls and owns the buffers).
 Forward ("miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph:
 contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
   moe_permute_nvfp4 (amax of X once, metadata, gather fused with the NVFP4
-  quantization of the gathered rows; the bf16 rows are kept only for the
-  backward)  ->  grouped_gemm_w4a4_silu_gate (gate+up with the SiLU gate and
+  quantization of the gathered rows; the bf16 permuted rows are kept for the
+  backward's gate+up weight gradient unless it gathers them from X)  ->  grouped_gemm_w4a4_silu_gate (gate+up with the SiLU gate and
   the amax of H in its epilogue; Y1 is stored only for the backward)  ->
   nvfp4_quantize(H, amax_in=amax_H)  ->  grouped_gemm_w4a4 (down)  ->
   moe_unpermute (routing-weighted combine).  When F is not a multiple of 128
@@ -14,7 +14,10 @@ contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
 Backward in BF16 (same page, first paragraph), no amax reduction at all:
   moe_gather(dY, weighted)  ->  NN dgrad of the down projection  ->
   silu_gate_bwd  ->  TN wgrad of the down projection  ->  NN dgrad of gate+up
-  ->  moe_unpermute (unweighted sum back to tokens)  ->  TN wgrad of gate+up.
+  ->  moe_unpermute (unweighted sum back to tokens)  ->  TN wgrad of gate+up,
+  on the kept permuted rows, or with its activation rows gathered from X
+  through the routing's src (grouped_gemm_bf16_tn_gather: no 268 MB copy at
+  8192 tokens, measured ~0.1 ms slower than the copy's TN plus its write).
 """
 
 import torch
@@ -57,10 +60,11 @@ class Buffers:
             self.dw_gu = e(E, 2 * F, D, dt=f32)
 
 
-def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=True):
-    """W4A4 MoE forward; returns the routing metadata dict.  The bf16
-    permuted rows (buf.x_perm) and Y1 (buf.y1) are written only when
-    keep_x_perm (the BF16 backward needs them)."""
+def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_y1=True, keep_x_perm=True, fuse_silu=True):
+    """W4A4 MoE forward; returns the routing metadata dict.  Y1 (buf.y1) is
+    written when keep_y1 and the bf16 permuted rows (buf.x_perm) when
+    keep_x_perm (the BF16 backward needs Y1, and X_perm unless it gathers
+    from X)."""
     E = buf.E
     meta = ops.moe_permute_nvfp4(topk_ids, E, x, x_perm=buf.x_perm if keep_x_perm else None,
                                  want_x_perm=keep_x_perm, amax_out=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
@@ -68,7 +72,7 @@ def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=
     wgu = (wq_gu["q"], wq_gu["s"], wq_gu["g"])
     if fuse_silu and buf.F % 128 == 0:
         ops.grouped_gemm_w4a4_silu_gate(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"],
-                                        y1=buf.y1 if keep_x_perm else None, want_y1=keep_x_perm, h=buf.h,
+                                        y1=buf.y1 if keep_y1 else None, want_y1=keep_y1, h=buf.h,
                                         amax_out=buf.amax[1:2])
     else:
         ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"], out=buf.y1)
@@ -80,10 +84,13 @@ def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_x_perm=True, fuse_silu=
     return meta
 
 
-def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None):
+def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None, x=None):
     """BF16 backward of ``forward`` (weight gradients in fp32).  Each
     elementwise consumer runs right after its producer, before a weight-
-    gradient GEMM streams its fp32 output through the caches.
+    gradient GEMM streams its fp32 output through the caches.  With ``x``
+    (the forward's [T, D] tokens) the gate+up weight gradient gathers its
+    activation rows from x; without it, from buf.x_perm (forward with
+    keep_x_perm=True).
 
     With ``wgrad_stream`` (a torch stream) the two weight-gradient GEMMs run
     there, each after the op whose output it reads, overlapping the rest of
@@ -92,15 +99,21 @@ def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None):
     main = torch.cuda.current_stream()
     off = meta["offsets"]
 
-    def wgrad(a, b, out):
-        if wgrad_stream is None:
+    def tn(a, b, out, gather):
+        if gather:
+            ops.grouped_gemm_bf16_tn_gather(a, b, meta["src"], buf.k, off, out=out)
+        else:
             ops.grouped_gemm_bf16(ops.TN, a, b, off, out=out)
+
+    def wgrad(a, b, out, gather=False):
+        if wgrad_stream is None:
+            tn(a, b, out, gather)
             return
         ready = torch.cuda.Event()
         ready.record(main)
         wgrad_stream.wait_event(ready)
         with torch.cuda.stream(wgrad_stream):
-            ops.grouped_gemm_bf16(ops.TN, a, b, off, out=out)
+            tn(a, b, out, gather)
 
     ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
     if wgrad_stream is not None:
@@ -111,7 +124,10 @@ def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None):
         wgrad(buf.dy2, buf.h, buf.dw_dn)
     ops.grouped_gemm_bf16(ops.NN, buf.dy1, w_gu, off, out=buf.dx_perm)
     ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
-    wgrad(buf.dy1, buf.x_perm, buf.dw_gu)
+    if x is not None:
+        wgrad(buf.dy1, x, buf.dw_gu, gather=True)
+    else:
+        wgrad(buf.dy1, buf.x_perm, buf.dw_gu)
     if wgrad_stream is not None:
         done = torch.cuda.Event()
         done.record(wgrad_stream)

@@ -215,6 +215,21 @@ def grouped_gemm_bf16(layout, a, b, offsets, num_experts=None, out=None, out_dty
     return out
 
 
+def grouped_gemm_bf16_tn_gather(a, b, src, k, offsets, num_experts=None, out=None, out_dtype=torch.float32,
+                                accumulate=False):
+    """TN weight gradient with B rows gathered: C_e = sum_{r in e} a[r]^T b[src[r] // k]."""
+    _dev(a, b, src, offsets, out)
+    M, K = a.shape
+    N = b.shape[1]
+    E = offsets.numel() - 1 if num_experts is None else num_experts
+    out = torch.empty((E, K, N), dtype=out_dtype, device=a.device) if out is None else out
+    rc = _lib.load().grouped_gemm_bf16_tn_gather(_ptr(a), _ptr(b), _ptr(src), int(k), b.shape[0], _ptr(offsets), E,
+                                                 M, N, K, _ptr(out), _DT[out.dtype], int(bool(accumulate)),
+                                                 _stream())
+    _check("grouped_gemm_bf16_tn_gather", rc)
+    return out
+
+
 def silu_gate_fwd(y1, h=None, amax_out=None, want_amax=True):
     """H = silu(G) * U for y1 = [G | U]; returns (h, amax)."""
     _dev(y1, h, amax_out)

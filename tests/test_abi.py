@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
-              "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "silu_gate_fwd",
+              "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16",
+              "grouped_gemm_bf16_tn_gather", "silu_gate_fwd",
               "silu_gate_bwd", "moe_permute_nvfp4",
               "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
         assert n in names
@@ -165,6 +166,25 @@ def test_gemm_silu_gate_validation(lib):
     assert g(*bad) == -2                       # Y1 alignment
     bad = list(args); bad[12] = FAKE + 2
     assert g(*bad) == -2                       # H alignment
+
+
+def test_gemm_tn_gather_validation(lib):
+    g = lib.grouped_gemm_bf16_tn_gather
+    args = [FAKE, FAKE, FAKE, 8, 100, FAKE, 4, 64, 64, 64, FAKE, 0, 0, None]
+    bad = list(args); bad[3] = 0
+    assert g(*bad) == -1                       # k < 1
+    bad = list(args); bad[2] = None
+    assert g(*bad) == -1                       # b_src NULL with rows to reduce
+    bad = list(args); bad[4] = -1
+    assert g(*bad) == -1                       # negative b_rows
+    bad = list(args); bad[11] = 1; bad[12] = 1
+    assert g(*bad) == -1                       # accumulate into bf16
+    bad = list(args); bad[9] = 48
+    assert g(*bad) == -2                       # K % 32
+    bad = list(args); bad[2] = FAKE + 2
+    assert g(*bad) == -2                       # b_src alignment
+    bad = list(args); bad[4] = 1 << 25
+    assert g(*bad) == -2                       # b_rows * N * 2 >= 2^31
 
 
 def test_silu_validation(lib):

@@ -127,7 +127,7 @@ def test_backward(step):
         lo, hi = int(off[e]), int(off[e + 1])
         er = np.arange(lo, hi, dtype=np.int64)
         dy2_e, h_e = _rows(buf.dy2, er), _rows(buf.h, er)
-        dy1_e, xp_e = _rows(buf.dy1, er), _rows(buf.x_perm, er)
+        dy1_e, xp_e = _rows(buf.dy1, er), d["x"][to_np(meta["src"])[er] // d["k"]]
         for name, a, b, dw in (("dW_dn", dy2_e, h_e, buf.dw_dn), ("dW_gu", dy1_e, xp_e, buf.dw_gu)):
             ii = rng.integers(0, a.shape[1], 64)
             jj = rng.integers(0, b.shape[1], 64)
@@ -162,7 +162,7 @@ def test_forward_only_workloads(cfg):
     wq_gu = moe_layer.quantize_expert_weights(to_gpu(d["w_gu"], torch.bfloat16))
     wq_dn = moe_layer.quantize_expert_weights(to_gpu(d["w_dn"], torch.bfloat16))
     buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=False)
-    meta = moe_layer.forward(x, ids, tw, wq_gu, wq_dn, buf, keep_x_perm=False)
+    meta = moe_layer.forward(x, ids, tw, wq_gu, wq_dn, buf, keep_y1=False, keep_x_perm=False)
     torch.cuda.synchronize()
     off, dest, src = moe.permute_metadata(d["topk_ids"], E)
     np.testing.assert_array_equal(to_np(meta["offsets"]), off)

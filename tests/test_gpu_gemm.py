@@ -202,3 +202,51 @@ def test_moe_8k_backward_shapes_sampled():
         lo, hi = off[e], off[e + 1]
         ref, ab = gemm.grouped_gemm_bf16("TN", dy2[lo:hi], h[lo:hi], [0, hi - lo])
         assert_gemm_close(dw_np[e], ref[0], ab[0], what="TN expert %d" % e)
+
+
+@pytest.mark.parametrize("counts,K,N,k", [
+    ([0, 1, 200, 0, 70], 96, 160, 3),   # empty and 1-row experts, ragged tails
+    ([300, 0, 257, 3], 320, 288, 2),
+])
+def test_bf16_tn_gather_small(counts, K, N, k):
+    # The gathered weight gradient against the oracle's TN on the explicitly
+    # gathered rows, and bit for bit against the library's TN on those rows.
+    # A few rows carry b_src = -1 (no source row: zeros).
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(31 + K)
+    E, M = len(counts), sum(counts)
+    T = (M + k - 1) // k + 5
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    src = rng.integers(0, T * k, M).astype(np.int32)
+    src[rng.choice(M, min(M, 4), replace=False)] = -1
+    a = _bf(rng, (M, K))
+    x = _bf(rng, (T, N), 0.05)
+    xg = np.where((src >= 0)[:, None], x[np.maximum(src, 0) // k], 0.0).astype(np.float32)
+    a_g, offs_g = to_gpu(a, torch.bfloat16), to_gpu(offs, torch.int32)
+    c = ops.grouped_gemm_bf16_tn_gather(a_g, to_gpu(x, torch.bfloat16), to_gpu(src, torch.int32), k, offs_g)
+    c_ref = ops.grouped_gemm_bf16(ops.TN, a_g, to_gpu(xg, torch.bfloat16), offs_g)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int32), c_ref.view(torch.int32))
+    ref, ab = gemm.grouped_gemm_bf16("TN", a, xg, offs)
+    assert_gemm_close(to_np(c), ref, ab, what="TN gather")
+
+
+def test_bf16_tn_gather_moe_8k_gate_up():
+    # Full-size weight gradient of the gate+up projection as the backward
+    # runs it: dY1 against the unpermuted tokens gathered through src, bit
+    # for bit equal to the TN GEMM on the permuted copy of the tokens.
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    d = workloads.moe_8k_update()
+    E, k = d["E"], d["k"]
+    x = to_gpu(d["x"], torch.bfloat16)
+    r = ops.moe_permute(to_gpu(d["topk_ids"], torch.int32), E, x=x)
+    R = r["x_perm"].shape[0]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    dy1 = (torch.randn(R, 2 * d["F"], device="cuda", generator=gen) * 1e-3).to(torch.bfloat16)
+    dw = ops.grouped_gemm_bf16_tn_gather(dy1, x, r["src"], k, r["offsets"])
+    dw_ref = ops.grouped_gemm_bf16(ops.TN, dy1, r["x_perm"], r["offsets"])
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dw_ref.view(torch.int32))

@@ -109,6 +109,21 @@ def test_backward_with_wgrad_stream_matches_serial():
                            t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)), n
 
 
+def test_backward_gathered_gate_up_matches_copy():
+    # The gate+up weight gradient gathered from X through src gives the same
+    # bits as the TN GEMM on the kept permuted copy.
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer
+    d, meta, buf, wq_gu, wq_dn = _run(256, 8, 16, 256, 128)
+    ref = buf.dw_gu.clone()
+    buf.dw_gu.fill_(7.0)
+    dy, tw = to_gpu(d["dy"], torch.bfloat16), to_gpu(d["topk_w"], torch.float32)
+    w_gu, w_dn = to_gpu(d["w_gu"], torch.bfloat16), to_gpu(d["w_dn"], torch.bfloat16)
+    moe_layer.backward(dy, tw, w_gu, w_dn, meta, buf, x=to_gpu(d["x"], torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(buf.dw_gu.view(torch.int32), ref.view(torch.int32))
+
+
 def test_silu_extremes():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
