@@ -519,6 +519,31 @@ def main():
             per_op.setdefault(n, []).append(e0.elapsed_time(e1))
     per_op = {n: sum(v) / len(v) for n, v in per_op.items()}
 
+    # The same serial step captured once into a HIP graph and replayed as
+    # many times: the launch gaps between its kernels shrink.  Reported beside
+    # the eager step time, which the per-op events above belong to.
+    graph_ms = None
+    if wstream is None:
+        gstream = torch.cuda.Stream()
+        gstream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gstream):
+            for _, fn in seq:
+                fn()
+        torch.cuda.current_stream().wait_stream(gstream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, fn in seq:
+                fn()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # The plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped
     # GEMM on the same shape and routing, each timed alone; the latter and
     # the standalone quantize below read the bf16 X_perm, written here once
@@ -695,6 +720,9 @@ def main():
                    "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)",
                    "wgrad_stream": wstream is not None},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4), "value": round(step_flops / (graph_ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(T / (graph_ms * 1e-3), 1)},
         "step_gflop": round(step_flops / 1e9, 1),
         "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
