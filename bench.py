@@ -284,11 +284,11 @@ def pmc_summary(fetch_dir, write_dir, clock_dir=None):
              "# `bench.py --pmc-run` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the op's",
              "# kernels) scaled by the counters' reading of a plain %d-byte device copy:" % CALIB_BYTES,
              "# fetch x%.4f, write x%.4f.  Bytes per launch; 'sources' fingerprints the HIP sources (code, comments removed)." % (sf, sw),
-             "# commands: cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
-             "-d $REPO/gpurun_out/pmc_fetch -o run -- python $REPO/bench.py --pmc-run --steps 2 --warmup 1",
-             "#   (the same with WRITE_SIZE into $REPO/gpurun_out/pmc_write and with GRBM_GUI_ACTIVE into",
-             "#   $REPO/gpurun_out/pmc_clock), then python $REPO/bench.py --pmc-summary $REPO/gpurun_out/pmc_fetch",
-             "#   $REPO/gpurun_out/pmc_write $REPO/gpurun_out/pmc_clock",
+             "# commands ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run -- python $REPO/bench.py",
+             "#   --pmc-run --steps 2 --warmup 1 (the same with WRITE_SIZE into $OUT/pmc_write and with",
+             "#   GRBM_GUI_ACTIVE into $OUT/pmc_clock), then python $REPO/bench.py --pmc-summary",
+             "#   $OUT/pmc_fetch $OUT/pmc_write $OUT/pmc_clock",
              "sources %s" % source_digest()]
     for (name, fb, kn), (_, wb, _) in zip(fetch, write):
         lines.append("op %s fetch %.0f write %.0f kernels %s" % (name, fb * sf, wb * sw, ";".join(kn)))
