@@ -35,6 +35,15 @@ inline int dtype_bytes(int dt) {
 // keep every CU busy without a huge tail.
 constexpr int kStreamBlocks = 256 * 8;
 
+// Grid limit of the one-pass streaming kernels (quantize, gather-quantize,
+// combine, SiLU backward): they launch one thread (or one workgroup) per
+// unit of work and keep a grid-stride loop only for inputs beyond this many
+// workgroups of 256 threads (2^28 work-items, below the dispatch's 2^32).
+// On MI355X a grid that covers the tensor once streams 13-15% faster than a
+// grid capped at a few thousand workgroups that loops (measured on a cold
+// 268 MB bf16 quantize: 6.0 against 5.3 TB/s).
+constexpr int64_t kMaxStreamGrid = int64_t(1) << 20;
+
 // -------------------------------------------------------------- device side
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -276,7 +276,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 template <int IN, int OUT, bool WEIGHTED>
 void launch_gather(const void* x, int64_t row_elems, const int32_t* src, const float* w, int k, int64_t R, void* out,
                    float* amax_out, hipStream_t st) {
-  int64_t grid = R < 2048 ? R : 2048;
+  // One workgroup per row; with a fused amax every workgroup ends in one
+  // same-address atomic, which serializes, so that grid stays capped.
+  const int64_t cap = amax_out ? 2048 : kMaxStreamGrid;
+  int64_t grid = R < cap ? R : cap;
   if (grid < 1) grid = 1;
   gather_kernel<IN, OUT, WEIGHTED><<<(unsigned)grid, 256, 0, st>>>(
       reinterpret_cast<const uint8_t*>(x), row_elems, src, w, k, R, reinterpret_cast<uint8_t*>(out), amax_out);
@@ -322,8 +325,7 @@ __global__ __launch_bounds__(NT) void gather_quantize_kernel(const uint4* __rest
                                                              uint4* __restrict__ x_perm, const float* __restrict__ amax,
                                                              uint2* __restrict__ q, uint8_t* __restrict__ scales,
                                                              float* __restrict__ gscale) {
-  const float g = global_scale(amax[0]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = g;
+  if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = global_scale(amax[0]);
   const int64_t nblk = R * bpr;
   for (int64_t b = blockIdx.x * (int64_t)NT + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * NT) {
     const int64_t p = b / bpr, j = b - p * bpr;
@@ -334,6 +336,11 @@ __global__ __launch_bounds__(NT) void gather_quantize_kernel(const uint4* __rest
       w0 = in[0];
       w1 = in[1];
     }
+    // amax is read after the row's loads are issued (the empty asm keeps the
+    // compiler from hoisting it out of the loop), so the three loads (src,
+    // the row, amax) cost two latencies rather than three.
+    asm volatile("" ::: "memory");
+    const float g = global_scale(amax[0]);
     if (x_perm) {
       x_perm[2 * b] = w0;
       x_perm[2 * b + 1] = w1;
@@ -495,7 +502,7 @@ extern "C" int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* des
   if (arch != NVFP4MOE_OK) return arch;
   if (T == 0 || D == 0) return NVFP4MOE_OK;
   hipStream_t st = as_stream(stream);
-  const unsigned grid = (unsigned)(T < 4096 ? T : 4096);
+  const unsigned grid = (unsigned)(T < kMaxStreamGrid ? T : kMaxStreamGrid);
   const uint8_t* y = reinterpret_cast<const uint8_t*>(y_perm);
   uint8_t* o = reinterpret_cast<uint8_t*>(out);
   if (y_dtype == NVFP4MOE_BF16 && out_dtype == NVFP4MOE_BF16)
@@ -545,7 +552,7 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
   // Launched even without rows: it also writes the global scale.
   const int64_t bpr = D / 16, nblk = R * bpr;
   int64_t grid = cdiv(nblk > 0 ? nblk : 1, 256);
-  if (grid > 256 * 16) grid = 256 * 16;
+  if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
   gather_quantize_kernel<256><<<(unsigned)grid, 256, 0, st>>>(
       reinterpret_cast<const uint4*>(x), bpr, src, k, R, reinterpret_cast<uint4*>(x_perm), amax,
       reinterpret_cast<uint2*>(q), scales, gscale);

@@ -62,6 +62,8 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const uint16_t* __restric
   }
 }
 
+// The forward folds max|H| into one atomic per workgroup, so its grid is
+// capped (same-address atomics serialize).
 inline unsigned grid_for(int64_t work) {
   const int64_t g = cdiv(work, 256);
   return (unsigned)(g < 1 ? 1 : g > 256 * 8 ? 256 * 8 : g);
@@ -95,7 +97,9 @@ extern "C" int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t 
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   if (R * F == 0) return NVFP4MOE_OK;
-  silu_bwd_kernel<<<grid_for(R * F / 8), 256, 0, as_stream(stream)>>>(
+  int64_t grid = cdiv(R * F / 8, 256);
+  if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
+  silu_bwd_kernel<<<(unsigned)grid, 256, 0, as_stream(stream)>>>(
       reinterpret_cast<const uint16_t*>(y1), reinterpret_cast<const uint16_t*>(dh), R, F,
       reinterpret_cast<uint16_t*>(dy1));
   return launch_status();
