@@ -957,7 +957,8 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   X(9, 256, 256, 4, 2, 4, 32)    \
   X(10, 256, 128, 4, 1, 3, 32)   \
   X(11, 128, 256, 2, 2, 3, 32)   \
-  X(12, 256, 256, 4, 2, 3, 32)
+  X(12, 256, 256, 4, 2, 3, 32)   \
+  X(13, 256, 256, 2, 2, 4, 32)
 
 // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
 // 256 x 256 tiles on 8 waves (4 x 2); two 64-k stages for the NT and W4A4

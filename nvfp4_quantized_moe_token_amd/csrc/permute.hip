@@ -9,7 +9,8 @@
 //   1. count_kernel  -- per chunk of kChunk assignments, a histogram over
 //                       experts (LDS atomics; counts are order-free).
 //   2. scan_kernel   -- one workgroup: per-expert totals -> offsets, and
-//                       the first row of every (chunk, expert) pair.
+//                       the first row of every (chunk, expert) pair; src
+//                       entries past the valid assignments become -1.
 //   3. rank_kernel   -- per chunk, four waves walk their 256 assignments in
 //                       64-lane steps; equal ids inside a step are matched
 //                       with ballots over the id bits, so the rank of an
@@ -43,14 +44,20 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 }
 
 // counts[c][e] (in) -> first permuted row of (chunk c, expert e) (out);
-// offsets[e] = exclusive prefix of the per-expert totals.  1024 threads are
-// split into `slices` threads per expert, each owning a contiguous range of
-// chunks, so every sequential walk is at most ceil(nchunks / slices) long.
+// offsets[e] = exclusive prefix of the per-expert totals; src[p] = -1 for
+// the rows p in [offsets[E], R) that no valid assignment fills.  1024
+// threads are split into `slices` threads per expert, each owning a
+// contiguous range of chunks, so every sequential walk is at most
+// ceil(nchunks / slices) long; the walks read kScanBatch counts at a time so
+// that their loads are in flight together.
+constexpr int kScanBatch = 8;
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int64_t nchunks, int E,
-                                                    int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ offsets, int64_t R,
+                                                    int32_t* __restrict__ src) {
   __shared__ int32_t ssum[kMaxExperts];   // per (expert, slice) partial sums
   __shared__ int32_t ebase[kMaxExperts];  // per expert first row
   __shared__ int32_t wsum[16];
+  __shared__ int32_t s_valid;
   const int slices = E >= 1024 ? 1 : 1024 / E;
   const int64_t cps = (nchunks + slices - 1) / slices;
   // Phase 1: slice sums.
@@ -59,7 +66,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
     if (e < E) {
       int32_t sum = 0;
       const int64_t c1 = (sl + 1) * cps < nchunks ? (sl + 1) * cps : nchunks;
-      for (int64_t c = sl * cps; c < c1; ++c) sum += counts[c * E + e];
+      for (int64_t c = sl * cps; c < c1; c += kScanBatch) {
+        int32_t v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? counts[(c + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) sum += v[u];
+      }
       ssum[e * slices + sl] = sum;
     }
   }
@@ -92,8 +105,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
       for (int sl = 0; sl < slices; ++sl) run += ssum[e * slices + sl];
     }
   }
-  if (threadIdx.x == 1023) offsets[E] = run;
+  if (threadIdx.x == 1023) {
+    offsets[E] = run;
+    s_valid = run;
+  }
   __syncthreads();
+  // Rows past the valid assignments (ids outside [0, E) were skipped).
+  for (int64_t p = s_valid + (int64_t)threadIdx.x; p < R; p += 1024) src[p] = -1;
   // Phase 3: every slice walks its chunk range from its own start row.
   for (int e0 = 0; e0 < E; e0 += 1024 / slices) {
     const int e = e0 + (int)threadIdx.x / slices, sl = (int)threadIdx.x % slices;
@@ -101,10 +119,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
       int32_t r = ebase[e];
       for (int q = 0; q < sl; ++q) r += ssum[e * slices + q];
       const int64_t c1 = (sl + 1) * cps < nchunks ? (sl + 1) * cps : nchunks;
-      for (int64_t c = sl * cps; c < c1; ++c) {
-        const int32_t v = counts[c * E + e];
-        counts[c * E + e] = r;
-        r += v;
+      for (int64_t c = sl * cps; c < c1; c += kScanBatch) {
+        int32_t v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? counts[(c + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+          if (c + u < c1) counts[(c + u) * E + e] = r;
+          r += v[u];
+        }
       }
     }
   }
@@ -173,13 +196,6 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
     if (valid && (match >> lane) == 1ull) cur[e] += __popcll(match);
     __builtin_amdgcn_wave_barrier();
   }
-}
-
-// src entries past offsets[E] (skipped assignments) are -1.
-__global__ void src_tail_kernel(const int32_t* __restrict__ offsets, int E, int64_t R, int32_t* __restrict__ src) {
-  const int64_t valid = offsets[E];
-  for (int64_t p = valid + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < R; p += (int64_t)gridDim.x * blockDim.x)
-    src[p] = -1;
 }
 
 // Row gather (optionally weighted and dtype-converting) with fused amax.
@@ -417,17 +433,26 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
 }  // namespace nvfp4moe
 
 namespace nvfp4moe {
-// Routing metadata for R assignments: histograms, scan, stable ranks, src
-// tail.  amax_cleared (nullable) is zeroed on the way.
+// Routing metadata for R assignments: histograms, scan (with the src tail),
+// stable ranks.  amax_cleared (nullable) is zeroed by the first kernel;
+// `between` enqueues work that runs after it and before the scan.
+template <class Between>
 static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* amax_cleared, void* workspace,
-                           int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st) {
+                           int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st,
+                           Between between) {
   const int64_t chunks = cdiv(R, kChunk);
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
   count_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, amax_cleared);
-  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets);
+  const int rc = between();
+  if (rc != NVFP4MOE_OK) return rc;
+  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets, R, src);
   rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
-  src_tail_kernel<<<(unsigned)(cdiv(R, 256) < 1024 ? cdiv(R, 256) : 1024), 256, 0, st>>>(offsets, E, R, src);
   return launch_status();
+}
+static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* amax_cleared, void* workspace,
+                           int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st) {
+  return launch_metadata(topk_ids, R, E, amax_cleared, workspace, offsets, dest, src, status, st,
+                         [] { return (int)NVFP4MOE_OK; });
 }
 }  // namespace nvfp4moe
 
@@ -536,17 +561,22 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   hipStream_t st = as_stream(stream);
-  const float* amax = amax_in;
-  if (!amax_in) {
-    // The activation amax is taken once, over the T unpermuted rows.
-    const int rc = launch_amax(x, NVFP4MOE_BF16, T * D * 2 / 16, 1, amax_out, st);
-    if (rc != NVFP4MOE_OK) return rc;
-    amax = amax_out;
-  }
+  const float* amax = amax_in ? amax_in : amax_out;
   if (R == 0) {
+    if (!amax_in) {
+      const int rc = launch_amax(x, NVFP4MOE_BF16, T * D * 2 / 16, 1, amax_out, st);
+      if (rc != NVFP4MOE_OK) return rc;
+    }
     fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
   } else {
-    const int rc = launch_metadata(topk_ids, R, E, nullptr, workspace, offsets, dest, src, status, st);
+    // The activation amax is taken once, over the T unpermuted rows, right
+    // after the histogram kernel has cleared amax_out.
+    const int rc = launch_metadata(topk_ids, R, E, amax_in ? nullptr : amax_out, workspace, offsets, dest, src,
+                                   status, st, [&] {
+                                     return amax_in ? (int)NVFP4MOE_OK
+                                                    : launch_amax_uncleared(x, NVFP4MOE_BF16, T * D * 2 / 16, 1,
+                                                                            amax_out, st);
+                                   });
     if (rc != NVFP4MOE_OK) return rc;
   }
   // Launched even without rows: it also writes the global scale.

@@ -97,8 +97,14 @@ __global__ __launch_bounds__(NT) void quantize_kernel(const uint4* __restrict__ 
 // Enqueue max |x| of each of `groups` equal consecutive parts of n16 16-byte
 // words (bf16 or fp32) into amax_out[groups] (cleared first).
 int launch_amax(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out, hipStream_t st) {
-  constexpr int NT = 256;
   fill_u32_kernel<<<(unsigned)cdiv(groups, 256), 256, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, groups);
+  return launch_amax_uncleared(x, x_dtype, n16_per_group, groups, amax_out, st);
+}
+
+// The same into an amax_out that an earlier launch on the stream cleared.
+int launch_amax_uncleared(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out,
+                          hipStream_t st) {
+  constexpr int NT = 256;
   if (n16_per_group > 0) {
     // At most ~512 workgroups in all: every workgroup ends in one atomic on
     // its group's amax, and same-address atomics serialize (2048 of them
