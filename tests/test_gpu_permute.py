@@ -237,6 +237,40 @@ def test_permute_nvfp4_equals_unfused_path():
     assert (to_np(b["q"])[R_valid:] == 0).all() and (to_np(b["scales"])[R_valid:] == 0).all()
 
 
+def test_permute_nvfp4_computed_amax_clears_stale_buffer_and_marks_tail():
+    """Fused call with the amax computed: a stale amax_out (larger than any
+    |x|) is cleared before the reduction, and with invalid ids the src rows
+    past offsets[E] are -1 (written by the scan) on two calls in a row."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(21)
+    T, k, E, D = 515, 8, 12, 128
+    x = workloads._bf16(rng.standard_normal((T, D)).astype(np.float32))
+    x_g = to_gpu(x, torch.bfloat16)
+    amax_out = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+    for bad in (3, 11):
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+        bad_at = rng.choice(T * k, bad, replace=False)
+        ids.reshape(-1)[bad_at] = np.where(np.arange(bad) % 2 == 0, E, -3)
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        r = ops.moe_permute_nvfp4(to_gpu(ids, torch.int32), E, x_g, amax_out=amax_out, status=st)
+        torch.cuda.synchronize()
+        assert to_np(amax_out)[0] == np.float32(np.abs(x).max())
+        off = to_np(r["offsets"])
+        assert off[-1] == T * k - bad
+        src = to_np(r["src"])
+        assert (src[T * k - bad:] == -1).all() and (src[:T * k - bad] >= 0).all()
+        dest = to_np(r["dest"])
+        assert (dest[bad_at] == -1).all()
+        assert to_np(st)[0] == 1
+        keep = np.ones(T * k, bool)
+        keep[bad_at] = False
+        flat = ids.reshape(-1)
+        o2, _, s2 = moe.permute_metadata(np.where(keep, flat, 0)[keep].reshape(1, -1), E)
+        np.testing.assert_array_equal(off, o2)
+        np.testing.assert_array_equal(np.nonzero(keep)[0][s2], src[:T * k - bad])
+
+
 def test_permute_nvfp4_zero_tokens():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
