@@ -339,6 +339,27 @@ def kernel_stats_summary(d):
         print("%-72s %6d %11.1f %10.2f %10.2f %10.2f %6.2f" % (n, c, t, a, lo, hi, p))
 
 
+def dispatch_summary(d, name):
+    """Per-launch durations of the kernels whose name contains `name` in a
+    `rocprofv3 --kernel-trace --output-format csv` run, grouped by grid size
+    (one group per tensor size): count, median, min and max in microseconds."""
+    import csv
+    paths = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not paths:
+        sys.exit("no *kernel_trace.csv under %s" % d)
+    groups = {}
+    with open(paths[-1]) as f:
+        for r in csv.DictReader(f):
+            if name not in r["Kernel_Name"]:
+                continue
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+            groups.setdefault(key, []).append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+    print("%-40s %14s %6s %10s %10s %10s" % ("kernel", "work-items", "calls", "median_us", "min_us", "max_us"))
+    for (kn, grid), ts in sorted(groups.items(), key=lambda kv: kv[0][1]):
+        ts.sort()
+        print("%-40s %14d %6d %10.2f %10.2f %10.2f" % (kn[:40], grid, len(ts), ts[len(ts) // 2], ts[0], ts[-1]))
+
+
 def bench_dense(args):
     """The dense special case on the Qwen3-4B up-projection shape
     (X [4096, 2560], W [9728, 2560], one expert with offsets [0, M]): NVFP4
@@ -433,7 +454,12 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE run directories, optionally a GRBM_GUI_ACTIVE one")
     ap.add_argument("--kernel-stats-summary", metavar="DIR")
+    ap.add_argument("--dispatch-summary", nargs=2, metavar=("DIR", "KERNEL"),
+                    help="per-launch durations of one kernel in a kernel-trace run, by grid size")
     args = ap.parse_args()
+    if args.dispatch_summary:
+        dispatch_summary(*args.dispatch_summary)
+        return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
