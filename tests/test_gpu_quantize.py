@@ -135,6 +135,23 @@ def test_grouped_expert_weights():
     _assert_same(w.reshape(E * N, K), torch.bfloat16, groups=E)
 
 
+def test_many_groups_and_group_grid_limits():
+    """Amax reduction at its grid limits: more groups than the reduction's
+    workgroup budget (one workgroup per group), a group smaller than one
+    workgroup's first loads, and fp32 input with a per-group outlier."""
+    require_gpu()
+    rng = np.random.default_rng(12)
+    G, N, K = 300, 2, 32                  # 300 groups of 2 rows
+    w = (rng.standard_normal((G * N, K)) * 0.5).astype(np.float32)
+    w[rng.integers(0, G * N, 40), rng.integers(0, K, 40)] *= 300.0
+    _assert_same(w, torch.bfloat16, groups=G)
+    _assert_same(w, torch.float32, groups=G)
+    _assert_same(w[:3], torch.bfloat16, groups=1)   # 3 rows: 12 words, far below one pass
+    big = rng.standard_normal((4096 + 3, 48)).astype(np.float32)
+    big[4098, 17] = -7000.0                          # the amax sits in the last, ragged pass
+    _assert_same(big, torch.bfloat16, groups=1)
+
+
 def test_expert_weights_full_size_sampled():
     # Expert weights at the MoE down-projection shape [128, 2048, 768] (403 MB
     # of bf16), one global scale per expert, amax computed by the library.
