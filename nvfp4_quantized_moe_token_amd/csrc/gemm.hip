@@ -98,6 +98,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Wait until at most min(n, MAX) vector memory operations are outstanding
+// (n wave-uniform).
+template <int MAX>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  if constexpr (MAX <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAX)
+      wait_vmcnt<MAX>();
+    else
+      wait_vmcnt_upto<MAX - 1>(n);
+  }
+}
+constexpr int kMaxEpilogueStores = 32;
+
 // Wait until at most `ahead` steps of NDMA loads each are outstanding
 // (ahead in [0, MAX], wave-uniform).
 template <int MAX, int NDMA>
@@ -148,8 +170,11 @@ __device__ __forceinline__ int rswz(int r) {
 // Any 4 consecutive rows k = 4i..4i+3 then put a transposed read's 32- and
 // 64-byte row segments on disjoint banks.
 __device__ __forceinline__ int mswz(int k) { return (0xCA60 >> ((k & 3) * 4)) & 15; }  // {0, 6, 10, 12}
-// Clamped [lo, hi) row range of expert e.
-__device__ __forceinline__ void expert_range(const int32_t* __restrict__ off, int e, int64_t M, int& lo, int& hi) {
+// Clamped [lo, hi) row range of expert e.  `off` is the global offsets array
+// or its copy in LDS.
+typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
+template <class OffPtr>
+__device__ __forceinline__ void expert_range(OffPtr off, int e, int64_t M, int& lo, int& hi) {
   lo = off[e];
   hi = off[e + 1];
   lo = lo < 0 ? 0 : lo > M ? (int)M : lo;
@@ -182,8 +207,8 @@ __device__ int count_row_blocks(const int32_t* __restrict__ off, int E, int64_t 
 // tiles of one expert are numbered n-tile-major when NMAJOR (the expert's
 // row blocks that share a weight panel are neighbours, so they run side by
 // side on one XCD), row-block-major otherwise.
-template <int BM, bool NMAJOR>
-__device__ bool find_tile(const int32_t* __restrict__ off, int E, int64_t M, int64_t L, int n_tiles, int& e_out,
+template <int BM, bool NMAJOR, class OffPtr>
+__device__ bool find_tile(OffPtr off, int E, int64_t M, int64_t L, int n_tiles, int& e_out,
                           int64_t& r0, int64_t& r1, int& n_out) {
   const int lane = threadIdx.x & 63;
   const int64_t slot = L / n_tiles;  // the expert's tiles span its row blocks x n_tiles
@@ -424,6 +449,23 @@ template <int N>
 struct IntConst {
   static constexpr int value = N;
 };
+// NVFP4 operand regions of a row-grouped tile: A rows [m0, m_end) (codes and
+// scales); B the n-tile's rows of the expert (SiLU-gate tiles gather gate
+// and up rows: the region is the whole expert).
+__device__ __forceinline__ void nv_a_regions(const Params& p, int64_t m0, int64_t m_end, __amdgpu_buffer_rsrc_t& ra,
+                                             __amdgpu_buffer_rsrc_t& rsa) {
+  ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * (p.K / 2), (m_end - m0) * (p.K / 2));
+  rsa = make_rsrc(p.as + m0 * (p.K / 16), (m_end - m0) * (p.K / 16));
+}
+template <int BN, bool SILU>
+__device__ __forceinline__ void nv_b_regions(const Params& p, int expert, int64_t n0, __amdgpu_buffer_rsrc_t& rb,
+                                             __amdgpu_buffer_rsrc_t& rsb) {
+  const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
+  const int64_t brow = (int64_t)expert * p.N + (SILU ? 0 : n0);
+  rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
+  rsb = make_rsrc(p.bs + brow * (p.K / 16), nv * (p.K / 16));
+}
+
 // ---- the kernel ----
 
 // Two waves per SIMD (at most 256 VGPRs each): one 8-wave workgroup, or two
@@ -482,6 +524,30 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   const int64_t t_end = total * (xcd + 1) / 8, t_step = gridDim.x >> 3;
 
   float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
+
+  // Plain W4A4 with bf16 output (PF): the next tile's first stage is loaded
+  // during the current tile's last step, into the ring slot that step does
+  // not read, and the epilogue stages its results through the other slot.
+  // The next tile then starts on data already in flight, and its first wait
+  // lets the previous epilogue's stores stay outstanding (they were issued
+  // after those loads, and a wave's memory counter retires in order).  Each
+  // wave finds the next tile itself from a copy of the offsets in LDS, so
+  // no vector load (whose wait would also wait for the stores) runs in
+  // between.
+  constexpr bool PF = MODE == W4A4 && !OUT32 && S == 2;
+  constexpr int kOffLds = 1025;  // experts whose offsets fit the LDS copy
+  __shared__ int32_t s_off[PF ? kOffLds : 1];
+  const bool pf_on = PF && p.E < kOffLds;
+  if (pf_on) {
+    for (int i = threadIdx.x; i <= p.E; i += NW * 64) s_off[i] = p.offsets[i];
+    __syncthreads();
+  }
+  lds_i32_t* off_lds = (lds_i32_t*)s_off;
+  int slot0 = 0;            // ring slot of this tile's stage 0
+  bool pre = false;         // this tile's stage 0 is in flight (loaded during the previous tile)
+  int nst = 0;              // global stores this wave issued after that prefetch
+  int nx_e = -1, nx_nt = 0; // the next tile, found during the last step
+  int64_t nx_r0 = 0, nx_r1 = 0;
   for (int64_t L = total * xcd / 8 + (blockIdx.x >> 3); L < t_end; L += t_step) {
     int expert;
     int64_t m0, m_end;  // output rows (row-grouped) or C_e rows (TN)
@@ -499,6 +565,13 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       int hi;
       expert_range(p.offsets, expert, p.M, lo, hi);
       red = hi - lo;
+    } else if (PF && pre) {
+      // Found (and its first stage loaded) during the previous tile.
+      expert = nx_e;
+      m0 = nx_r0;
+      m_end = nx_r1;
+      n0 = (int64_t)nx_nt * BN;
+      red = p.K;
     } else {
       if (wid == 0) {
         int e = -1, nt = 0;
@@ -527,8 +600,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     } else if constexpr (MODE == TN_BF16) {
       ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + (int64_t)lo * p.K, red * p.K * 2);
     } else {
-      ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * (p.K / 2), (m_end - m0) * (p.K / 2));
-      rsa = make_rsrc(p.as + m0 * (p.K / 16), (m_end - m0) * (p.K / 16));
+      nv_a_regions(p, m0, m_end, ra, rsa);
     }
     if constexpr (MODE == NT_BF16) {
       const int64_t nv = p.N - n0 < BN ? p.N - n0 : BN;
@@ -539,11 +611,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       rb = p.bsrc ? make_rsrc(p.b, p.b_rows * p.N * 2)
                   : make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
     } else {
-      // SiLU-gate tiles gather gate and up rows: the region is the expert.
-      const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
-      const int64_t brow = (int64_t)expert * p.N + (SILU ? 0 : n0);
-      rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
-      rsb = make_rsrc(p.bs + brow * (p.K / 16), nv * (p.K / 16));
+      nv_b_regions<BN, SILU>(p, expert, n0, rb, rsb);
     }
     const int64_t gate_f = SILU ? p.N / 2 : 0;
     const int64_t j0 = n0 / 2;
@@ -558,6 +626,24 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       const int64_t rr = s * BKB + (wid + NW * i) * 2 + h;
       const uint32_t voff = lane < 2 * BLoad::N_INSTR && rr < red ? (uint32_t)((lo + rr) * 4) : kOOB;
       dma4(rix, (uint32_t)(uintptr_t)(const lds_void_t*)gidx + (wid * S + (int)(s % S)) * 256, voff);
+    };
+    // One NVFP4 stage (codes and scales of A and B) of a tile with the given
+    // regions into the LDS stage at byte address st.
+    auto nv_load = [&](__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, __amdgpu_buffer_rsrc_t rsa_,
+                       __amdgpu_buffer_rsrc_t rsb_, int64_t j0_, int64_t k0, uint32_t st) {
+      // Codes: 128 bytes (256 elements) per row, laid out like a K-major
+      // bf16 tile of 64 16-bit units per row.
+      KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 4, k0 / 4, p.K / 4);
+      KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
+      // Scales: 16 bytes per row, 64 rows per load, A rows first.
+#pragma unroll
+      for (int i = 0; i < SC_INSTR; ++i) {
+        const int idx = wid + NW * i;
+        const bool is_a = idx * 64 < BM;
+        const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+        const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
+        dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
+      }
     };
     auto load_step = [&](int64_t kt, int stage) {
       const uint32_t st = smem_lds + stage * STAGE;
@@ -587,19 +673,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
         index_load(kt + S - 1);
       } else {
-        // Codes: 128 bytes (256 elements) per row, laid out like a K-major
-        // bf16 tile of 64 16-bit units per row.
-        KMajorLoader<BM, NW>::load(st, wid, ra, p.K / 4, k0 / 4, p.K / 4);
-        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb, p.K / 4, k0 / 4, p.K / 4, gate_f, j0);
-        // Scales: 16 bytes per row, 64 rows per load, A rows first.
-#pragma unroll
-        for (int i = 0; i < SC_INSTR; ++i) {
-          const int idx = wid + NW * i;
-          const bool is_a = idx * 64 < BM;
-          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0) : row;
-          dma16(is_a ? rsa : rsb, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
-        }
+        nv_load(ra, rb, rsa, rsb, j0, k0, st);
       }
     };
 
@@ -623,20 +697,57 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       for (int s = 0; s < S - 1; ++s) index_load(s);
       wait_vmcnt<0>();
     }
+    // PF: the global scales are read with scalar loads (constant address
+    // space), so that no vector-memory wait -- which would also wait for the
+    // previous epilogue's stores or the prefetched stage -- comes from them.
+    float alpha_t = 1.0f;
+    if constexpr (PF) {
+      typedef __attribute__((address_space(4))) const float const_f32_t;
+      const_f32_t* ag = (const_f32_t*)p.ag;
+      const_f32_t* bg = (const_f32_t*)p.bg;
+      alpha_t = ag[0] * bg[__builtin_amdgcn_readfirstlane(expert)];
+    }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (s < nk) load_step(s, s);
+      if (s < nk && !(PF && pre && s == 0)) load_step(s, (slot0 + s) % S);
+    bool pre_next = false;
 
     for (int64_t kt = 0; kt < nk; ++kt) {
       // This wave's loads for step kt are done once at most `ahead` later
       // steps' loads are outstanding; the barrier then makes every wave's
-      // loads visible and frees the stage read in the previous step.
+      // loads visible and frees the stage read in the previous step.  A
+      // prefetched first stage is followed only by the previous epilogue's
+      // nst stores, which may stay outstanding.
       const int64_t ahead = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
-      wait_steps_ahead<S - 2, NDMA>((int)ahead);
+      if (PF && pre && kt == 0)
+        wait_vmcnt_upto<kMaxEpilogueStores>(nst);
+      else
+        wait_steps_ahead<S - 2, NDMA>((int)ahead);
       lds_barrier();
-      if (kt + S - 1 < nk) load_step(kt + S - 1, (int)((kt + S - 1) % S));
+      if (kt + S - 1 < nk) load_step(kt + S - 1, (int)((slot0 + kt + S - 1) % S));
+      if constexpr (PF) {
+        // Last step: find the next tile (every wave, from the LDS offsets)
+        // and load its first stage into the slot this step does not read.
+        if (pf_on && kt == nk - 1 && L + t_step < t_end) {
+          int e = -1, nt = 0;
+          int64_t r0 = 0, r1 = 0;
+          const bool ok = find_tile<BM, kNMajor>(off_lds, p.E, p.M, L + t_step, p.n_tiles, e, r0, r1, nt);
+          // The lookup is wave-uniform; say so, so that the regions stay scalar.
+          if (__builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0) {
+            nx_e = __builtin_amdgcn_readfirstlane(e);
+            nx_nt = __builtin_amdgcn_readfirstlane(nt);
+            nx_r0 = uniform64(r0);
+            nx_r1 = uniform64(r1);
+            __amdgpu_buffer_rsrc_t na, nb, nsa, nsb;
+            nv_a_regions(p, nx_r0, nx_r1, na, nsa);
+            nv_b_regions<BN, SILU>(p, nx_e, (int64_t)nx_nt * BN, nb, nsb);
+            nv_load(na, nb, nsa, nsb, (int64_t)nx_nt * BN / 2, 0, smem_lds + (uint32_t)((slot0 + nk) % S) * STAGE);
+            pre_next = true;
+          }
+        }
+      }
 
-      const uint8_t* st = smem + (int)(kt % S) * STAGE;
+      const uint8_t* st = smem + (int)((slot0 + kt) % S) * STAGE;
       // One step of MFMAs over the first NA fragment rows of this wave.
       auto compute = [&](auto na_tag) {
         constexpr int NA = decltype(na_tag)::value;
@@ -721,7 +832,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // four consecutive output columns 8*g + 4*(l/32) + 0..3 in registers
     // 4g..4g+3 -- one 8-byte (bf16) or 16-byte (fp32) store each.
     float alpha = 1.0f;
-    if (NV) alpha = p.ag[0] * p.bg[expert];
+    if (PF) alpha = alpha_t;
+    else if (NV) alpha = p.ag[0] * p.bg[expert];
     const int64_t ldc = p.N;
     float* C32 = reinterpret_cast<float*>(p.c);
     uint16_t* C16 = reinterpret_cast<uint16_t*>(p.c);
@@ -797,9 +909,14 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // every global store instruction writes whole 128-byte lines of
     // consecutive rows (16 bytes per lane) instead of 32 partial lines.
     constexpr int REGION = 32 * WTN * 4;  // one 32-row block in fp32
+    // PF: bf16 blocks, in the ring slot of the tile's last stage (the other
+    // slot holds the next tile's first stage).
+    constexpr int REGION_PF = 32 * WTN * 2;
+    static_assert(!PF || NW * REGION_PF <= STAGE, "PF epilogue staging");
     if constexpr (NW * REGION <= S * STAGE && WTN % 32 == 0) {
       lds_barrier();
-      uint8_t* reg = smem + wid * REGION;
+      uint8_t* reg = PF ? smem + (int)((slot0 + nk - 1) % S) * STAGE + wid * REGION_PF : smem + wid * REGION;
+      if constexpr (PF) nst = 0;
       const int q = lane & 31, h = lane >> 5;
       const int64_t col0 = n0 + wn * WTN;
 #pragma unroll
@@ -850,6 +967,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
             const int r = t * (64 / CH) + lane / CH, ch = lane % CH;
             const uint4 v = *reinterpret_cast<const uint4*>(reg + r * (WTN * 2) + ((ch ^ (r & (CH - 1))) << 4));
             const int64_t row = row0 + r, col = col0 + ch * 8;
+            if constexpr (PF) nst += __ballot(row < m_end && col < p.N) != 0 ? 1 : 0;
             if (row < m_end && col < p.N) *reinterpret_cast<uint4*>(C16 + cbase + row * ldc + col) = v;
           }
         }
@@ -883,6 +1001,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
       }
     }
+    }
+    if constexpr (PF) {
+      slot0 = (int)((slot0 + nk) % S);
+      pre = pre_next;
     }
   }
   // W4A4_SILU: one atomic per workgroup for the amax of H (every wave of the
