@@ -525,7 +525,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
 
   float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
 
-  // Plain W4A4 with bf16 output (PF): the next tile's first stage is loaded
+  // NVFP4 layouts with bf16 output (PF): the next tile's first stage is loaded
   // during the current tile's last step, into the ring slot that step does
   // not read, and the epilogue stages its results through the other slot.
   // The next tile then starts on data already in flight, and its first wait
@@ -846,22 +846,25 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       uint16_t* Hp = reinterpret_cast<uint16_t*>(p.h);
       const int64_t F = p.N / 2;
       float m = 0.0f;
-      // Gate, up and H of each 32-row block leave through a private LDS
-      // region of the wave (three 32 x FW bf16 parts, 16-byte chunks
-      // XOR-swizzled by row), read back by rows: every global store then
-      // writes 16 bytes per lane and whole 128-byte lines.
+      // Gate and up of each 32-row block leave through a private LDS region
+      // of the wave (two 32 x FW bf16 parts, 16-byte chunks XOR-swizzled by
+      // row) and are read back by rows; H is computed from the read-back
+      // rows (the same bf16 gate and up values), so every global store
+      // writes 16 bytes per lane and whole 128-byte lines.  PF: the region
+      // lies in the ring slot of the tile's last stage.
       constexpr int FW = WTN / 2;                // features per wave
       constexpr int CH = FW / 8;                 // 16-byte chunks per row and part
       constexpr int PART = 32 * FW * 2;
-      static_assert(NW * 3 * PART <= S * STAGE && (CH & (CH - 1)) == 0 && 64 % CH == 0, "SiLU staging");
+      static_assert(NW * 2 * PART <= (PF ? STAGE : S * STAGE) && (CH & (CH - 1)) == 0 && 64 % CH == 0,
+                    "SiLU staging");
       lds_barrier();  // the stage ring is free: every wave is past its last step
-      uint8_t* reg = smem + wid * 3 * PART;
+      uint8_t* reg = (PF ? smem + (int)((slot0 + nk - 1) % S) * STAGE : smem) + wid * 2 * PART;
+      if constexpr (PF) nst = 0;
       const int q = lane & 31, hh = lane >> 5;
       const int64_t f0 = j0 + wn * FW;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int64_t row0 = m0 + wm * WTM + i * 32;
-        const bool valid = row0 + q < m_end;
 #pragma unroll
         for (int jj = 0; jj < FN / 2; ++jj)
 #pragma unroll
@@ -872,16 +875,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
             const uint32_t g23 = pack_bf16x2(ga[4 * g + 2] * alpha, ga[4 * g + 3] * alpha);
             const uint32_t u01 = pack_bf16x2(ua[4 * g] * alpha, ua[4 * g + 1] * alpha);
             const uint32_t u23 = pack_bf16x2(ua[4 * g + 2] * alpha, ua[4 * g + 3] * alpha);
-            const uint32_t h01 = pack_bf16x2(silu_gate(bf16_lo(g01), bf16_lo(u01)), silu_gate(bf16_hi(g01), bf16_hi(u01)));
-            const uint32_t h23 = pack_bf16x2(silu_gate(bf16_lo(g23), bf16_lo(u23)), silu_gate(bf16_hi(g23), bf16_hi(u23)));
             // features jj*32 + 8g + 4hh .. +3: chunk jj*4 + g, half hh
             const int off = q * (FW * 2) + (((jj * 4 + g) ^ (q & (CH - 1))) << 4) + 8 * hh;
             *reinterpret_cast<uint2*>(reg + off) = make_uint2(g01, g23);
             *reinterpret_cast<uint2*>(reg + PART + off) = make_uint2(u01, u23);
-            *reinterpret_cast<uint2*>(reg + 2 * PART + off) = make_uint2(h01, h23);
-            if (valid)
-              m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(h01)), fabsf(bf16_hi(h01))),
-                                 fmaxf(fabsf(bf16_lo(h23)), fabsf(bf16_hi(h23)))));
           }
 #pragma unroll
         for (int t = 0; t < 32 * CH / 64; ++t) {
@@ -890,17 +887,29 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
           const int64_t row = row0 + r, f = f0 + ch * 8;
           const uint4 vg = *reinterpret_cast<const uint4*>(reg + off);
           const uint4 vu = *reinterpret_cast<const uint4*>(reg + PART + off);
-          const uint4 vh = *reinterpret_cast<const uint4*>(reg + 2 * PART + off);
-          if (row < m_end) {
+          const uint32_t gw[4] = {vg.x, vg.y, vg.z, vg.w}, uw[4] = {vu.x, vu.y, vu.z, vu.w};
+          uint32_t hw[4];
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            hw[w] = pack_bf16x2(silu_gate(bf16_lo(gw[w]), bf16_lo(uw[w])), silu_gate(bf16_hi(gw[w]), bf16_hi(uw[w])));
+          const bool valid = row < m_end;
+          if constexpr (PF) nst += __ballot(valid) != 0 ? (C16 ? 3 : 1) : 0;
+          if (valid) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(hw[w])), fabsf(bf16_hi(hw[w]))));
             if (C16) {
               *reinterpret_cast<uint4*>(C16 + row * ldc + f) = vg;
               *reinterpret_cast<uint4*>(C16 + row * ldc + F + f) = vu;
             }
-            *reinterpret_cast<uint4*>(Hp + row * F + f) = vh;
+            *reinterpret_cast<uint4*>(Hp + row * F + f) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
           }
         }
       }
       silu_amax = fmaxf(silu_amax, m);
+      if constexpr (PF) {
+        slot0 = (int)((slot0 + nk) % S);
+        pre = pre_next;
+      }
       continue;
     }
     // The wave's results leave through a private LDS region (the stage ring
