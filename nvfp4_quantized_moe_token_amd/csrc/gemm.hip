@@ -535,10 +535,13 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   // no vector load (whose wait would also wait for the stores) runs in
   // between.
   constexpr bool PF = MODE == W4A4 && !OUT32 && S == 2;
-  constexpr int kOffLds = 1025;  // experts whose offsets fit the LDS copy
-  __shared__ int32_t s_off[PF ? kOffLds : 1];
-  const bool pf_on = PF && p.E < kOffLds;
-  if (pf_on) {
+  // Every layout keeps a copy of the expert offsets in LDS (up to 1024
+  // experts), so the per-tile lookups read LDS rather than global memory.
+  constexpr int kOffLds = 1025;
+  __shared__ int32_t s_off[kOffLds];
+  const bool off_in_lds = p.E < kOffLds;
+  const bool pf_on = PF && off_in_lds;
+  if (off_in_lds) {
     for (int i = threadIdx.x; i <= p.E; i += NW * 64) s_off[i] = p.offsets[i];
     __syncthreads();
   }
@@ -563,7 +566,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       m_end = p.K;
       n0 = (int64_t)(rem % p.n_tiles) * BN;
       int hi;
-      expert_range(p.offsets, expert, p.M, lo, hi);
+      if (off_in_lds)
+        expert_range(off_lds, expert, p.M, lo, hi);
+      else
+        expert_range(p.offsets, expert, p.M, lo, hi);
       red = hi - lo;
     } else if (PF && pre) {
       // Found (and its first stage loaded) during the previous tile.
@@ -576,7 +582,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       if (wid == 0) {
         int e = -1, nt = 0;
         int64_t r0 = 0, r1 = 0;
-        const bool ok = find_tile<BM, kNMajor>(p.offsets, p.E, p.M, L, p.n_tiles, e, r0, r1, nt);
+        const bool ok = off_in_lds ? find_tile<BM, kNMajor>(off_lds, p.E, p.M, L, p.n_tiles, e, r0, r1, nt)
+                                   : find_tile<BM, kNMajor>(p.offsets, p.E, p.M, L, p.n_tiles, e, r0, r1, nt);
         if (lane == 0) {
           s_tile[0] = ok ? e : -1;
           s_tile[1] = r0;
