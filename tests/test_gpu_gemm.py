@@ -49,6 +49,27 @@ def test_w4a4_small(M, N, K, counts, out_dtype):
     assert_gemm_close(c, ref, ab, bf16_out=out_dtype == torch.bfloat16)
 
 
+@pytest.mark.parametrize("E,rows_per,N,K", [
+    (300, 60, 512, 128),     # 600 tiles (several per workgroup), one step each: next-tile prefetch
+    (160, 150, 512, 640),    # three steps per tile (the last one partial), ~480 tiles
+    (1100, 16, 96, 64),      # more experts than the LDS offsets copy holds: global lookups, no prefetch
+])
+def test_w4a4_many_tiles_full(E, rows_per, N, K):
+    """Every output element of launches where each workgroup runs several
+    tiles in a row (the bf16-output path loads the next tile's first stage
+    during the current tile's last step), with ragged expert sizes."""
+    require_gpu()
+    rng = np.random.default_rng(E + K)
+    counts = rng.integers(0, 2 * rows_per, E)
+    counts[rng.random(E) < 0.1] = 0
+    M = int(counts.sum())
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a, b = _nv_operands(rng, M, N, K, E)
+    c = _gpu_w4a4(a, b, offs, torch.bfloat16)
+    ref, ab = gemm.grouped_gemm_w4a4(a[0], a[1], a[2], b[0], b[1], b[2], offs)
+    assert_gemm_close(c, ref, ab, bf16_out=True)
+
+
 def test_w4a4_rows_past_offsets_untouched():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
@@ -153,6 +174,27 @@ def test_bf16_small(layout, out_dtype, counts, K, N):
     if layout == "TN":
         for e in np.flatnonzero(np.asarray(counts) == 0):
             assert (to_np(c)[e] == 0).all(), "empty expert %d" % e
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_bf16_more_experts_than_lds_offsets(layout):
+    """1100 experts (past the 1024 whose offsets the GEMMs copy to LDS): the
+    per-tile lookups read the offsets from global memory."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(23)
+    E, K, N = 1100, 64, 96
+    counts = rng.integers(0, 12, E)
+    M = int(counts.sum())
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = _bf(rng, (M, K))
+    b = _bf(rng, (E, N, K) if layout == "NT" else (E, K, N) if layout == "NN" else (M, N), 0.05)
+    lay = {"NT": ops.NT, "NN": ops.NN, "TN": ops.TN}[layout]
+    c = ops.grouped_gemm_bf16(lay, to_gpu(a, torch.bfloat16), to_gpu(b, torch.bfloat16),
+                              to_gpu(offs, torch.int32), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, ab = gemm.grouped_gemm_bf16(layout, a, b, offs)
+    assert_gemm_close(to_np(c), ref, ab, what=layout)
 
 
 def test_bf16_tn_accumulate():
