@@ -40,7 +40,10 @@
 // consecutive tiles -- the n-tiles of one row block, the row blocks of one
 // expert -- share that XCD's L2.  Row-grouped layouts (NT, NN, W4A4) order
 // tiles by (expert row block, n-tile); TN tiles are (expert, k-tile, n-tile)
-// and reduce over the expert's rows.
+// and reduce over the expert's rows.  The expert offsets are copied to LDS
+// at kernel start (up to 1024 experts) for the per-tile lookups.  The plain
+// W4A4 GEMM with bf16 output also loads the next tile's first stage during
+// the current tile's last step (see the kernel).
 #include "common.hpp"
 
 namespace nvfp4moe {
