@@ -528,7 +528,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
 
   float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
 
-  // NVFP4 layouts with bf16 output (PF): the next tile's first stage is loaded
+  // Plain W4A4 with bf16 output (PF): the next tile's first stage is loaded
   // during the current tile's last step, into the ring slot that step does
   // not read, and the epilogue stages its results through the other slot.
   // The next tile then starts on data already in flight, and its first wait
@@ -536,7 +536,9 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   // after those loads, and a wave's memory counter retires in order).  Each
   // wave finds the next tile itself from a copy of the offsets in LDS, so
   // no vector load (whose wait would also wait for the stores) runs in
-  // between.
+  // between.  With the SiLU-gate epilogue and in the NN layout the same
+  // scheme raised register spills and measured slower, so they keep the
+  // plain loop.
   constexpr bool PF = MODE == W4A4 && !OUT32 && S == 2;
   // Every layout keeps a copy of the expert offsets in LDS (up to 1024
   // experts), so the per-tile lookups read LDS rather than global memory.
