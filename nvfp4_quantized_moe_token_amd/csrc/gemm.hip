@@ -862,16 +862,13 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       // of the wave (two 32 x FW bf16 parts, 16-byte chunks XOR-swizzled by
       // row) and are read back by rows; H is computed from the read-back
       // rows (the same bf16 gate and up values), so every global store
-      // writes 16 bytes per lane and whole 128-byte lines.  PF: the region
-      // lies in the ring slot of the tile's last stage.
+      // writes 16 bytes per lane and whole 128-byte lines.
       constexpr int FW = WTN / 2;                // features per wave
       constexpr int CH = FW / 8;                 // 16-byte chunks per row and part
       constexpr int PART = 32 * FW * 2;
-      static_assert(NW * 2 * PART <= (PF ? STAGE : S * STAGE) && (CH & (CH - 1)) == 0 && 64 % CH == 0,
-                    "SiLU staging");
+      static_assert(!PF && NW * 2 * PART <= S * STAGE && (CH & (CH - 1)) == 0 && 64 % CH == 0, "SiLU staging");
       lds_barrier();  // the stage ring is free: every wave is past its last step
-      uint8_t* reg = (PF ? smem + (int)((slot0 + nk - 1) % S) * STAGE : smem) + wid * 2 * PART;
-      if constexpr (PF) nst = 0;
+      uint8_t* reg = smem + wid * 2 * PART;
       const int q = lane & 31, hh = lane >> 5;
       const int64_t f0 = j0 + wn * FW;
 #pragma unroll
@@ -905,7 +902,6 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
           for (int w = 0; w < 4; ++w)
             hw[w] = pack_bf16x2(silu_gate(bf16_lo(gw[w]), bf16_lo(uw[w])), silu_gate(bf16_hi(gw[w]), bf16_hi(uw[w])));
           const bool valid = row < m_end;
-          if constexpr (PF) nst += __ballot(valid) != 0 ? (C16 ? 3 : 1) : 0;
           if (valid) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(hw[w])), fabsf(bf16_hi(hw[w]))));
@@ -918,10 +914,6 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
       }
       silu_amax = fmaxf(silu_amax, m);
-      if constexpr (PF) {
-        slot0 = (int)((slot0 + nk) % S);
-        pre = pre_next;
-      }
       continue;
     }
     // The wave's results leave through a private LDS region (the stage ring
