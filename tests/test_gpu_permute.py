@@ -172,6 +172,32 @@ def test_unpermute(weighted):
     assert_bf16_close(to_np(out), ref, scale=scale, what="unpermute bf16")
     err = np.abs(to_np(out32) - ref)
     assert (err <= 2.0 ** -21 * scale + 1e-30).all()
+    # The bf16 output is the fp32 output (same fma order) rounded once.
+    assert torch.equal(out, out32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("weighted", [True, False])
+def test_unpermute_skipped_assignments(weighted):
+    """Assignments with dest = -1 (skipped by the permutation) add nothing:
+    the reference is the oracle's sum with those weights set to zero."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(31)
+    T, k, D, R = 300, 8, 256, 2400
+    dest = rng.permutation(R).astype(np.int32)
+    skip = rng.random(R) < 0.05
+    dest_g = dest.copy()
+    dest_g[skip] = -1
+    y = workloads._bf16(rng.standard_normal((R, D)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32) if weighted else None
+    out = ops.moe_unpermute(to_gpu(y, torch.bfloat16), to_gpu(dest_g, torch.int32), T, k,
+                            topk_w=None if w is None else to_gpu(w, torch.float32), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    w_eff = (np.ones((T, k), np.float32) if w is None else w).reshape(-1).copy()
+    w_eff[skip] = 0.0
+    ref = moe.unpermute(y, dest, k, w_eff.reshape(T, k))
+    scale = moe.unpermute_absbound(y, dest, k, w_eff.reshape(T, k))
+    assert (np.abs(to_np(out) - ref) <= 2.0 ** -21 * scale + 1e-30).all()
 
 
 @pytest.mark.parametrize("cfg", ["moe_4k", "moe_16k_skew", "moe_8k_update"])
