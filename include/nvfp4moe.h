@@ -134,7 +134,9 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t 
  *             offsets[E] are -1).
  *   amax_out  fp32 [1] or NULL: max |x| over the gathered rows (F32/BF16
  *             payloads only; 0 for an empty gather).
- *   workspace device scratch of moe_permute_workspace_size(T, k, E) bytes.
+ *   workspace device scratch of moe_permute_workspace_size(T, k, E) bytes
+ *             (per-chunk expert histograms; moe_permute_nvfp4 also keeps the
+ *             parts of its activation amax there).
  */
 size_t moe_permute_workspace_size(int64_t T, int k, int E);
 int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype,

@@ -24,23 +24,61 @@ namespace {
 
 constexpr int kChunk = 1024;      // assignments per chunk (4 waves x 4 steps x 64)
 constexpr int kMaxExperts = 4096;
+constexpr int kAmaxParts = 256;   // workgroups that reduce the activation amax with the histograms
+// Byte offset of the amax parts in the permutation workspace (after the
+// per-chunk histograms, 256-byte aligned).
+constexpr int64_t amax_parts_offset(int64_t chunks, int E) { return (chunks * E * 4 + 255) / 256 * 256; }
 
-__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ ids, int64_t R, int E,
-                                                    int32_t* __restrict__ counts, float* __restrict__ amax_out) {
+__device__ __forceinline__ float max_abs_bf16x8(const uint4 v) {
+  const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[j])), fabsf(bf16_hi(ws[j]))));
+  return m;
+}
+
+// Workgroups below `chunks` build one chunk's histogram.  With x given (the
+// fused permute-quantize), every workgroup also takes the max |x| of its
+// contiguous slice of the n16 16-byte words of X and stores it in
+// amax_part[blockIdx.x] (no atomics; the scan kernel reduces the parts).
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ ids, int64_t R, int E, int64_t chunks,
+                                                    int32_t* __restrict__ counts, float* __restrict__ amax_out,
+                                                    const uint4* __restrict__ x, int64_t n16,
+                                                    float* __restrict__ amax_part) {
   __shared__ int32_t hist[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0 && amax_out) *amax_out = 0.0f;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kChunk;
-  for (int i = threadIdx.x; i < kChunk; i += 256) {
-    const int64_t a = base + i;
-    if (a < R) {
-      const int32_t e = ids[a];
-      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  __shared__ float red[4];
+  if (blockIdx.x < chunks) {
+    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && amax_out) *amax_out = 0.0f;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kChunk;
+    for (int i = threadIdx.x; i < kChunk; i += 256) {
+      const int64_t a = base + i;
+      if (a < R) {
+        const int32_t e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+      }
     }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = hist[e];
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+  if (x) {
+    const int64_t w0 = n16 * blockIdx.x / gridDim.x, w1 = n16 * (blockIdx.x + 1) / gridDim.x;
+    float m = 0.0f;
+    int64_t i = w0 + threadIdx.x;
+    for (; i + 3 * 256 < w1; i += 4 * 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = x[i + u * 256];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) m = fmaxf(m, max_abs_bf16x8(v[u]));
+    }
+    for (; i < w1; i += 256) m = fmaxf(m, max_abs_bf16x8(x[i]));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) amax_part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
 }
 
 // counts[c][e] (in) -> first permuted row of (chunk c, expert e) (out);
@@ -51,13 +89,30 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
 // ceil(nchunks / slices) long; the walks read kScanBatch counts at a time so
 // that their loads are in flight together.
 constexpr int kScanBatch = 8;
+//
+// With amax_part given, it also reduces the nparts activation-amax parts of
+// the histogram launch into amax_out[0].
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int64_t nchunks, int E,
                                                     int32_t* __restrict__ offsets, int64_t R,
-                                                    int32_t* __restrict__ src) {
+                                                    int32_t* __restrict__ src, const float* __restrict__ amax_part,
+                                                    int nparts, float* __restrict__ amax_out) {
   __shared__ int32_t ssum[kMaxExperts];   // per (expert, slice) partial sums
   __shared__ int32_t ebase[kMaxExperts];  // per expert first row
   __shared__ int32_t wsum[16];
   __shared__ int32_t s_valid;
+  __shared__ float amax_red[16];
+  if (amax_part) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += 1024) m = fmaxf(m, amax_part[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) amax_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float v = amax_red[0];
+      for (int w = 1; w < 16; ++w) v = fmaxf(v, amax_red[w]);
+      *amax_out = v;
+    }
+  }
   const int slices = E >= 1024 ? 1 : 1024 / E;
   const int64_t cps = (nchunks + slices - 1) / slices;
   // Phase 1: slice sums.
@@ -434,25 +489,23 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint8_t* __restric
 
 namespace nvfp4moe {
 // Routing metadata for R assignments: histograms, scan (with the src tail),
-// stable ranks.  amax_cleared (nullable) is zeroed by the first kernel;
-// `between` enqueues work that runs after it and before the scan.
-template <class Between>
+// stable ranks.  amax_cleared (nullable) is zeroed by the first kernel.
+// With amax_x given (n16 16-byte bf16 words), the histogram launch also
+// reduces max |x| in parts (workspace after the counts) and the scan writes
+// it to amax_dst: no separate amax launch.
 static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* amax_cleared, void* workspace,
                            int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st,
-                           Between between) {
+                           const void* amax_x = nullptr, int64_t amax_n16 = 0, float* amax_dst = nullptr) {
   const int64_t chunks = cdiv(R, kChunk);
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
-  count_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, amax_cleared);
-  const int rc = between();
-  if (rc != NVFP4MOE_OK) return rc;
-  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets, R, src);
+  float* parts = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + amax_parts_offset(chunks, E));
+  const int64_t nblk = amax_x ? (chunks > kAmaxParts ? chunks : kAmaxParts) : chunks;
+  count_kernel<<<(unsigned)nblk, 256, 0, st>>>(topk_ids, R, E, chunks, counts, amax_cleared,
+                                               reinterpret_cast<const uint4*>(amax_x), amax_n16, parts);
+  scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets, R, src, amax_x ? parts : nullptr, (int)nblk,
+                                  amax_dst);
   rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
   return launch_status();
-}
-static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* amax_cleared, void* workspace,
-                           int32_t* offsets, int32_t* dest, int32_t* src, int32_t* status, hipStream_t st) {
-  return launch_metadata(topk_ids, R, E, amax_cleared, workspace, offsets, dest, src, status, st,
-                         [] { return (int)NVFP4MOE_OK; });
 }
 }  // namespace nvfp4moe
 
@@ -461,7 +514,9 @@ using namespace nvfp4moe;
 extern "C" size_t moe_permute_workspace_size(int64_t T, int k, int E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   const int64_t chunks = cdiv(T * k, kChunk);
-  return (size_t)((chunks > 0 ? chunks : 1) * E * 4 + 256);
+  // per-chunk histograms, then the amax parts of the fused permute-quantize
+  const int64_t parts = chunks > kAmaxParts ? chunks : kAmaxParts;
+  return (size_t)(amax_parts_offset(chunks > 0 ? chunks : 1, E) + parts * 4);
 }
 
 extern "C" int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype,
@@ -569,14 +624,10 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
     }
     fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
   } else {
-    // The activation amax is taken once, over the T unpermuted rows, right
-    // after the histogram kernel has cleared amax_out.
-    const int rc = launch_metadata(topk_ids, R, E, amax_in ? nullptr : amax_out, workspace, offsets, dest, src,
-                                   status, st, [&] {
-                                     return amax_in ? (int)NVFP4MOE_OK
-                                                    : launch_amax_uncleared(x, NVFP4MOE_BF16, T * D * 2 / 16, 1,
-                                                                            amax_out, st);
-                                   });
+    // The activation amax is taken once, over the T unpermuted rows, by the
+    // histogram launch (in parts) and the scan (their max).
+    const int rc = launch_metadata(topk_ids, R, E, nullptr, workspace, offsets, dest, src, status, st,
+                                   amax_in ? nullptr : x, T * D * 2 / 16, amax_in ? nullptr : amax_out);
     if (rc != NVFP4MOE_OK) return rc;
   }
   // Launched even without rows: it also writes the global scale.
