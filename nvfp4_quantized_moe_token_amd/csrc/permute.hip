@@ -7,10 +7,12 @@
 // Metadata is a deterministic stable counting sort of the flattened
 // assignments i = t*k + j by expert id:
 //   1. count_kernel  -- per chunk of kChunk assignments, a histogram over
-//                       experts (LDS atomics; counts are order-free).
+//                       experts (LDS atomics; counts are order-free); for
+//                       the fused permute-quantize also max |x| of X in parts.
 //   2. scan_kernel   -- one workgroup: per-expert totals -> offsets, and
 //                       the first row of every (chunk, expert) pair; src
-//                       entries past the valid assignments become -1.
+//                       entries past the valid assignments become -1; the
+//                       max of the amax parts.
 //   3. rank_kernel   -- per chunk, four waves walk their 256 assignments in
 //                       64-lane steps; equal ids inside a step are matched
 //                       with ballots over the id bits, so the rank of an
