@@ -88,6 +88,11 @@ def test_permute_validation(lib):
     ws = lib.moe_permute_workspace_size(100, 8, 128)
     assert ws >= 128 * 4
     assert lib.moe_permute_workspace_size(-1, 8, 128) == 0
+    # histograms (one per 1024 assignments) plus the fused call's amax parts
+    # (one per histogram workgroup, at least 256)
+    for T, k, E in [(100, 8, 128), (8192, 8, 128), (131072, 8, 128), (1, 1, 4096)]:
+        chunks = -(-T * k // 1024)
+        assert lib.moe_permute_workspace_size(T, k, E) >= chunks * E * 4 + max(chunks, 256) * 4
     assert p(FAKE, 100, 0, 128, None, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, ws, None, None) == -1  # k = 0
     assert p(FAKE, 100, 8, 5000, None, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 10 ** 9, None, None) == -2  # E too big
     assert p(FAKE, 100, 8, 128, None, 1, 0, None, None, FAKE, FAKE, None, FAKE, ws, None, None) == -1  # offsets NULL
