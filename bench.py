@@ -309,6 +309,56 @@ def pmc_summary(fetch_dir, write_dir, clock_dir=None):
     print("\n".join(lines))
 
 
+def mfma_summary(d):
+    """Per op of one moe_8k_update step, from a rocprofv3 --pmc run of
+    `bench.py --pmc-run` with SQ_INSTS_VALU_MFMA_MOPS_F16,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE:
+    the MFMA FLOPs the hardware executed (MOPS x 512) against the algorithmic
+    FLOPs (the difference is tile padding), the executed TFLOP/s over the ops'
+    dispatch time, and the fraction of SIMD cycles the MFMA unit was busy."""
+    import csv
+    vals, names, ns = {}, {}, {}
+    for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                i = int(r["Dispatch_Id"])
+                names[i] = r["Kernel_Name"]
+                ns[i] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                c = vals.setdefault(i, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(vals)
+    marks = [j for j, i in enumerate(ids) if MARKER in names[i]][-(len(STEP_OPS) + 1):]
+    T, k, E, D, F = 8192, 8, 128, 2048, 768
+    simds = 256 * 4
+    lines = ["# MFMA work per op of one moe_8k_update step (8192 tokens, d_model 2048, 128 experts, top-8, FFN 768),",
+             "# from one rocprofv3 --pmc run of `bench.py --pmc-run` (counters summed over each op's dispatches).",
+             "# executed = (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16) x 512 FLOPs; algorithmic = 2*M*N*K of the op;",
+             "# busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); TFLOP/s over the",
+             "# dispatch time; peak 2516.6 TFLOP/s (16-bit dense MFMA at 2.4 GHz).",
+             "# command ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&",
+             "#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES",
+             "#   GRBM_GUI_ACTIVE --output-format csv -d $OUT/pmc_mfma -o run -- python $REPO/bench.py --pmc-run",
+             "#   --steps 2 --warmup 1, then python $REPO/bench.py --mfma-summary $OUT/pmc_mfma",
+             "sources %s" % source_digest(),
+             "%-20s %12s %12s %8s %10s %10s %8s %8s" % ("op", "exec_GF", "algo_GF", "exec/alg", "us", "exec_TF",
+                                                      "of_peak", "busy")]
+    for j, name in enumerate(STEP_OPS):
+        seg = ids[marks[j] + 1:marks[j + 1]]
+        mops = sum(vals[i].get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + vals[i].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+                   for i in seg)
+        if mops == 0:
+            continue
+        ex = mops * 512.0
+        alg = op_work(name, T, k, E, D, F)[0]
+        t = sum(ns[i] for i in seg)
+        busy = sum(vals[i].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for i in seg)
+        gui = sum(vals[i].get("GRBM_GUI_ACTIVE", 0.0) for i in seg) / 8.0
+        lines.append("%-20s %12.1f %12.1f %8.3f %10.1f %10.1f %7.1f%% %7.1f%%" % (
+            name, ex / 1e9, alg / 1e9, ex / alg, t / 1e3, ex / (t * 1e-9) / 1e12,
+            100.0 * ex / (t * 1e-9) / 1e12 / PEAK_BF16_TFLOPS, 100.0 * busy / (gui * simds) if gui else 0.0))
+    print("\n".join(lines))
+
+
 # Ops that launch the same kernel (one template instance per GEMM mode): the
 # roofline of a kernel averages over all of its launches in a step, as
 # rocprofv3's per-kernel statistics do.
@@ -454,11 +504,16 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE run directories, optionally a GRBM_GUI_ACTIVE one")
     ap.add_argument("--kernel-stats-summary", metavar="DIR")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="per-op executed MFMA FLOPs and MFMA busy fraction from a --pmc-run counter run")
     ap.add_argument("--dispatch-summary", nargs=2, metavar=("DIR", "KERNEL"),
                     help="per-launch durations of one kernel in a kernel-trace run, by grid size")
     args = ap.parse_args()
     if args.dispatch_summary:
         dispatch_summary(*args.dispatch_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)

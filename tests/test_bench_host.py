@@ -87,3 +87,30 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_mfma_summary_counts_executed_flops(tmp_path, capsys):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows, i = [], 0
+    T, k, E, D, F = 8192, 8, 128, 2048, 768
+    for name in bench.STEP_OPS:
+        rows.append([i, "void at::native::FillFunctor<int>", "GRBM_GUI_ACTIVE", 0.0, 0, 1]); i += 1
+        alg = bench.op_work(name, T, k, E, D, F)[0]
+        if alg:
+            # executed = algorithmic + 10%, over 1 ms; MFMA busy half of 1000 cycles on every SIMD
+            for cn, v in (("SQ_INSTS_VALU_MFMA_MOPS_F16", alg * 1.1 / 512), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0),
+                          ("SQ_VALU_MFMA_BUSY_CYCLES", 500.0 * 1024), ("GRBM_GUI_ACTIVE", 1000.0 * 8)):
+                rows.append([i, "gemm_" + name, cn, v, 0, 1_000_000])
+            i += 1
+        else:
+            rows.append([i, "elementwise_" + name, "SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0, 0, 1000]); i += 1
+    rows.append([i, "void at::native::FillFunctor<int>", "GRBM_GUI_ACTIVE", 0.0, 0, 1])
+    _write(str(tmp_path / "m" / "run_counter_collection.csv"), hdr, rows)
+    bench.mfma_summary(str(tmp_path / "m"))
+    ops = [l.split() for l in capsys.readouterr().out.splitlines() if l and not l.startswith(("#", "sources", "op "))]
+    gemm_ops = [n for n in bench.STEP_OPS if bench.op_work(n, T, k, E, D, F)[0]]
+    assert [o[0] for o in ops] == gemm_ops
+    for o in ops:
+        assert float(o[3]) == pytest.approx(1.1, abs=1e-3)      # executed / algorithmic
+        assert float(o[4]) == pytest.approx(1000.0)             # us
+        assert o[7] == "50.0%"                                  # MFMA busy
