@@ -238,6 +238,25 @@ def load_traffic():
     return out if digest == source_digest() else {}
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_moe_8k_update.txt")
+
+
+def load_mfma():
+    """Per-op MFMA counters (executed GFLOP, MFMA busy fraction) from the
+    committed summary, or {} when absent or taken on different sources."""
+    if not os.path.exists(MFMA_FILE):
+        return {}
+    digest, out = None, {}
+    with open(MFMA_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "sources":
+                digest = parts[1]
+            elif len(parts) == 8 and parts[0] in STEP_OPS:
+                out[parts[0]] = {"executed_gflop": float(parts[1]), "mfma_busy": round(float(parts[7].rstrip("%")) / 100, 4)}
+    return out if digest == source_digest() else {}
+
+
 def short_name(n):
     """Kernel name without namespace, return type and parameter list."""
     n = n.replace("(anonymous namespace)::", "").replace("nvfp4moe::", "")
@@ -698,6 +717,7 @@ def main():
     step_flops = (f1 + f2) * (3 if backward else 1)
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
     traffic = load_traffic()
+    mfma = load_mfma() if (T, k, E, D, F) == (8192, 8, 128, 2048, 768) else {}
     kernels = {}
     for name, ms in list(per_op.items()) + list(per_op_extra.items()):
         fl, by = op_work(name, T, k, E, D, F, backward)
@@ -718,6 +738,11 @@ def main():
             if fl:
                 ent["frac_bf16_peak_at_sustained_clock"] = round(
                     ent["tflops"] / (PEAK_BF16_TFLOPS * tr["clock_ghz"] / PEAK_CLOCK_GHZ), 4)
+        if name in mfma:
+            # rocprofv3 counters (profiles/): MFMA FLOPs executed (padding
+            # included) and the MFMA unit's busy fraction of SIMD cycles
+            ent["mfma_executed_gflop_counter"] = mfma[name]["executed_gflop"]
+            ent["mfma_busy_counter"] = mfma[name]["mfma_busy"]
         kernels[name] = ent
 
     def traffic_bytes(names):
@@ -766,6 +791,10 @@ def main():
         common = {"traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "algorithmic_flops": round(fl),
                   "flop_per_byte": round(fl / by, 1), "ridge_flop_per_byte": round(RIDGE, 1),
                   "avg_launch_ms": round(ms, 4)}
+        if all(o in mfma for o in names):
+            # time-weighted MFMA busy fraction of the kernel's launches (counters)
+            common["mfma_busy_counter"] = round(sum(mfma[o]["mfma_busy"] * per_op[o] for o in names) /
+                                                sum(per_op[o] for o in names), 4)
         if fl / by < RIDGE:
             return {"kernel": kname, "ops": names, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), **common,

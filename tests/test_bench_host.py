@@ -114,3 +114,18 @@ def test_mfma_summary_counts_executed_flops(tmp_path, capsys):
         assert float(o[3]) == pytest.approx(1.1, abs=1e-3)      # executed / algorithmic
         assert float(o[4]) == pytest.approx(1000.0)             # us
         assert o[7] == "50.0%"                                  # MFMA busy
+
+
+def test_committed_mfma_summary_parses():
+    """The committed MFMA summary lists the step's GEMM ops with their busy
+    fractions; load_mfma returns them when the sources fingerprint matches."""
+    path = os.path.join(ROOT, "profiles", "mfma_moe_8k_update.txt")
+    lines = open(path).read().splitlines()
+    assert any(l.startswith("sources ") for l in lines)
+    rows = [l.split() for l in lines if l.split() and l.split()[0] in bench.STEP_OPS]
+    assert {r[0] for r in rows} >= {"w4a4_gate_up_silu", "w4a4_down", "bf16_tn_gate_up", "bf16_nn_gate_up"}
+    for r in rows:
+        assert 0.0 < float(r[7].rstrip("%")) < 100.0
+        assert 1.0 <= float(r[3]) < 1.2                 # executed / algorithmic: padding only
+    m = bench.load_mfma()
+    assert m == {} or set(m) == {r[0] for r in rows}
