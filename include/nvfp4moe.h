@@ -150,8 +150,9 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x,
  * metadata, amax reuse and op fusion: [JA], fourth paragraph).  Computes the
  * same offsets/dest/src as moe_permute, optionally the bf16 rows x_perm, and
  * q/scales/gscale equal to nvfp4_quantize(x_perm, groups = 1, amax) --
- * bit for bit -- without reading x_perm back: each permuted row is encoded
- * while it is gathered from x.
+ * bit for bit -- without reading x_perm back: each row of x is encoded once
+ * and its codes and scales (and bf16 copy) are written to its k permuted
+ * rows.
  *   x        [T][D] bf16, 16-byte aligned; D % 16 == 0.
  *   x_perm   [T*k][D] bf16 out, or NULL when only the NVFP4 rows are needed.
  *   amax_in  fp32 [1] or NULL.  When NULL, max |x| over the T rows of x

@@ -383,41 +383,31 @@ int gather_dispatch(const void* x, int x_dtype, int64_t row_elems, const int32_t
   return NVFP4MOE_EINVAL;
 }
 
-// Gather fused with NVFP4 quantization of the gathered rows (token-wise
-// path with op fusion: "miniTE報告、NVFP4強化学習の安定性を検証", fourth
-// paragraph).  Thread-blocks walk the 16-element blocks b = p*bpr + j of the
-// permuted rows: each reads its 32 bytes from token src[p]/k, optionally
-// stores them to x_perm, and writes the block's codes and scale with the
-// same encoding as nvfp4_quantize on x_perm (so the result equals
-// quantize(permute(X)), which equals permute(quantize(X)) row by row).
-// Rows with src < 0 (past offsets[E]) are zeros.  X is read once per
-// assignment from cache instead of X_perm being re-read from HBM.
+// Permutation fused with NVFP4 quantization (token-wise path with op
+// fusion: "miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph), by
+// scatter: each 16-element block of X is read once (T rows, not the T*k
+// permuted ones), quantized once, and its codes and scale (and its bf16 copy
+// when x_perm is wanted) are written to the k permuted rows dest[t*k+j] of
+// its token.  Rows past offsets[E] (skipped assignments) are written as
+// zeros.  quantize(permute(X)) == permute(quantize(X)) row by row, so the
+// result equals nvfp4_quantize on the gathered X_perm.  One thread per block
+// of X; the amax is read after the block's loads are issued (the empty asm
+// keeps the compiler from hoisting it), so the latencies overlap.
 template <int NT>
-__global__ __launch_bounds__(NT) void gather_quantize_kernel(const uint4* __restrict__ x, int64_t bpr,
-                                                             const int32_t* __restrict__ src, int k, int64_t R,
-                                                             uint4* __restrict__ x_perm, const float* __restrict__ amax,
-                                                             uint2* __restrict__ q, uint8_t* __restrict__ scales,
-                                                             float* __restrict__ gscale) {
+__global__ __launch_bounds__(NT) void quantize_scatter_kernel(const uint4* __restrict__ x, int64_t T, int k,
+                                                              int64_t bpr, const int32_t* __restrict__ dest,
+                                                              const int32_t* __restrict__ offsets, int E, int64_t R,
+                                                              uint4* __restrict__ x_perm,
+                                                              const float* __restrict__ amax, uint2* __restrict__ q,
+                                                              uint8_t* __restrict__ scales, float* __restrict__ gscale) {
   if (blockIdx.x == 0 && threadIdx.x == 0) gscale[0] = global_scale(amax[0]);
-  const int64_t nblk = R * bpr;
-  for (int64_t b = blockIdx.x * (int64_t)NT + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * NT) {
-    const int64_t p = b / bpr, j = b - p * bpr;
-    const int32_t s = src[p];
-    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-    if (s >= 0) {
-      const uint4* in = x + ((int64_t)(s / k) * bpr + j) * 2;
-      w0 = in[0];
-      w1 = in[1];
-    }
-    // amax is read after the row's loads are issued (the empty asm keeps the
-    // compiler from hoisting it out of the loop), so the three loads (src,
-    // the row, amax) cost two latencies rather than three.
+  const int64_t nblk = T * bpr;
+  const int64_t tid = blockIdx.x * (int64_t)NT + threadIdx.x, stride = (int64_t)gridDim.x * NT;
+  for (int64_t b = tid; b < nblk; b += stride) {
+    const int64_t t = b / bpr, j = b - t * bpr;
+    const uint4 w0 = x[2 * b], w1 = x[2 * b + 1];
     asm volatile("" ::: "memory");
     const float g = global_scale(amax[0]);
-    if (x_perm) {
-      x_perm[2 * b] = w0;
-      x_perm[2 * b + 1] = w1;
-    }
     const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     float v[16];
 #pragma unroll
@@ -428,8 +418,27 @@ __global__ __launch_bounds__(NT) void gather_quantize_kernel(const uint4* __rest
     uint2 codes;
     uint32_t S;
     quantize_block(v, g, codes, S);
-    q[b] = codes;
-    scales[b] = (uint8_t)S;
+    for (int jj = 0; jj < k; ++jj) {
+      const int32_t r = dest[t * k + jj];
+      if (r < 0) continue;
+      const int64_t ob = (int64_t)r * bpr + j;
+      if (x_perm) {
+        x_perm[2 * ob] = w0;
+        x_perm[2 * ob + 1] = w1;
+      }
+      q[ob] = codes;
+      scales[ob] = (uint8_t)S;
+    }
+  }
+  int64_t valid = offsets[E];
+  valid = valid < 0 ? 0 : valid > R ? R : valid;
+  for (int64_t b = valid * bpr + tid; b < R * bpr; b += stride) {
+    if (x_perm) {
+      x_perm[2 * b] = make_uint4(0, 0, 0, 0);
+      x_perm[2 * b + 1] = make_uint4(0, 0, 0, 0);
+    }
+    q[b] = make_uint2(0, 0);
+    scales[b] = 0;
   }
 }
 
@@ -633,11 +642,11 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
     if (rc != NVFP4MOE_OK) return rc;
   }
   // Launched even without rows: it also writes the global scale.
-  const int64_t bpr = D / 16, nblk = R * bpr;
+  const int64_t bpr = D / 16, nblk = T * bpr;
   int64_t grid = cdiv(nblk > 0 ? nblk : 1, 256);
   if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
-  gather_quantize_kernel<256><<<(unsigned)grid, 256, 0, st>>>(
-      reinterpret_cast<const uint4*>(x), bpr, src, k, R, reinterpret_cast<uint4*>(x_perm), amax,
+  quantize_scatter_kernel<256><<<(unsigned)grid, 256, 0, st>>>(
+      reinterpret_cast<const uint4*>(x), T, k, bpr, dest, offsets, E, R, reinterpret_cast<uint4*>(x_perm), amax,
       reinterpret_cast<uint2*>(q), scales, gscale);
   return launch_status();
 }
