@@ -25,6 +25,7 @@ Prints one JSON line (N = 1).
 """
 
 import argparse
+import gc
 import glob
 import hashlib
 import json
@@ -145,7 +146,8 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
     ]
     if backward:
         seq += [
-            ("gather_dy", lambda: ops.moe_gather(inp["dy"], m()["src"], k, topk_w=inp["tw"], out=buf.dy2)),
+            ("gather_dy", lambda: ops.moe_scatter(inp["dy"], m()["dest"], m()["offsets"], k, topk_w=inp["tw"],
+                                                  out=buf.dy2)),
             ("bf16_nn_down", lambda: ops.grouped_gemm_bf16(ops.NN, buf.dy2, inp["w_dn"], m()["offsets"],
                                                            out=buf.dh)),
             ("silu_gate_bwd", lambda: ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)),
@@ -586,6 +588,14 @@ def main():
     meta_box = {}
     seq = step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward)
     wstream = torch.cuda.Stream() if (args.overlap and backward) else None
+    # Python's garbage collector is paused from here to the end of the timed
+    # steps: a full collection in the middle of a step stalls the launching
+    # thread for tens of milliseconds, and the GPU idles once it has drained
+    # what was queued.  The collection that precedes the pause runs before
+    # the warmup, so the GPU is back at its working clock when timing starts
+    # (an idle gap just before the timed region cost ~3% in measurements).
+    gc.collect()
+    gc.disable()
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         run_step(torch, seq, wstream, False)
@@ -615,6 +625,7 @@ def main():
         marks.append(run_step(torch, seq, wstream, True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ms_per_step = wall * 1e3 / args.steps
     per_op = {}
     for evs in marks:
@@ -638,6 +649,7 @@ def main():
         with torch.cuda.graph(graph):
             for _, fn in seq:
                 fn()
+        gc.disable()
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
@@ -646,6 +658,7 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        gc.enable()
 
     # The plain W4A4 gate+up GEMM (bf16 Y1, no epilogue) and the BF16 grouped
     # GEMM on the same shape and routing, each timed alone; the latter and

@@ -183,6 +183,24 @@ int moe_gather(const void* x, int x_dtype, int64_t row_elems, const int32_t* src
                nvfp4moe_stream_t stream);
 
 /*
+ * moe_scatter -- the same rows as moe_gather with weights, written from the
+ * token side: out[dest[t*k+j]] = w[t*k+j] * x[t] (w = 1 when topk_w is NULL),
+ * scaled in fp32 and rounded to out_dtype (RNE); assignments with dest < 0
+ * are skipped and rows of out past offsets[E] are written as zeros.  Equal,
+ * bit for bit, to moe_gather(x, src, topk_w) for the src and dest of one
+ * permutation; each row of x is read once.  Row i of the backward's
+ * dY2[dest] = w * dY ([JA] first paragraph: the BF16 backward).
+ *   x [T][row_elems] F32/BF16, dest [T*k], topk_w [T*k] fp32 or NULL,
+ *   offsets [E+1] (device), out [T*k][row_elems]; 16-byte aligned rows,
+ *   row_elems % 8 == 0.
+ * Errors: EINVAL (NULL, negative sizes, bad dtype), ESHAPE (row_elems % 8,
+ * alignment, T*k >= 2^31).
+ */
+int moe_scatter(const void* x, int x_dtype, int64_t row_elems, const int32_t* dest,
+                const float* topk_w, const int32_t* offsets, int E, int64_t T, int k, void* out,
+                int out_dtype, nvfp4moe_stream_t stream);
+
+/*
  * moe_unpermute -- out[t] = sum_{j=0..k-1} w[t][j] * y_perm[dest[t*k+j]]
  * (w = 1 when topk_w is NULL: the gradient of the row gather), accumulated
  * in fp32 in ascending j with fused multiply-add, then rounded to out_dtype

@@ -23,6 +23,7 @@ SIGNATURES = {
     "moe_permute_nvfp4": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_size, c_vp, c_vp]),
     "moe_gather": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_vp]),
+    "moe_scatter": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_int, c_i64, c_int, c_vp, c_int, c_vp]),
     "moe_unpermute": (c_int, [c_vp, c_int, c_vp, c_vp, c_i64, c_int, c_i64, c_vp, c_int, c_vp]),
     "grouped_gemm_w4a4": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
                                   c_vp, c_int, c_int, c_vp, c_vp, c_size, c_vp]),

@@ -383,6 +383,38 @@ int gather_dispatch(const void* x, int x_dtype, int64_t row_elems, const int32_t
   return NVFP4MOE_EINVAL;
 }
 
+// Eight values of a row piece (bf16 or fp32) as fp32, and back (bf16: RNE).
+template <int IN>
+__device__ __forceinline__ void load8(const uint8_t* in, float (&v)[8]) {
+  if (IN == NVFP4MOE_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(in);
+    const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_lo(ws[q]);
+      v[2 * q + 1] = bf16_hi(ws[q]);
+    }
+  } else {
+    const uint4 u0 = reinterpret_cast<const uint4*>(in)[0], u1 = reinterpret_cast<const uint4*>(in)[1];
+    v[0] = __uint_as_float(u0.x); v[1] = __uint_as_float(u0.y);
+    v[2] = __uint_as_float(u0.z); v[3] = __uint_as_float(u0.w);
+    v[4] = __uint_as_float(u1.x); v[5] = __uint_as_float(u1.y);
+    v[6] = __uint_as_float(u1.z); v[7] = __uint_as_float(u1.w);
+  }
+}
+template <int OUT>
+__device__ __forceinline__ void store8(uint8_t* o, const float (&v)[8]) {
+  if (OUT == NVFP4MOE_BF16) {
+    *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  } else {
+    reinterpret_cast<uint4*>(o)[0] =
+        make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    reinterpret_cast<uint4*>(o)[1] =
+        make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
+  }
+}
+
 // Permutation fused with NVFP4 quantization (token-wise path with op
 // fusion: "miniTE報告、NVFP4強化学習の安定性を検証", fourth paragraph), by
 // scatter: each 16-element block of X is read once (T rows, not the T*k
@@ -439,6 +471,40 @@ __global__ __launch_bounds__(NT) void quantize_scatter_kernel(const uint4* __res
     }
     q[b] = make_uint2(0, 0);
     scales[b] = 0;
+  }
+}
+
+// out[dest[t*k+j]] = w[t*k+j] * x[t] (w = 1 when NULL), fp32 product rounded
+// to the output type: the scatter form of the weighted gather.  One thread
+// per 8-element piece of a token row: the piece is read once and written to
+// the token's k permuted rows.  Rows of out past offsets[E] are zeros.
+template <int IN, int OUT>
+__global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict__ x, int64_t T, int k, int64_t n8,
+                                                      const int32_t* __restrict__ dest, const float* __restrict__ w,
+                                                      const int32_t* __restrict__ offsets, int E, int64_t R,
+                                                      uint8_t* __restrict__ out) {
+  constexpr int ib = IN == NVFP4MOE_F32 ? 4 : 2;
+  constexpr int ob = OUT == NVFP4MOE_F32 ? 4 : 2;
+  const int64_t tid = blockIdx.x * 256ll + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = tid; i < T * n8; i += stride) {
+    const int64_t t = i / n8, c = i - t * n8;
+    float v[8];
+    load8<IN>(x + (t * n8 + c) * 8 * ib, v);
+    for (int j = 0; j < k; ++j) {
+      const int32_t r = dest[t * k + j];
+      if (r < 0) continue;
+      const float wt = w ? w[t * k + j] : 1.0f;
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = v[q] * wt;
+      store8<OUT>(out + ((int64_t)r * n8 + c) * 8 * ob, o);
+    }
+  }
+  int64_t valid = offsets[E];
+  valid = valid < 0 ? 0 : valid > R ? R : valid;
+  for (int64_t i = valid * n8 + tid; i < R * n8; i += stride) {
+    float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    store8<OUT>(out + i * 8 * ob, z);
   }
 }
 
@@ -580,6 +646,38 @@ extern "C" int moe_gather(const void* x, int x_dtype, int64_t row_elems, const i
   if (arch != NVFP4MOE_OK) return arch;
   if (R == 0 || row_elems == 0) return NVFP4MOE_OK;
   return gather_dispatch(x, x_dtype, row_elems, src, topk_w, k, R, out, out_dtype, nullptr, as_stream(stream));
+}
+
+extern "C" int moe_scatter(const void* x, int x_dtype, int64_t row_elems, const int32_t* dest, const float* topk_w,
+                           const int32_t* offsets, int E, int64_t T, int k, void* out, int out_dtype,
+                           nvfp4moe_stream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || row_elems < 0) return NVFP4MOE_EINVAL;
+  if ((x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16) || (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16))
+    return NVFP4MOE_EINVAL;
+  if (!offsets) return NVFP4MOE_EINVAL;
+  if (T > 0 && row_elems > 0 && (!x || !dest || !out)) return NVFP4MOE_EINVAL;
+  if (row_elems % 8 != 0 || !aligned(x, 16) || !aligned(out, 16)) return NVFP4MOE_ESHAPE;
+  if (T * k > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  const int64_t R = T * k, n8 = row_elems / 8;
+  if (R == 0 || n8 == 0) return NVFP4MOE_OK;
+  int64_t grid = cdiv(T * n8, 256);
+  if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
+  hipStream_t st = as_stream(stream);
+  const uint8_t* xi = reinterpret_cast<const uint8_t*>(x);
+  uint8_t* o = reinterpret_cast<uint8_t*>(out);
+#define NVS(I, O)                                                                                                 \
+  if (x_dtype == I && out_dtype == O) {                                                                          \
+    scatter_kernel<I, O><<<(unsigned)grid, 256, 0, st>>>(xi, T, k, n8, dest, topk_w, offsets, E, R, o);          \
+    return launch_status();                                                                                      \
+  }
+  NVS(NVFP4MOE_BF16, NVFP4MOE_BF16)
+  NVS(NVFP4MOE_BF16, NVFP4MOE_F32)
+  NVS(NVFP4MOE_F32, NVFP4MOE_F32)
+  NVS(NVFP4MOE_F32, NVFP4MOE_BF16)
+#undef NVS
+  return NVFP4MOE_EINVAL;
 }
 
 extern "C" int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* dest, const float* topk_w, int64_t T,

@@ -12,7 +12,7 @@ contiguous layout, device-side metadata, amax reuse, grouped GEMM, fusion):
   moe_unpermute (routing-weighted combine).  When F is not a multiple of 128
   the gate+up GEMM and silu_gate_fwd run as two launches.
 Backward in BF16 (same page, first paragraph), no amax reduction at all:
-  moe_gather(dY, weighted)  ->  NN dgrad of the down projection  ->
+  moe_scatter(dY, weighted)  ->  NN dgrad of the down projection  ->
   silu_gate_bwd  ->  TN wgrad of the down projection  ->  NN dgrad of gate+up
   ->  moe_unpermute (unweighted sum back to tokens)  ->  TN wgrad of gate+up,
   on the kept permuted rows, or with its activation rows gathered from X
@@ -115,7 +115,7 @@ def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None, x=None):
         with torch.cuda.stream(wgrad_stream):
             tn(a, b, out, gather)
 
-    ops.moe_gather(dy, meta["src"], buf.k, topk_w=topk_w, out=buf.dy2)
+    ops.moe_scatter(dy, meta["dest"], meta["offsets"], buf.k, topk_w=topk_w, out=buf.dy2)
     if wgrad_stream is not None:
         wgrad(buf.dy2, buf.h, buf.dw_dn)
     ops.grouped_gemm_bf16(ops.NN, buf.dy2, w_dn, off, out=buf.dh)

@@ -145,6 +145,22 @@ def moe_gather(x, src, k, topk_w=None, out=None, out_dtype=None):
     return out
 
 
+def moe_scatter(x, dest, offsets, k, topk_w=None, out=None, out_dtype=None):
+    """out[dest[t*k+j]] = w[t*k+j] * x[t]: the weighted gather written from the
+    token side (each row of x read once); rows past offsets[E] are zeros."""
+    _dev(x, dest, offsets, topk_w, out)
+    T = x.shape[0]
+    R = T * k
+    E = offsets.numel() - 1
+    row_elems = x.shape[1] if x.dim() == 2 else x[0].numel()
+    odt = x.dtype if out_dtype is None else out_dtype
+    out = torch.empty((R,) + tuple(x.shape[1:]), dtype=odt, device=x.device) if out is None else out
+    rc = _lib.load().moe_scatter(_ptr(x), _DT[x.dtype], row_elems, _ptr(dest), _ptr(topk_w), _ptr(offsets), E, T,
+                                 k, _ptr(out), _DT[out.dtype], _stream())
+    _check("moe_scatter", rc)
+    return out
+
+
 def moe_unpermute(y_perm, dest, T, k, topk_w=None, out=None, out_dtype=torch.bfloat16):
     """out[t] = sum_j w[t, j] * y_perm[dest[t*k + j]]."""
     _dev(y_perm, dest, topk_w, out)

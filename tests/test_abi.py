@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
-              "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16",
+              "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "moe_scatter",
               "grouped_gemm_bf16_tn_gather", "silu_gate_fwd",
               "silu_gate_bwd", "moe_permute_nvfp4",
               "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
@@ -125,6 +125,11 @@ def test_gather_unpermute_validation(lib):
     assert lib.moe_gather(FAKE, 1, 64, FAKE, None, 0, 10, FAKE, 1, None) == -1
     assert lib.moe_gather(FAKE, 2, 64, FAKE, FAKE, 8, 10, FAKE, 2, None) == -1  # weighted bytes
     assert lib.moe_gather(FAKE, 1, 12, FAKE, FAKE, 8, 10, FAKE, 1, None) == -2
+    sc = lib.moe_scatter
+    assert sc(FAKE, 1, 64, FAKE, None, FAKE, 4, 10, 0, FAKE, 1, None) == -1       # k = 0
+    assert sc(FAKE, 2, 64, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None) == -1       # u8 payload
+    assert sc(FAKE, 1, 64, FAKE, None, None, 4, 10, 8, FAKE, 1, None) == -1       # offsets NULL
+    assert sc(FAKE, 1, 12, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None) == -2       # row_elems % 8
     assert lib.moe_unpermute(FAKE, 2, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
     assert lib.moe_unpermute(FAKE, 1, FAKE, None, 4, 8, 60, FAKE, 1, None) == -2
     assert lib.moe_unpermute(None, 1, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
