@@ -22,8 +22,10 @@ technical report:
 The pages name NVFP4 but never define it.  The definition used here is the
 library's own: 1x16 blocks along K, an E4M3 (OCP E4M3FN) block scale derived
 from each block's amax, one FP32 global (decode) scale per tensor, and E2M1
-codes rounded to nearest, ties to even.  Every further reading is listed in
-DESIGN.md.
+codes rounded to nearest, ties to even.  Every further reading where the
+pages are silent (op order of the block scale, sign of zero, nibble order,
+permutation order, accumulation order of the combine) is stated in the
+docstring of the function that takes it.
 
 Modules:
   nvfp4   -- scalar codecs, quantize, dequantize           (fp32 as defined)
