@@ -35,7 +35,7 @@ inline int dtype_bytes(int dt) {
 // keep every CU busy without a huge tail.
 constexpr int kStreamBlocks = 256 * 8;
 
-// Grid limit of the one-pass streaming kernels (quantize, gather-quantize,
+// Grid limit of the one-pass streaming kernels (quantize, quantize-scatter,
 // combine, SiLU backward): they launch one thread (or one workgroup) per
 // unit of work and keep a grid-stride loop only for inputs beyond this many
 // workgroups of 256 threads (2^28 work-items, below the dispatch's 2^32).

@@ -1,6 +1,6 @@
 // NVFP4 encoding of one 1x16 block: global scale, E4M3 block scale and
 // E2M1 codes (device functions shared by the quantizer and the fused
-// gather-quantize of the permutation).
+// quantize-scatter of the permutation).
 //
 // Steps (per block with amax a, global scale g): t = a/6, u = t/g,
 // S = E4M3_RNE_satfinite(u), d = decode(S) * g, code = sign(x) |
