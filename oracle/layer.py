@@ -5,22 +5,31 @@ Dataflow ("miniTE報告、NVFP4強化学習の安定性を検証", first and fou
 paragraphs: token-wise NVFP4 forward over a contiguous permuted layout with
 amax reuse; BF16 backward):
 
-  forward   X --permute--> X_perm --quantize(amax_X)--> A1
-            Y1 = A1 . Wgu_e^T          (grouped W4A4, gate rows then up rows)
-            H  = silu(G) * U           (amax_H taken from H as stored)
-            A2 = quantize(H, amax_H);  Y2 = A2 . Wdn_e^T
-            out[t] = sum_j w[t, j] * Y2[dest[t*k + j]]
-  backward  dY2[p] = w[src[p]] * dY[src[p] // k]
-            dH = dY2 . Wdn_e;  dWdn_e = dY2_e^T . H_e
-            dY1 = silu-gate backward;  dX_perm = dY1 . Wgu_e;  dWgu_e = dY1_e^T . X_perm_e
-            dX[t] = sum_j dX_perm[dest[t*k + j]]
+  forward   x_perm = X[src // k]                   (permute)
+            a1 = quantize(x_perm, amax_x)          (amax_x = max|X|)
+            y1 = a1 . Wgu_e^T                      (grouped W4A4, gate rows then up rows)
+            h  = silu(G) * U                       (amax_h = max|h| as stored)
+            a2 = quantize(h, amax_h)
+            y2 = a2 . Wdn_e^T
+            out[t] = sum_j w[t, j] * y2[dest[t*k + j]]
+  backward  dy2[p] = w[src[p]] * dY[src[p] // k]
+            dh = dy2 . Wdn_e                 dw_dn_e = dy2_e^T . h_e
+            dy1 = silu-gate backward(y1, dh)
+            dx_perm = dy1 . Wgu_e            dw_gu_e = dy1_e^T . x_perm_e
+            dX[t] = sum_j dx_perm[dest[t*k + j]]
 
-Where the GPU path stores a tensor as bf16 the composition rounds it to
-bf16 too (round to nearest even), so that quantization downstream sees the
-same kind of values; every product itself is fp64.  Parity tests compare the
-GPU stage by stage, feeding the GPU's own stored intermediates into the next
-oracle stage, because a requantized tensor's codes may flip at rounding
-boundaries.
+Each stage is one function of the stored tensors it reads
+(``forward_stage`` / ``backward_stage``), and ``forward`` / ``backward`` run
+the stages in order, each reading what the previous ones stored.  The GPU
+parity tests call the same stage functions with the GPU's own stored
+tensors, so the wiring -- which tensor feeds which product, where the
+routing weight enters -- is written once, here, and is the wiring the pins
+in ``tests/test_oracle_layer.py`` hold to an independent per-token loop and
+to automatic differentiation.
+
+Where the GPU path stores a tensor as bf16 the chain rounds it to bf16 too
+(round to nearest even), so that quantization downstream sees the same kind
+of values; every product itself is fp64.
 """
 
 import numpy as np
@@ -44,39 +53,147 @@ def quantize_weights(w):
     return q.reshape(E, N, K // 2), s.reshape(E, N, K // 16), g, amax
 
 
+FORWARD_STAGES = ("x_perm", "a1", "y1", "h", "a2", "y2", "out")
+BACKWARD_STAGES = ("dy2", "dh", "dw_dn", "dy1", "dx_perm", "dw_gu", "dx")
+# stages whose stored form is bf16 (the chain rounds them)
+_BF16_STORED = {"y1", "h", "y2", "out", "dy2", "dh", "dy1", "dx_perm", "dx"}
+
+
+def _row_experts(offsets, rows, n):
+    off = np.asarray(offsets, dtype=np.int64)
+    r = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    return np.searchsorted(off, r, side="right") - 1
+
+
+def _rowwise_w4a4(a, b, offsets, rows):
+    """Rows of a grouped W4A4 product; ``a`` holds only the listed rows
+    when ``rows`` is given."""
+    aq, as_, ag = a
+    if rows is None:
+        return gemm.grouped_gemm_w4a4(aq, as_, ag, b[0], b[1], b[2], offsets)
+    ex = _row_experts(offsets, rows, len(rows))
+    # each listed row is its own one-row group of its expert
+    E = len(offsets) - 1
+    N = b[0].shape[1]
+    C = np.zeros((len(rows), N))
+    AB = np.zeros((len(rows), N))
+    for e in np.unique(ex):
+        if e < 0 or e >= E:
+            continue
+        sel = np.nonzero(ex == e)[0]
+        c, ab = gemm.grouped_gemm_w4a4(aq[sel], as_[sel], ag, b[0][e:e + 1], b[1][e:e + 1],
+                                       np.asarray(b[2]).reshape(E)[e:e + 1], [0, sel.size])
+        C[sel], AB[sel] = c, ab
+    return C, AB
+
+
+def _rowwise_bf16_nn(a, w, offsets, rows):
+    """Rows of the grouped BF16 NN product a . W_e (``a`` restricted to
+    ``rows`` when given)."""
+    if rows is None:
+        return gemm.grouped_gemm_bf16("NN", a, w, offsets)
+    ex = _row_experts(offsets, rows, len(rows))
+    C = np.zeros((len(rows), w.shape[2]))
+    AB = np.zeros_like(C)
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        c, ab = gemm.grouped_gemm_bf16("NN", a[sel], w[e:e + 1], [0, sel.size])
+        C[sel], AB[sel] = c, ab
+    return C, AB
+
+
+def forward_stage(name, s, x, topk_w, wq_gu, wq_dn, offsets, dest, src, rows=None):
+    """One forward stage computed from the stored tensors in ``s``.
+
+    ``s`` maps stage names (and "amax_x", "amax_h") to stored values.  With
+    ``rows`` (permuted-row indices) the row-wise stages read and return only
+    those rows: every row-wise entry of ``s`` is then already restricted to
+    ``rows``.  Returns (value, bound): bound is sum|a*b| per element for the
+    GEMMs and the combine, None elsewhere; quantize stages return the
+    (q, scales, g) triple.
+    """
+    k = np.asarray(topk_w).shape[1]
+    if name == "x_perm":                       # contiguous per-expert layout
+        sr = src if rows is None else np.asarray(src)[rows]
+        return moe.gather_rows(x, sr, k), None
+    if name == "a1":                           # amax reuse: max|X| of the unpermuted tokens
+        q, sc, g, _ = nvfp4.quantize(s["x_perm"], amax=[s["amax_x"]])
+        return (q, sc, g), None
+    if name == "y1":
+        return _rowwise_w4a4(s["a1"], wq_gu, offsets, rows)
+    if name == "h":
+        return moe.silu_gate_fwd(s["y1"]), None
+    if name == "a2":
+        q, sc, g, _ = nvfp4.quantize(s["h"], amax=[s["amax_h"]])
+        return (q, sc, g), None
+    if name == "y2":
+        return _rowwise_w4a4(s["a2"], wq_dn, offsets, rows)
+    if name == "out":                          # dest indexes the stored y2 rows
+        return moe.unpermute(s["y2"], dest, k, topk_w), moe.unpermute_absbound(s["y2"], dest, k, topk_w)
+    raise ValueError(name)
+
+
+def backward_stage(name, s, dy, topk_w, w_gu, w_dn, offsets, dest, src, rows=None):
+    """One stage of the BF16 backward computed from the stored tensors in
+    ``s`` (the forward's x_perm, y1, h and the backward's own dy2, dh, dy1,
+    dx_perm).  ``rows`` as in ``forward_stage`` (row-wise stages only; the
+    weight gradients reduce over every row of ``s``, grouped by
+    ``offsets``).  Returns (value, bound) like ``forward_stage``.
+    """
+    k = np.asarray(topk_w).shape[1]
+    if name == "dy2":      # backward of the weighted combine: the weight enters here, once
+        sr = src if rows is None else np.asarray(src)[rows]
+        return moe.gather_rows(dy, sr, k, topk_w), None
+    if name == "dh":       # backward of y2 = h . Wdn_e^T w.r.t. h
+        return _rowwise_bf16_nn(s["dy2"], w_dn, offsets, rows)
+    if name == "dw_dn":    # ... w.r.t. Wdn_e: reduction over the expert's rows
+        return gemm.grouped_gemm_bf16("TN", s["dy2"], s["h"], offsets)
+    if name == "dy1":
+        return moe.silu_gate_bwd(s["y1"], s["dh"]), None
+    if name == "dx_perm":  # backward of y1 = x_perm . Wgu_e^T w.r.t. x_perm
+        return _rowwise_bf16_nn(s["dy1"], w_gu, offsets, rows)
+    if name == "dw_gu":
+        return gemm.grouped_gemm_bf16("TN", s["dy1"], s["x_perm"], offsets)
+    if name == "dx":       # backward of the permutation: unweighted sum of a token's rows
+        return moe.unpermute(s["dx_perm"], dest, k, None), moe.unpermute_absbound(s["dx_perm"], dest, k, None)
+    raise ValueError(name)
+
+
+def _store(name, value):
+    """The stored (GPU-side) form of a stage's value."""
+    if name in _BF16_STORED:
+        return bf16_round(value)
+    if name in ("dw_dn", "dw_gu"):
+        return np.asarray(value, np.float32)
+    if name == "x_perm":
+        return np.asarray(value, np.float32)
+    return value
+
+
 def forward(x, topk_ids, topk_w, w_gu, w_dn, wq_gu=None, wq_dn=None):
     """MoE layer forward.  x [T, D] (bf16 values as float32), topk_ids /
     topk_w [T, k], w_gu [E, 2F, D], w_dn [E, D, F] (bf16 values).
-    Returns a dict with every intermediate."""
-    T, k = topk_ids.shape
+    Returns a dict with every stored intermediate and the routing metadata."""
     E = w_gu.shape[0]
     off, dest, src = moe.permute_metadata(topk_ids, E)
-    x_perm = moe.gather_rows(x, src, k).astype(np.float32)
-    amax_x = np.float32(np.abs(np.asarray(x, np.float32)).max()) if x.size else np.float32(0)
-    a1 = nvfp4.quantize(x_perm, amax=[amax_x])
-    b1 = wq_gu if wq_gu is not None else quantize_weights(w_gu)
-    y1_64, _ = gemm.grouped_gemm_w4a4(a1[0], a1[1], a1[2], b1[0], b1[1], b1[2], off)
-    y1 = bf16_round(y1_64)
-    h = bf16_round(moe.silu_gate_fwd(y1))
-    amax_h = np.float32(np.abs(h).max()) if h.size else np.float32(0)
-    a2 = nvfp4.quantize(h, amax=[amax_h])
-    b2 = wq_dn if wq_dn is not None else quantize_weights(w_dn)
-    y2_64, _ = gemm.grouped_gemm_w4a4(a2[0], a2[1], a2[2], b2[0], b2[1], b2[2], off)
-    y2 = bf16_round(y2_64)
-    out = bf16_round(moe.unpermute(y2, dest, k, topk_w))
-    return dict(offsets=off, dest=dest, src=src, x_perm=x_perm, amax_x=amax_x,
-                a1=a1, y1=y1, h=h, amax_h=amax_h, a2=a2, y2=y2, out=out)
+    wq_gu = wq_gu if wq_gu is not None else quantize_weights(w_gu)
+    wq_dn = wq_dn if wq_dn is not None else quantize_weights(w_dn)
+    s = dict(offsets=off, dest=dest, src=src,
+             amax_x=np.float32(np.abs(np.asarray(x, np.float32)).max()) if x.size else np.float32(0))
+    for name in FORWARD_STAGES:
+        v, _ = forward_stage(name, s, x, topk_w, wq_gu, wq_dn, off, dest, src)
+        s[name] = _store(name, v)
+        if name == "h":
+            s["amax_h"] = np.float32(np.abs(s["h"]).max()) if s["h"].size else np.float32(0)
+    return s
 
 
 def backward(fwd, dy, topk_w, w_gu, w_dn):
-    """BF16 backward of ``forward`` given the upstream gradient dy [T, D]."""
-    k = topk_w.shape[1]
+    """BF16 backward of ``forward`` given the upstream gradient dy [T, D];
+    weight gradients in fp32, activation gradients rounded to bf16."""
     off, dest, src = fwd["offsets"], fwd["dest"], fwd["src"]
-    dy2 = bf16_round(moe.gather_rows(dy, src, k, topk_w))
-    dh = bf16_round(gemm.grouped_gemm_bf16("NN", dy2, w_dn, off)[0])
-    dw_dn = gemm.grouped_gemm_bf16("TN", dy2, fwd["h"], off)[0].astype(np.float32)
-    dy1 = bf16_round(moe.silu_gate_bwd(fwd["y1"], dh))
-    dx_perm = bf16_round(gemm.grouped_gemm_bf16("NN", dy1, w_gu, off)[0])
-    dw_gu = gemm.grouped_gemm_bf16("TN", dy1, fwd["x_perm"], off)[0].astype(np.float32)
-    dx = bf16_round(moe.unpermute(dx_perm, dest, k, None))
-    return dict(dy2=dy2, dh=dh, dw_dn=dw_dn, dy1=dy1, dx_perm=dx_perm, dw_gu=dw_gu, dx=dx)
+    s = {n: fwd[n] for n in ("x_perm", "y1", "h")}
+    for name in BACKWARD_STAGES:
+        v, _ = backward_stage(name, s, dy, topk_w, w_gu, w_dn, off, dest, src)
+        s[name] = _store(name, v)
+    return {n: s[n] for n in BACKWARD_STAGES}

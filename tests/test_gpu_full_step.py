@@ -5,8 +5,10 @@ buffers).  Every stage is checked against the oracle fed with the GPU's own
 stored input of that stage, on what the oracle can afford at this size:
 the whole routing metadata, and for four experts (the first, the largest,
 the last and a seeded one) the first and last row of every 256-row tile plus
-seeded rows; two experts' weight gradients on seeded elements; seeded
-tokens of the two combines.  Integer outputs are compared bit for bit,
+seeded rows; the full weight gradients of two experts; seeded tokens of the
+two combines.  The reference of each stage is the oracle's own stage
+function (oracle.layer.forward_stage / backward_stage), whose wiring the CPU
+tests pin.  Integer outputs are compared bit for bit,
 GEMMs within |C - C_ref| <= 1e-3 * sum|a*b| (+ bf16 output rounding)."""
 
 import numpy as np
@@ -15,7 +17,7 @@ import torch
 
 import workloads
 from _helpers import assert_bf16_close, assert_gemm_close, gpu, require_gpu, to_gpu, to_np
-from oracle import gemm, moe, nvfp4
+from oracle import gemm, layer, moe, nvfp4
 from oracle.layer import bf16_round
 
 pytestmark = gpu
@@ -70,79 +72,77 @@ def test_metadata_and_fused_permute_quantize(step):
     assert to_np(buf.a1_g)[0] == g[0]
 
 
+def _stage_args(step):
+    d, meta = step["d"], step["meta"]
+    return step["off"], to_np(meta["dest"]), to_np(meta["src"])
+
+
 def test_gate_up_silu_requantize_down_combine(step):
-    d, meta, buf, rows, off = step["d"], step["meta"], step["buf"], step["rows"], step["off"]
+    """Forward stages on sampled rows, each from the oracle's stage function
+    (oracle.layer's wiring) fed the GPU's stored rows."""
+    d, meta, buf, rows = step["d"], step["meta"], step["buf"], step["rows"]
+    off, dest, src = _stage_args(step)
     wq_gu, wq_dn = step["wq_gu"], step["wq_dn"]
     wg = (to_np(wq_gu["q"]), to_np(wq_gu["s"]), to_np(wq_gu["g"]))
     wd = (to_np(wq_dn["q"]), to_np(wq_dn["s"]), to_np(wq_dn["g"]))
-    a1 = (to_np(buf.a1_q), to_np(buf.a1_s), to_np(buf.a1_g))
-    y1_ref, ab1 = gemm.grouped_gemm_w4a4(*a1, *wg, off, rows=rows)
-    y1 = _rows(buf.y1, rows)
-    assert_gemm_close(y1, y1_ref, ab1, bf16_out=True, what="gate+up (fused epilogue)")
-    h = _rows(buf.h, rows)
-    assert_bf16_close(h, moe.silu_gate_fwd(y1), what="fused SiLU gate")
     amax = to_np(buf.amax)
+    g = dict(a1=(_rows(buf.a1_q, rows), _rows(buf.a1_s, rows), to_np(buf.a1_g)), y1=_rows(buf.y1, rows),
+             h=_rows(buf.h, rows), a2=(_rows(buf.a2_q, rows), _rows(buf.a2_s, rows), to_np(buf.a2_g)),
+             amax_x=amax[0], amax_h=amax[1])
+    fs = lambda n, s=g, r=rows, dst=dest, tw=d["topk_w"]: layer.forward_stage(  # noqa: E731
+        n, s, d["x"], tw, wg, wd, off, dst, src, rows=r)
+    ref, ab = fs("y1")
+    assert_gemm_close(g["y1"], ref, ab, bf16_out=True, what="gate+up (fused epilogue)")
+    assert_bf16_close(g["h"], fs("h")[0], what="fused SiLU gate")
     assert amax[1] == np.abs(to_np(buf.h)).max()
-    q2, s2, g2, _ = nvfp4.quantize(h, amax=[amax[1]])
-    np.testing.assert_array_equal(_rows(buf.a2_q, rows), q2)
-    np.testing.assert_array_equal(_rows(buf.a2_s, rows), s2)
-    a2 = (to_np(buf.a2_q), to_np(buf.a2_s), to_np(buf.a2_g))
-    y2_ref, ab2 = gemm.grouped_gemm_w4a4(*a2, *wd, off, rows=rows)
-    assert_gemm_close(_rows(buf.y2, rows), y2_ref, ab2, bf16_out=True, what="down")
+    q2, s2, g2 = layer.forward_stage("a2", g, None, d["topk_w"], wg, wd, off, dest, src)[0]
+    np.testing.assert_array_equal(g["a2"][0], q2)
+    np.testing.assert_array_equal(g["a2"][1], s2)
+    assert to_np(buf.a2_g)[0] == g2[0]
+    ref, ab = fs("y2")
+    assert_gemm_close(_rows(buf.y2, rows), ref, ab, bf16_out=True, what="down")
     # combine: seeded tokens, from the GPU's own Y2 rows
     k = d["k"]
-    dest = to_np(meta["dest"])
     toks = np.sort(step["rng"].choice(d["T"], 32, replace=False))
     sub = dest.reshape(-1, k)[toks].reshape(-1)
-    y2s = _rows(buf.y2, sub)
     local = np.arange(sub.size, dtype=np.int64)
-    ref = moe.unpermute(y2s, local, k, d["topk_w"][toks])
-    bound = moe.unpermute_absbound(y2s, local, k, d["topk_w"][toks])
+    ref, bound = fs("out", s=dict(y2=_rows(buf.y2, sub)), r=None, dst=local, tw=d["topk_w"][toks])
     assert_bf16_close(_rows(buf.out, toks), ref, scale=bound, what="combine")
 
 
 def test_backward(step):
-    d, meta, buf, rows, off = step["d"], step["meta"], step["buf"], step["rows"], step["off"]
-    k, F = d["k"], d["F"]
-    src = to_np(meta["src"])
-    dy2 = _rows(buf.dy2, rows)
-    assert_bf16_close(dy2, moe.gather_rows(d["dy"], src[rows], k, d["topk_w"]), what="dY2")
-    expert_of = np.searchsorted(off, rows, side="right") - 1
-    dh = _rows(buf.dh, rows)
-    for i, (r, e) in enumerate(zip(rows, expert_of)):
-        ref, ab = gemm.grouped_gemm_bf16("NN", dy2[i:i + 1], d["w_dn"][e:e + 1], [0, 1])
-        assert_gemm_close(dh[i:i + 1], ref, ab, bf16_out=True, what="dH row %d" % r)
-    y1 = _rows(buf.y1, rows)
-    dy1 = _rows(buf.dy1, rows)
-    dy1_ref = moe.silu_gate_bwd(y1, dh)
-    scale = np.abs(dy1_ref) + 1e-3 * np.abs(np.concatenate([dh, dh], axis=1)) * (np.abs(y1) + 1)
-    assert_bf16_close(dy1, dy1_ref, scale=scale, what="dY1")
-    dxp = _rows(buf.dx_perm, rows)
-    for i, (r, e) in enumerate(zip(rows, expert_of)):
-        ref, ab = gemm.grouped_gemm_bf16("NN", dy1[i:i + 1], d["w_gu"][e:e + 1], [0, 1])
-        assert_gemm_close(dxp[i:i + 1], ref, ab, bf16_out=True, what="dX_perm row %d" % r)
-    # weight gradients of two experts, seeded elements, over all their rows
-    rng = step["rng"]
+    """Backward stages on sampled rows, two experts' full weight gradients
+    and seeded tokens of the dX combine, each from the oracle's stage
+    function fed the GPU's stored inputs."""
+    d, meta, buf, rows = step["d"], step["meta"], step["buf"], step["rows"]
+    off, dest, src = _stage_args(step)
+    k = d["k"]
+    g = dict(dy2=_rows(buf.dy2, rows), dh=_rows(buf.dh, rows), y1=_rows(buf.y1, rows), dy1=_rows(buf.dy1, rows))
+    bs = lambda n, s=g, r=rows, o=off, dst=dest, tw=d["topk_w"]: layer.backward_stage(  # noqa: E731
+        n, s, d["dy"], tw, d["w_gu"], d["w_dn"], o, dst, src, rows=r)
+    assert_bf16_close(g["dy2"], bs("dy2")[0], what="dY2")
+    ref, ab = bs("dh")
+    assert_gemm_close(g["dh"], ref, ab, bf16_out=True, what="dH")
+    dy1_ref, _ = bs("dy1")
+    scale = np.abs(dy1_ref) + 1e-3 * np.abs(np.concatenate([g["dh"], g["dh"]], axis=1)) * (np.abs(g["y1"]) + 1)
+    assert_bf16_close(g["dy1"], dy1_ref, scale=scale, what="dY1")
+    ref, ab = bs("dx_perm")
+    assert_gemm_close(_rows(buf.dx_perm, rows), ref, ab, bf16_out=True, what="dX_perm")
+    # weight gradients of two experts in full, over all their rows
     for e in (step["experts"][0], step["experts"][-1]):
         lo, hi = int(off[e]), int(off[e + 1])
         er = np.arange(lo, hi, dtype=np.int64)
-        dy2_e, h_e = _rows(buf.dy2, er), _rows(buf.h, er)
-        dy1_e, xp_e = _rows(buf.dy1, er), d["x"][to_np(meta["src"])[er] // d["k"]]
-        for name, a, b, dw in (("dW_dn", dy2_e, h_e, buf.dw_dn), ("dW_gu", dy1_e, xp_e, buf.dw_gu)):
-            ii = rng.integers(0, a.shape[1], 64)
-            jj = rng.integers(0, b.shape[1], 64)
-            ref = np.einsum("ri,ri->i", a[:, ii].astype(np.float64), b[:, jj].astype(np.float64))
-            ab = np.einsum("ri,ri->i", np.abs(a[:, ii]).astype(np.float64), np.abs(b[:, jj]).astype(np.float64))
-            got = to_np(dw[e])[ii, jj]
-            assert_gemm_close(got, ref, ab, what="%s expert %d" % (name, e))
+        se = dict(dy2=_rows(buf.dy2, er), h=_rows(buf.h, er), dy1=_rows(buf.dy1, er), x_perm=_rows(buf.x_perm, er))
+        one = np.array([0, hi - lo], dtype=np.int64)
+        for name, dw in (("dw_dn", buf.dw_dn), ("dw_gu", buf.dw_gu)):
+            ref, ab = layer.backward_stage(name, se, d["dy"], d["topk_w"], d["w_gu"][e:e + 1],
+                                           d["w_dn"][e:e + 1], one, dest, src)
+            assert_gemm_close(to_np(dw[e]), ref[0], ab[0], what="%s expert %d" % (name, e))
     # dX combine: seeded tokens, from the GPU's own dX_perm rows
-    dest = to_np(meta["dest"])
-    toks = np.sort(rng.choice(d["T"], 32, replace=False))
+    toks = np.sort(step["rng"].choice(d["T"], 32, replace=False))
     sub = dest.reshape(-1, k)[toks].reshape(-1)
-    dxs = _rows(buf.dx_perm, sub)
     local = np.arange(sub.size, dtype=np.int64)
-    ref = moe.unpermute(dxs, local, k, None)
-    bound = moe.unpermute_absbound(dxs, local, k, None)
+    ref, bound = bs("dx", s=dict(dx_perm=_rows(buf.dx_perm, sub)), r=None, dst=local, tw=d["topk_w"][toks])
     assert_bf16_close(_rows(buf.dx, toks), ref, scale=bound, what="dX")
 
 

@@ -8,7 +8,7 @@ import torch
 
 import workloads
 from _helpers import assert_bf16_close, assert_gemm_close, gpu, require_gpu, to_gpu, to_np
-from oracle import gemm, moe, nvfp4
+from oracle import layer, moe
 from oracle.layer import quantize_weights
 
 pytestmark = gpu
@@ -31,63 +31,52 @@ def _run(T, k, E, D, F, s=1.1, seed=0):
 
 @pytest.mark.parametrize("T,k,E,D,F", [(256, 8, 16, 256, 128), (100, 2, 5, 128, 192)])
 def test_layer_stagewise(T, k, E, D, F):
+    """Every stage against the oracle's own stage function (the wiring of
+    oracle.layer, pinned on the CPU), fed the GPU's stored inputs."""
     require_gpu()
     d, meta, buf, wq_gu, wq_dn = _run(T, k, E, D, F)
     off, dest, src = moe.permute_metadata(d["topk_ids"], E)
     np.testing.assert_array_equal(to_np(meta["offsets"]), off)
     np.testing.assert_array_equal(to_np(meta["dest"]), dest)
-    # permute + amax + quantize (bit-exact)
-    xp = to_np(buf.x_perm)
-    np.testing.assert_array_equal(xp, d["x"][src // k])
+    np.testing.assert_array_equal(to_np(meta["src"]), src)
     amax = to_np(buf.amax)
     assert amax[0] == np.abs(d["x"]).max()
-    a1 = nvfp4.quantize(xp, amax=[amax[0]])
-    np.testing.assert_array_equal(to_np(buf.a1_q), a1[0])
-    np.testing.assert_array_equal(to_np(buf.a1_s), a1[1])
     wg = quantize_weights(d["w_gu"])
     wd = quantize_weights(d["w_dn"])
     for gpu_w, ref_w in ((wq_gu, wg), (wq_dn, wd)):
         np.testing.assert_array_equal(to_np(gpu_w["q"]), ref_w[0])
         np.testing.assert_array_equal(to_np(gpu_w["s"]), ref_w[1])
         np.testing.assert_array_equal(to_np(gpu_w["g"]), ref_w[2])
-    # GEMM1
-    y1_ref, ab1 = gemm.grouped_gemm_w4a4(a1[0], a1[1], a1[2], wg[0], wg[1], wg[2], off)
-    y1 = to_np(buf.y1)
-    assert_gemm_close(y1, y1_ref, ab1, bf16_out=True, what="gate+up")
-    # SiLU gate + amax of H
-    h = to_np(buf.h)
-    assert_bf16_close(h, moe.silu_gate_fwd(y1), what="silu gate")
-    assert amax[1] == np.abs(h).max()
-    # requantize H with the reused amax (bit-exact), GEMM2
-    a2 = nvfp4.quantize(h, amax=[amax[1]])
-    np.testing.assert_array_equal(to_np(buf.a2_q), a2[0])
-    np.testing.assert_array_equal(to_np(buf.a2_s), a2[1])
-    y2_ref, ab2 = gemm.grouped_gemm_w4a4(a2[0], a2[1], a2[2], wd[0], wd[1], wd[2], off)
-    y2 = to_np(buf.y2)
-    assert_gemm_close(y2, y2_ref, ab2, bf16_out=True, what="down")
-    # unpermute-combine
-    out_ref = moe.unpermute(y2, dest, k, d["topk_w"])
-    assert_bf16_close(to_np(buf.out), out_ref, scale=moe.unpermute_absbound(y2, dest, k, d["topk_w"]),
-                      what="combine")
+    # the GPU's stored tensors, by stage name
+    g = dict(x_perm=to_np(buf.x_perm), a1=(to_np(buf.a1_q), to_np(buf.a1_s), to_np(buf.a1_g)),
+             y1=to_np(buf.y1), h=to_np(buf.h), a2=(to_np(buf.a2_q), to_np(buf.a2_s), to_np(buf.a2_g)),
+             y2=to_np(buf.y2), out=to_np(buf.out), amax_x=amax[0], amax_h=amax[1],
+             dy2=to_np(buf.dy2), dh=to_np(buf.dh), dw_dn=to_np(buf.dw_dn), dy1=to_np(buf.dy1),
+             dx_perm=to_np(buf.dx_perm), dw_gu=to_np(buf.dw_gu), dx=to_np(buf.dx))
+    assert g["amax_h"] == np.abs(g["h"]).max()
+    fs = lambda n: layer.forward_stage(n, g, d["x"], d["topk_w"], wg, wd, off, dest, src)  # noqa: E731
+    bs = lambda n: layer.backward_stage(n, g, d["dy"], d["topk_w"], d["w_gu"], d["w_dn"], off, dest, src)  # noqa: E731
+    np.testing.assert_array_equal(g["x_perm"], fs("x_perm")[0])
+    for name in ("a1", "a2"):      # quantize with the reused amax: bit-exact
+        ref, _ = fs(name)
+        for got, want in zip(g[name], ref):
+            np.testing.assert_array_equal(got, want, err_msg=name)
+    for name in ("y1", "y2"):
+        ref, ab = fs(name)
+        assert_gemm_close(g[name], ref, ab, bf16_out=True, what=name)
+    assert_bf16_close(g["h"], fs("h")[0], what="silu gate")
+    ref, bound = fs("out")
+    assert_bf16_close(g["out"], ref, scale=bound, what="combine")
     # backward
-    dy2 = to_np(buf.dy2)
-    assert_bf16_close(dy2, moe.gather_rows(d["dy"], src, k, d["topk_w"]), what="dY2")
-    dh_ref, abh = gemm.grouped_gemm_bf16("NN", dy2, d["w_dn"], off)
-    dh = to_np(buf.dh)
-    assert_gemm_close(dh, dh_ref, abh, bf16_out=True, what="dH")
-    dwd_ref, abwd = gemm.grouped_gemm_bf16("TN", dy2, h, off)
-    assert_gemm_close(to_np(buf.dw_dn), dwd_ref, abwd, what="dW_dn")
-    dy1 = to_np(buf.dy1)
-    dy1_ref = moe.silu_gate_bwd(y1, dh)
-    scale = np.abs(dy1_ref) + 1e-3 * np.abs(np.concatenate([dh, dh], axis=1)) * (np.abs(y1) + 1)
-    assert_bf16_close(dy1, dy1_ref, scale=scale, what="dY1")
-    dxp_ref, abx = gemm.grouped_gemm_bf16("NN", dy1, d["w_gu"], off)
-    dxp = to_np(buf.dx_perm)
-    assert_gemm_close(dxp, dxp_ref, abx, bf16_out=True, what="dX_perm")
-    dwg_ref, abwg = gemm.grouped_gemm_bf16("TN", dy1, xp, off)
-    assert_gemm_close(to_np(buf.dw_gu), dwg_ref, abwg, what="dW_gu")
-    dx_ref = moe.unpermute(dxp, dest, k, None)
-    assert_bf16_close(to_np(buf.dx), dx_ref, scale=moe.unpermute_absbound(dxp, dest, k, None), what="dX")
+    assert_bf16_close(g["dy2"], bs("dy2")[0], what="dY2")
+    for name, bf in (("dh", True), ("dw_dn", False), ("dx_perm", True), ("dw_gu", False)):
+        ref, ab = bs(name)
+        assert_gemm_close(g[name], ref, ab, bf16_out=bf, what=name)
+    dy1_ref, _ = bs("dy1")
+    scale = np.abs(dy1_ref) + 1e-3 * np.abs(np.concatenate([g["dh"], g["dh"]], axis=1)) * (np.abs(g["y1"]) + 1)
+    assert_bf16_close(g["dy1"], dy1_ref, scale=scale, what="dY1")
+    ref, bound = bs("dx")
+    assert_bf16_close(g["dx"], ref, scale=bound, what="dX")
 
 
 def test_backward_with_wgrad_stream_matches_serial():
