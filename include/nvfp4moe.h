@@ -149,15 +149,17 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int k, int E, const void* x,
  * gathered rows (token-wise path with contiguous layout, device-side
  * metadata, amax reuse and op fusion: [JA], fourth paragraph).  Computes the
  * same offsets/dest/src as moe_permute, optionally the bf16 rows x_perm, and
- * q/scales/gscale equal to nvfp4_quantize(x_perm, groups = 1, amax) --
- * bit for bit -- without reading x_perm back: each row of x is encoded once
- * and its codes and scales (and bf16 copy) are written to its k permuted
- * rows.
+ * q/scales/gscale equal to nvfp4_quantize(x_perm, groups = 1, amax_in =
+ * amax) -- bit for bit -- without reading x_perm back: each row of x is
+ * encoded once and its codes and scales (and bf16 copy) are written to its
+ * k permuted rows.
  *   x        [T][D] bf16, 16-byte aligned; D % 16 == 0.
  *   x_perm   [T*k][D] bf16 out, or NULL when only the NVFP4 rows are needed.
- *   amax_in  fp32 [1] or NULL.  When NULL, max |x| over the T rows of x
- *            (equal to that of x_perm: every token is routed) is computed
- *            first and written to amax_out (then non-NULL).
+ *   amax_in  fp32 [1] or NULL.  When NULL, amax = max |x| over all T rows of
+ *            x is computed first and written to amax_out (then non-NULL).
+ *            With every id valid it equals max |x_perm| (each token is
+ *            routed); a token whose ids are all invalid has no permuted row
+ *            but still counts (0 when D == 0).
  *   q        [T*k][D/2], scales [T*k][D/16], gscale [1] out (see
  *            nvfp4_quantize).  Rows past offsets[E] (invalid ids) are zeros.
  *   offsets, dest, src, workspace, status: as for moe_permute.

@@ -733,10 +733,14 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
     }
     fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
   } else {
-    // The activation amax is taken once, over the T unpermuted rows, by the
-    // histogram launch (in parts) and the scan (their max).
+    // The activation amax is taken once, over the T unpermuted rows of x
+    // (tokens whose ids are all invalid included), by the histogram launch
+    // (in parts) and the scan (their max).  Rows of no elements have no
+    // parts to reduce: the amax is then 0, written here.
+    const bool fused_amax = !amax_in && D > 0;
+    if (!amax_in && D == 0) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
     const int rc = launch_metadata(topk_ids, R, E, nullptr, workspace, offsets, dest, src, status, st,
-                                   amax_in ? nullptr : x, T * D * 2 / 16, amax_in ? nullptr : amax_out);
+                                   fused_amax ? x : nullptr, T * D * 2 / 16, fused_amax ? amax_out : nullptr);
     if (rc != NVFP4MOE_OK) return rc;
   }
   // Launched even without rows: it also writes the global scale.

@@ -351,3 +351,36 @@ def test_permute_nvfp4_zero_tokens():
     torch.cuda.synchronize()
     assert (to_np(r["offsets"]) == 0).all()
     assert to_np(r["amax"])[0] == 0.0 and to_np(r["gscale"])[0] == 1.0
+
+
+def test_permute_nvfp4_amax_counts_unrouted_token():
+    """A token whose ids are all invalid has no permuted row, yet the
+    computed amax is over every row of x (the header's contract), and the
+    codes are those of the oracle's quantize of the routed rows with that
+    amax.  With D == 0 the computed amax is 0."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(31)
+    T, k, E, D = 40, 3, 6, 64
+    x = workloads._bf16(rng.standard_normal((T, D)).astype(np.float32))
+    x[7, 5] = 96.0                       # the largest |x| sits in the unrouted token
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[7] = [E, -1, E + 4]
+    amax_out = torch.full((1,), 1e30, dtype=torch.float32, device="cuda")
+    r = ops.moe_permute_nvfp4(to_gpu(ids, torch.int32), E, to_gpu(x, torch.bfloat16), amax_out=amax_out)
+    torch.cuda.synchronize()
+    assert to_np(amax_out)[0] == np.float32(96.0)
+    off = to_np(r["offsets"])
+    R_valid = int(off[-1])
+    assert R_valid == T * k - k
+    src = to_np(r["src"])[:R_valid]
+    q, s, g, _ = nvfp4.quantize(x[src // k], amax=[np.float32(96.0)])
+    np.testing.assert_array_equal(to_np(r["q"])[:R_valid], q)
+    np.testing.assert_array_equal(to_np(r["scales"])[:R_valid], s)
+    assert to_np(r["gscale"])[0] == g[0]
+    # no elements per row: the amax is cleared, the global scale is 1
+    amax_out.fill_(5.0)
+    x0 = torch.zeros((T, 0), dtype=torch.bfloat16, device="cuda")
+    r0 = ops.moe_permute_nvfp4(to_gpu(ids, torch.int32), E, x0, amax_out=amax_out, want_x_perm=False)
+    torch.cuda.synchronize()
+    assert to_np(amax_out)[0] == 0.0 and to_np(r0["gscale"])[0] == 1.0
