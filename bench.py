@@ -206,6 +206,7 @@ def cpu_baseline():
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
+    host_cpus = os.cpu_count()
     T, k, E, D, F = 4096, 8, 64, 2048, 768
     d = workloads.moe(T, 0.0, with_dy=True, E=E, k=k, D=D, F=F, name="cpu_sample")
     wq_gu = oracle.layer.quantize_weights(d["w_gu"])
@@ -218,8 +219,9 @@ def cpu_baseline():
     flops = 3 * (f1 + f2)
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample="forward+backward of 4096 tokens x top-8 over 64 experts (512 rows per expert), "
-                       "d_model 2048, FFN 768, fp64 GEMMs on %d BLAS threads; %.1f s" % (cores, dt),
-                seconds=round(dt, 2), tokens_per_s=round(T / dt, 1))
+                       "d_model 2048, FFN 768, fp64 GEMMs on %d BLAS threads (elementwise numpy on 1); "
+                       "%.1f s" % (cores, dt),
+                blas_threads=int(cores), host_cpus=host_cpus, seconds=round(dt, 2), tokens_per_s=round(T / dt, 1))
 
 
 def load_traffic():
@@ -431,19 +433,18 @@ def dispatch_summary(d, name):
         print("%-40s %14d %6d %10.2f %10.2f %10.2f" % (kn[:40], grid, len(ts), ts[len(ts) // 2], ts[0], ts[-1]))
 
 
-def bench_dense(args):
+def dense_side(args):
     """The dense special case on the Qwen3-4B up-projection shape
     (X [4096, 2560], W [9728, 2560], one expert with offsets [0, M]): NVFP4
-    quantize of X (amax computed, cache flushed) and of W, the W4A4 GEMM to
-    bf16, and this build's BF16 NT GEMM on the same shape.  One JSON line;
-    `value` is the W4A4 GEMM's TFLOP/s (median of the timed repetitions)."""
+    quantize of X and of W (amax computed, cache flushed), the W4A4 GEMM to
+    bf16, and this build's BF16 NT GEMM on the same shape, each the median
+    of its timed repetitions (HIP events)."""
     import numpy as np
     import torch
     import workloads
     from nvfp4_quantized_moe_token_amd import ops
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     d = workloads.qwen3_4b_up()
     x = torch.from_numpy(np.ascontiguousarray(d["x"])).to(dev).to(torch.bfloat16)
     w = torch.from_numpy(np.ascontiguousarray(d["w"])).to(dev).to(torch.bfloat16)
@@ -471,7 +472,7 @@ def bench_dense(args):
     wq = ops.nvfp4_quantize(w)
     y4 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     yb = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    reps = max(5, args.steps)
+    reps = max(7, min(args.steps, 20))
     ms_qx = timed(lambda: ops.nvfp4_quantize(x, amax_out=xq[3], q=xq[0], scales=xq[1], gscale=xq[2]), 7, cold=True)
     ms_qw = timed(lambda: ops.nvfp4_quantize(w, amax_out=wq[3], q=wq[0], scales=wq[1], gscale=wq[2]), 7, cold=True)
     wq3 = (wq[0].view(1, N, K // 2), wq[1].view(1, N, K // 16), wq[2])
@@ -487,25 +488,40 @@ def bench_dense(args):
                 "algorithmic_bytes": in_bytes + M * N * 2}
 
     def quant_obj(ms, rows):
-        # the amax pass reads the tensor once more: 2 + 2 + 0.5625 B per element
+        # amax computed (amax_in not given): the amax pass reads the tensor
+        # once more, 2 + 2 + 0.5625 B per element
         by = rows * K * 2 * 2 + nvb(rows, K)
         gbs = by / (ms * 1e-3) / 1e9
-        return {"kernel": "amax + quantize (cold)", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4), "algorithmic_bytes": by}
+        return {"kernel": "amax + quantize (amax computed, cold)", "bound": "hbm", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
+                "algorithmic_bytes": by}
 
     w4 = gemm_obj(ms_w4, "grouped_gemm_w4a4 (E=1)", nvb(M, K) + nvb(N, K))
     bf = gemm_obj(ms_bf, "grouped_gemm_bf16 NT (E=1)", (M + N) * K * 2)
+    del flush
+    return {"M": M, "N": N, "K": K, "reps": reps,
+            "w4a4": {**w4, "frac_fp4_peak": round(w4["achieved"] / PEAK_FP4_TFLOPS, 4)},
+            "bf16": bf, "w4a4_speedup_vs_bf16": round(ms_bf / ms_w4, 3),
+            "quantize_x": quant_obj(ms_qx, M), "quantize_w": quant_obj(ms_qw, N)}
+
+
+def bench_dense(args):
+    """One JSON line for the dense workload: `value` is the W4A4 GEMM's
+    TFLOP/s (see dense_side)."""
+    import torch
+    torch.cuda.set_device(torch.device("cuda:0"))
+    r = dense_side(args)
+    w4 = r["w4a4"]
     res = {
         "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
-        "value": w4["achieved"], "unit": "TFLOP/s", "n_gpus": 1, "steps": reps, "warmup": 1,
-        "ms_per_step": round(ms_w4, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": w4["achieved"], "unit": "TFLOP/s", "n_gpus": 1, "steps": r["reps"], "warmup": 1,
+        "ms_per_step": w4["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16 mfma, fp32 acc", "data": "synthetic",
-        "config": {"workload": "qwen3_4b_up", "M": M, "N": N, "K": K, "parallelism": "none (1 GPU)"},
-        "w4a4_gemm": {**w4, "frac_fp4_peak": round(w4["achieved"] / PEAK_FP4_TFLOPS, 4),
-                      "speedup_vs_bf16": round(ms_bf / ms_w4, 3)},
-        "bf16_gemm": bf,
-        "quantize_x": quant_obj(ms_qx, M),
-        "quantize_w": quant_obj(ms_qw, N),
+        "config": {"workload": "qwen3_4b_up", "M": r["M"], "N": r["N"], "K": r["K"], "parallelism": "none (1 GPU)"},
+        "w4a4_gemm": {**w4, "speedup_vs_bf16": r["w4a4_speedup_vs_bf16"]},
+        "bf16_gemm": r["bf16"],
+        "quantize_x": r["quantize_x"],
+        "quantize_w": r["quantize_w"],
     }
     print(json.dumps(res), flush=True)
 
@@ -518,6 +534,8 @@ def main():
     ap.add_argument("--workload", default="moe_8k_update",
                     choices=["moe_8k_update", "moe_4k", "moe_16k_skew", "qwen3_4b_up"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense qwen3_4b_up W4A4 vs BF16 GEMM side measurement")
     ap.add_argument("--overlap", action="store_true",
                     help="weight-gradient GEMMs on a second stream (per-op times then overlap)")
     ap.add_argument("--pmc-run", action="store_true",
@@ -790,10 +808,12 @@ def main():
 
     def roofline_of_kernel(kname):
         """Roofline of one kernel over its launches in a step: algorithmic
-        work per launch / average launch duration (rocprofv3's avg).  The
-        bound is the lower ceiling: HBM when the kernel's algorithmic
-        FLOP/byte is below the ridge point (bf16 MFMA peak / HBM peak), the
-        MFMA otherwise; the other ceiling's fraction is reported beside it."""
+        work per launch / its average launch duration, both from the HIP
+        events around its launches inside the timed steps (on the stream it
+        runs on).  A GEMM is reported against the 16-bit MFMA peak -- the
+        contraction it runs -- with its HBM rate beside it (`hbm_view`);
+        its arithmetic intensity and the ridge point (bf16 MFMA peak / HBM
+        peak) are given so the reader can see which ceiling is nearer."""
         names = [o for o in STEP_OPS if KERNEL_OF_OP.get(o) == kname and o in per_op]
         n = len(names)
         ms = sum(per_op[o] for o in names) / n
@@ -801,21 +821,22 @@ def main():
         by = sum(op_work(o, T, k, E, D, F, backward)[1] for o in names) / n
         tfl = fl / (ms * 1e-3) / 1e12
         gbs = by / (ms * 1e-3) / 1e9
-        common = {"traffic": traffic_bytes(names), "algorithmic_bytes": round(by), "algorithmic_flops": round(fl),
-                  "flop_per_byte": round(fl / by, 1), "ridge_flop_per_byte": round(RIDGE, 1),
-                  "avg_launch_ms": round(ms, 4)}
+        tr = traffic_bytes(names)
+        out = {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(tfl, 1),
+               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tfl / PEAK_BF16_TFLOPS, 4),
+               "traffic": tr, "traffic_source": os.path.relpath(TRAFFIC_FILE, ROOT) if tr is not None else None,
+               "algorithmic_flops": round(fl), "algorithmic_bytes": round(by), "avg_launch_ms": round(ms, 4),
+               "flop_per_byte": round(fl / by, 1), "ridge_flop_per_byte": round(RIDGE, 1),
+               "hbm_view": {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4)},
+               **clock_fields(names, tfl)}
         if all(o in mfma for o in names):
-            # time-weighted MFMA busy fraction of the kernel's launches (counters)
-            common["mfma_busy_counter"] = round(sum(mfma[o]["mfma_busy"] * per_op[o] for o in names) /
-                                                sum(per_op[o] for o in names), 4)
-        if fl / by < RIDGE:
-            return {"kernel": kname, "ops": names, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), **common,
-                    "mfma_tflops": round(tfl, 1), "mfma_frac": round(tfl / PEAK_BF16_TFLOPS, 4),
-                    **{"mfma_" + key: v for key, v in clock_fields(names, tfl).items()}}
-        return {"kernel": kname, "ops": names, "bound": "mfma", "achieved": round(tfl, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tfl / PEAK_BF16_TFLOPS, 4), **common,
-                "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), **clock_fields(names, tfl)}
+            # time-weighted MFMA busy fraction of the kernel's launches, from
+            # the committed counter summary of the same kernel sources
+            out["mfma_busy_counter"] = round(sum(mfma[o]["mfma_busy"] * per_op[o] for o in names) /
+                                             sum(per_op[o] for o in names), 4)
+            out["mfma_busy_source"] = os.path.relpath(MFMA_FILE, ROOT)
+        return out
 
     # Dominant kernel: the largest share of the step's time.
     per_kernel = {}
@@ -829,9 +850,15 @@ def main():
 
     w4 = kernels["w4a4_gate_up"]
     bl = kernels["bf16_nt_gate_up_baseline"]
+    # The metric: the W4A4 grouped GEMMs of the step (gate+up with its SiLU
+    # epilogue, and down), their algorithmic FLOPs over their summed time.
+    w4_ops = ["w4a4_gate_up_silu", "w4a4_down"]
+    w4_ms = sum(per_op[o] for o in w4_ops)
+    w4_tflops = (f1 + f2) / (w4_ms * 1e-3) / 1e12
+    dense = dense_side(args) if not args.no_dense else None
     res = {
         "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
-        "value": round(tflops, 2),
+        "value": round(w4_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -845,15 +872,22 @@ def main():
         "config": {"workload": args.workload, "tokens": T, "d_model": D, "experts": E, "top_k": k, "ffn": F,
                    "step": "fwd W4A4 + bwd BF16" if backward else "fwd W4A4", "parallelism": "none (1 GPU)",
                    "wgrad_stream": wstream is not None},
-        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "value_definition": "W4A4 grouped GEMMs of the step (gate+up with the SiLU-gate epilogue, and down): "
+                            "%.1f GFLOP over their summed in-step time, HIP events" % ((f1 + f2) / 1e9),
+        "w4a4_in_step": {"ops": w4_ops, "ms": round(w4_ms, 4), "tflops": round(w4_tflops, 1),
+                         "frac_bf16_mfma_peak": round(w4_tflops / PEAK_BF16_TFLOPS, 4),
+                         "frac_fp4_mfma_peak": round(w4_tflops / PEAK_FP4_TFLOPS, 4)},
+        "step": {"ms": round(ms_per_step, 4), "gflop": round(step_flops / 1e9, 1), "tflops": round(tflops, 2),
+                 "frac_bf16_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                 "tokens_per_s": round(T / (ms_per_step * 1e-3), 1)},
         "graph_replay": None if graph_ms is None else {
-            "ms_per_step": round(graph_ms, 4), "value": round(step_flops / (graph_ms * 1e-3) / 1e12, 2),
+            "ms_per_step": round(graph_ms, 4), "tflops": round(step_flops / (graph_ms * 1e-3) / 1e12, 2),
             "tokens_per_s": round(T / (graph_ms * 1e-3), 1)},
-        "step_gflop": round(step_flops / 1e9, 1),
         "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
                       "bf16_same_shape_tflops": bl.get("tflops"),
                       "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3)},
+        "dense_qwen3_4b_up": dense,
         "quantize": roofline_of("quantize_x_perm_cold"),
         "quantize_16k": roofline_of("quantize_x_perm_16k_cold"),
         "permute_quantize": roofline_of("permute_quantize_x"),
