@@ -30,7 +30,8 @@ docstring of the function that takes it.
 Modules:
   nvfp4   -- scalar codecs, quantize, dequantize           (fp32 as defined)
   moe     -- permutation metadata, gather, unpermute, SiLU gate (fp64)
-  gemm    -- grouped W4A4 and BF16 GEMMs (fp64 on exact operands)
+  mx      -- MX formats (MXFP8 / MXFP4, E8M0 per 32) of the W4A8 variant
+  gemm    -- grouped W4A4, W4A8 and BF16 GEMMs (fp64 on exact operands)
   layer   -- the MoE layer forward / BF16 backward composed from the above
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
@@ -38,4 +39,4 @@ against hand-worked values (``tests/golden/``), brute force on tiny inputs,
 library routines and invariants -- never against itself.
 """
 
-from . import nvfp4, moe, gemm, layer  # noqa: F401
+from . import nvfp4, mx, moe, gemm, layer  # noqa: F401

@@ -15,7 +15,7 @@ tolerance |C - C_ref| <= 1e-3 * sum_k |a*b|.
 
 import numpy as np
 
-from . import nvfp4
+from . import mx, nvfp4
 
 
 def _segments(offsets):
@@ -45,6 +45,34 @@ def grouped_gemm_w4a4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, rows=None):
         if sel.size == 0:
             continue
         B = nvfp4.dequantize(b_q[e], b_s[e], np.asarray(b_g).reshape(E)[e:e + 1])
+        C[sel] = A[sel] @ B.T
+        AB[sel] = np.abs(A[sel]) @ np.abs(B).T
+    return C, AB
+
+
+def grouped_gemm_w4a8(a_q, a_s, b_q, b_s, offsets, rows=None, a_elem="e4m3", b_elem="e2m1"):
+    """The W4A8 variant: C[r, n] = sum_k deq(A)[r, k] * deq(B_e)[n, k] for r in
+    expert e's rows, A MXFP8 (E4M3 elements) and B MXFP4 (E2M1 elements),
+    both with E8M0 scales per 32 along K and no global scale.
+
+    a_q [M, K], a_s [M, K/32]; b_q [E, N, K/2], b_s [E, N, K/32]; offsets
+    [E+1].  ``rows`` restricts the result to those rows (then a_q / a_s
+    hold only those rows).  Returns (C fp64, absbound fp64).
+    """
+    off = np.asarray(offsets, dtype=np.int64)
+    E = off.size - 1
+    M = a_q.shape[0]
+    N = b_q.shape[1]
+    rows_idx = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    expert_of = np.searchsorted(off, rows_idx, side="right") - 1
+    A = mx.dequantize(a_q, a_s, a_elem)
+    C = np.zeros((len(rows_idx), N))
+    AB = np.zeros((len(rows_idx), N))
+    for e in range(E):
+        sel = np.nonzero(expert_of == e)[0]
+        if sel.size == 0:
+            continue
+        B = mx.dequantize(b_q[e], b_s[e], b_elem)
         C[sel] = A[sel] @ B.T
         AB[sel] = np.abs(A[sel]) @ np.abs(B).T
     return C, AB
