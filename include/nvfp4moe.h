@@ -71,6 +71,10 @@ typedef struct ihipStream_t* nvfp4moe_stream_t; /* == hipStream_t */
 #define NVFP4MOE_NN 1 /* C[M,N]   = A[M,K] . B_e[K,N]    (data gradient)     */
 #define NVFP4MOE_TN 2 /* C_e[K,N] = A_e[M_e,K]^T . B_e[M_e,N] (weight grad)  */
 
+/* MX element formats for mx_quantize (the W4A8 variant) */
+#define NVFP4MOE_MX_E4M3 0 /* MXFP8: E4M3 elements, one byte each */
+#define NVFP4MOE_MX_E2M1 1 /* MXFP4: E2M1 elements, two per byte */
+
 /* W4A4 GEMM epilogues */
 #define NVFP4MOE_EPI_NONE 0
 #define NVFP4MOE_EPI_SILU_GATE 1 /* c receives H = silu(gate) * up, see below */
@@ -259,6 +263,62 @@ int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const fl
                                 const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
                                 const int32_t* expert_offsets, int E, int64_t M_total, int64_t F,
                                 int64_t K, void* y1, void* h, float* amax_out,
+                                nvfp4moe_stream_t stream);
+
+/*
+ * mx_quantize -- MX quantization for the W4A8 variant, whose activations are
+ * MXFP8 ([JA], third paragraph: the activation-precision comparison of
+ * W4A16, W4A8 with MXFP8 activations, and W4A4).  The pages do not define MX;
+ * the library follows the published microscaling rule: every 32 consecutive
+ * elements of a row along K share one E8M0 scale byte S (value 2^(S-127));
+ * for a block with amax a > 0, S - 127 = floor(log2 a) - emax (emax 8 for
+ * E4M3, 2 for E2M1) clamped to [-127, 127], and S = 0 for an all-zero block.
+ * Element = (V / 2^(S-127)) rounded to nearest even and saturated to 448
+ * (E4M3) or 6 (E2M1); its sign bit is the sign of V (also for -0).  No global
+ * scale, no amax pass: each block is encoded from its own values.
+ *   x       [rows][K] F32 or BF16, 16-byte aligned, finite.
+ *   elem    NVFP4MOE_MX_E4M3: q [rows][K] bytes (16-byte aligned);
+ *           NVFP4MOE_MX_E2M1: q [rows][K/2] bytes, element 2j in the low
+ *           nibble (8-byte aligned).
+ *   scales  [rows][K/32] bytes out, row-major, unswizzled.
+ * Bit-exact and independent of launch shape.  Errors: EINVAL (NULL,
+ * negative, bad dtype or elem), ESHAPE (K % 32 != 0, alignment).
+ */
+int mx_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q,
+                uint8_t* scales, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_w4a8 -- the grouped GEMM of the W4A8 variant ([JA], third
+ * paragraph): MXFP8 activations (E4M3 elements) times MXFP4 expert weights
+ * (E2M1 elements), both with E8M0 scales per 32 along K, over the contiguous
+ * per-expert layout ([JA], fourth paragraph):
+ *   C[r][n] = sum_k deq(A)[r][k] * deq(B_e)[n][k],  r in [offsets[e], offsets[e+1])
+ * with deq = element * 2^(S-127).  The scales are powers of two, so gfx950's
+ * scaled MFMA takes them natively (no operand expansion); accumulation in
+ * fp32.  Rows >= offsets[E] are not written.
+ *   a_q [M_total][K], a_s [M_total][K/32]     (mx_quantize E4M3)
+ *   b_q [E][N][K/2],  b_s [E][N][K/32]        (mx_quantize E2M1)
+ *   offsets [E+1] int32 on the device; c [M_total][N] F32 or BF16.
+ * K % 128 == 0, N % 32 == 0; a_q, b_q, c 16-byte aligned, a_s, b_s 4-byte
+ * aligned; M_total, N, K < 2^31.  Errors: EINVAL (NULL, negative, bad
+ * dtype), ESHAPE (shape and alignment rules).
+ */
+int grouped_gemm_w4a8(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                      const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K, void* c,
+                      int c_dtype, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_w4a8_silu_gate -- the W4A8 gate+up GEMM with the SiLU gate
+ * and the amax of its output in the epilogue, as grouped_gemm_w4a4_silu_gate
+ * ([JA], fourth paragraph: op fusion): equal, bit for bit, to
+ * grouped_gemm_w4a8 (N = 2F, bf16 C) followed by silu_gate_fwd.
+ *   operands as grouped_gemm_w4a8 with N = 2F (B_e = [gate; up] rows)
+ *   y1 [M_total][2F] bf16 or NULL, h [M_total][F] bf16, amax_out [1] or NULL.
+ * F % 128 == 0, K % 128 == 0.  Errors as grouped_gemm_w4a8.
+ */
+int grouped_gemm_w4a8_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
+                                const uint8_t* b_s, const int32_t* expert_offsets, int E, int64_t M_total,
+                                int64_t F, int64_t K, void* y1, void* h, float* amax_out,
                                 nvfp4moe_stream_t stream);
 
 /*

@@ -29,6 +29,10 @@ SIGNATURES = {
                                   c_vp, c_int, c_int, c_vp, c_vp, c_size, c_vp]),
     "grouped_gemm_w4a4_silu_gate": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
                                             c_vp, c_vp, c_vp, c_vp]),
+    "mx_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
+    "grouped_gemm_w4a8": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp]),
+    "grouped_gemm_w4a8_silu_gate": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                            c_vp, c_vp]),
     "grouped_gemm_bf16": (c_int, [c_int, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_int,
                                   c_vp, c_size, c_vp]),
     "grouped_gemm_bf16_tn_gather": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_i64, c_i64, c_i64,
@@ -42,6 +46,7 @@ OK, EINVAL, ESHAPE, EARCH, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4, -5
 F32, BF16, U8 = 0, 1, 2
 NT, NN, TN = 0, 1, 2
 EPI_NONE, EPI_SILU_GATE = 0, 1
+MX_E4M3, MX_E2M1 = 0, 1
 ABI_VERSION = 1
 STATUS_BAD_EXPERT = 1
 

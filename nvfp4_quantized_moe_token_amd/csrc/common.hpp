@@ -99,6 +99,9 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);
 
 // max |x| per row-group (quantize.hip); amax_out is cleared first.
 int launch_amax(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out, hipStream_t st);
+// MX quantizer (mx.hip); arguments validated, rows * K > 0.
+int mx_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q, uint8_t* scales,
+                       hipStream_t st);
 // The same without clearing amax_out (an earlier launch on the stream did).
 int launch_amax_uncleared(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out,
                           hipStream_t st);

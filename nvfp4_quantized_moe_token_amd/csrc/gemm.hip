@@ -54,6 +54,8 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
@@ -63,12 +65,18 @@ constexpr int BK = 64;                       // reduction elements per MFMA grou
 #endif
 constexpr bool kNMajor = NVFP4MOE_GEMM_NMAJOR;  // tile order within an expert (find_tile)
 constexpr int NV_KS = 256;                   // reduction elements per NVFP4 stage
+constexpr int MX_KS = 128;                   // reduction elements per MX (W4A8) stage
 constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
 constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
-// W4A4_SILU: the W4A4 gate+up GEMM with the SiLU-gate epilogue.
-enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4 };
+// W4A4_SILU: the W4A4 gate+up GEMM with the SiLU-gate epilogue.  W4A8:
+// MXFP8 activations x MXFP4 weights on the scaled MFMA (W4A8_SILU: with the
+// SiLU-gate epilogue).
+enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6 };
 constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU; }
+constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU; }
+constexpr bool is_q(int mode) { return is_nv(mode) || is_mx(mode); }
+constexpr bool is_silu(int mode) { return mode == W4A4_SILU || mode == W4A8_SILU; }
 
 struct Params {
   const void* a;       // NT/NN/TN: bf16 A; W4A4: packed codes of A
@@ -85,8 +93,8 @@ struct Params {
   int accumulate;
   int n_tiles;         // tiles along N
   int k_tiles_tn;      // TN: tiles along K (rows of C_e)
-  void* h;             // W4A4_SILU: H [M][N/2] bf16 (c = Y1 or NULL)
-  float* amax;         // W4A4_SILU: max |H| (cleared before the launch), or NULL
+  void* h;             // SiLU-gate modes: H [M][N/2] bf16 (c = Y1 or NULL)
+  float* amax;         // SiLU-gate modes: max |H| (cleared before the launch), or NULL
   const int32_t* bsrc; // TN with gathered B: B row of reduction row r is bsrc[r] / bk (none if < 0)
   int bk;
   int bk_shift;        // log2(bk) when bk is a power of two, else -1
@@ -413,6 +421,34 @@ __device__ __forceinline__ f16x8_t nv_expand(const NVFrag& f, int kk) {
   return __builtin_bit_cast(f16x8_t, o);
 }
 
+// MX (W4A8) fragments of 64-element chunk c of a stage, in the operand
+// layouts of the scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (probed on the
+// device): for both operands lane l serves row l % 32 and its E8M0 scale
+// covers the 32-element block l / 32 of the chunk; a 4-bit operand holds
+// k = 32h .. 32h+31 (h = l / 32) in its 16 bytes, an 8-bit operand holds
+// k = 16h .. 16h+15 in bytes 0..15 and k = 32+16h .. 32+16h+15 in bytes
+// 16..31.
+// fp8 A: the 16-byte units 4c + h and 4c + 2 + h of the row's 128 bytes.
+__device__ __forceinline__ i32x8_t frag_mx_a(const uint8_t* codes, int base, int c, int lane) {
+  const int row = base + (lane & 31), h = lane >> 5;
+  const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(codes + row * 128 + (((4 * c + h) ^ kswz(row)) << 4));
+  const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(codes + row * 128 + (((4 * c + 2 + h) ^ kswz(row)) << 4));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// fp4 B: the 16-byte unit 2c + h of the row's 64 bytes (the operand's upper
+// four registers are not read for a 4-bit format).
+__device__ __forceinline__ i32x8_t frag_mx_b(const uint8_t* codes, int base, int c, int lane) {
+  const int row = base + (lane & 31), h = lane >> 5;
+  const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + row * 64 + (((2 * c + h) ^ rswz<64>(row)) << 4));
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+// E8M0 scale of the lane's row and block 2c + h, in byte 0 (the MFMA reads
+// byte 0 of the scale register with opsel 0); rows hold 4 bytes per stage.
+__device__ __forceinline__ int scale_mx(const uint8_t* sc, int base, int c, int lane) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(sc + (base + (lane & 31)) * 4);
+  return (int)(w >> (8 * (2 * c + (lane >> 5))));
+}
+
 // Scheduling hint: N_MFMA MFMAs with N_DS LDS reads interleaved one after
 // each MFMA (the reads feed the next sub-step), then any reads left over.
 template <int N_MFMA, int N_DS>
@@ -442,6 +478,8 @@ template <int MODE, bool A_SIDE, int ROWS, int NW, int BKB>
 constexpr int loads_per_wave() {
   if constexpr (is_nv(MODE))
     return KMajorLoader<ROWS, NW>::N_INSTR;
+  else if constexpr (is_mx(MODE))
+    return A_SIDE ? KMajorLoader<ROWS, NW>::N_INSTR : KMajorLoader<ROWS, NW, 64>::N_INSTR;
   else if constexpr ((A_SIDE && MODE == TN_BF16) || (!A_SIDE && MODE != NT_BF16))
     return MNMajorLoader<ROWS, NW, BKB>::N_INSTR;
   else
@@ -452,21 +490,26 @@ template <int N>
 struct IntConst {
   static constexpr int value = N;
 };
-// NVFP4 operand regions of a row-grouped tile: A rows [m0, m_end) (codes and
-// scales); B the n-tile's rows of the expert (SiLU-gate tiles gather gate
-// and up rows: the region is the whole expert).
+// Quantized operand regions of a row-grouped tile: A rows [m0, m_end) (codes
+// and scales); B the n-tile's rows of the expert (SiLU-gate tiles gather gate
+// and up rows: the region is the whole expert).  Bytes per row: NVFP4 codes
+// K/2 and scales K/16 for both operands; MX (W4A8) A codes K (fp8), B codes
+// K/2 (fp4), scales K/32 for both.
+template <bool MX>
 __device__ __forceinline__ void nv_a_regions(const Params& p, int64_t m0, int64_t m_end, __amdgpu_buffer_rsrc_t& ra,
                                              __amdgpu_buffer_rsrc_t& rsa) {
-  ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * (p.K / 2), (m_end - m0) * (p.K / 2));
-  rsa = make_rsrc(p.as + m0 * (p.K / 16), (m_end - m0) * (p.K / 16));
+  const int64_t cb = MX ? p.K : p.K / 2, sb = MX ? p.K / 32 : p.K / 16;
+  ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * cb, (m_end - m0) * cb);
+  rsa = make_rsrc(p.as + m0 * sb, (m_end - m0) * sb);
 }
-template <int BN, bool SILU>
+template <int BN, bool SILU, bool MX>
 __device__ __forceinline__ void nv_b_regions(const Params& p, int expert, int64_t n0, __amdgpu_buffer_rsrc_t& rb,
                                              __amdgpu_buffer_rsrc_t& rsb) {
   const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
   const int64_t brow = (int64_t)expert * p.N + (SILU ? 0 : n0);
+  const int64_t sb = MX ? p.K / 32 : p.K / 16;
   rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
-  rsb = make_rsrc(p.bs + brow * (p.K / 16), nv * (p.K / 16));
+  rsb = make_rsrc(p.bs + brow * sb, nv * sb);
 }
 
 // ---- the kernel ----
@@ -479,20 +522,24 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "bad wave tiling");
   constexpr bool NV = is_nv(MODE);
-  constexpr bool SILU = MODE == W4A4_SILU;
+  constexpr bool MX = is_mx(MODE);
+  constexpr bool QM = NV || MX;  // quantized operands, row-grouped
+  constexpr bool SILU = is_silu(MODE);
   // Reduction elements per pipeline stage: 64 for bf16 (128-byte rows);
   // 256 for NVFP4, so that each row brings a whole 128-byte line of codes
-  // and 16 bytes of scales per stage.
+  // and 16 bytes of scales per stage; 128 for MX (W4A8): 128 bytes of fp8
+  // codes per A row, 64 bytes of fp4 codes per B row, 4 scale bytes each.
   // bf16 stages hold BKB reduction elements (64: 128-byte K-major rows; 32:
   // 64-byte rows, for deeper rings in the same LDS).
-  static_assert(!NV || BKB == 64, "NVFP4 stages use 128-byte code rows");
-  constexpr int KS = NV ? NV_KS : BKB;
+  static_assert(!QM || BKB == 64, "quantized stages use 128-byte A code rows");
+  constexpr int KS = NV ? NV_KS : MX ? MX_KS : BKB;
   constexpr int A_BYTES = BM * BKB * 2;
-  constexpr int B_BYTES = BN * BKB * 2;
-  constexpr int SC_BYTES = NV ? (BM + BN) * 16 : 0;  // A scales then B scales
+  constexpr int B_BYTES = MX ? BN * 64 : BN * BKB * 2;
+  constexpr int SC_ROW = NV ? 16 : MX ? 4 : 0;             // scale bytes per row and stage
+  constexpr int SC_BYTES = (BM + BN) * SC_ROW;             // A scales then B scales
   constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static_assert(!NV || (BM + BN) % (64 * NW) == 0, "NVFP4 scales: rows per wave");
-  constexpr int SC_INSTR = NV ? (BM + BN) / (64 * NW) : 0;
+  static_assert(!QM || (BM + BN) % (64 * NW) == 0, "quantized scales: rows per wave");
+  constexpr int SC_INSTR = QM ? (BM + BN) / (64 * NW) : 0;
   // Per-wave loads per step, for the vmcnt waits.
   constexpr int A_INSTR = loads_per_wave<MODE, true, BM, NW, BKB>();
   constexpr int B_INSTR = loads_per_wave<MODE, false, BN, NW, BKB>();
@@ -612,7 +659,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     } else if constexpr (MODE == TN_BF16) {
       ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + (int64_t)lo * p.K, red * p.K * 2);
     } else {
-      nv_a_regions(p, m0, m_end, ra, rsa);
+      nv_a_regions<MX>(p, m0, m_end, ra, rsa);
     }
     if constexpr (MODE == NT_BF16) {
       const int64_t nv = p.N - n0 < BN ? p.N - n0 : BN;
@@ -623,7 +670,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       rb = p.bsrc ? make_rsrc(p.b, p.b_rows * p.N * 2)
                   : make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
     } else {
-      nv_b_regions<BN, SILU>(p, expert, n0, rb, rsb);
+      nv_b_regions<BN, SILU, MX>(p, expert, n0, rb, rsb);
     }
     const int64_t gate_f = SILU ? p.N / 2 : 0;
     const int64_t j0 = n0 / 2;
@@ -643,18 +690,34 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // regions into the LDS stage at byte address st.
     auto nv_load = [&](__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, __amdgpu_buffer_rsrc_t rsa_,
                        __amdgpu_buffer_rsrc_t rsb_, int64_t j0_, int64_t k0, uint32_t st) {
-      // Codes: 128 bytes (256 elements) per row, laid out like a K-major
-      // bf16 tile of 64 16-bit units per row.
-      KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 4, k0 / 4, p.K / 4);
-      KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
-      // Scales: 16 bytes per row, 64 rows per load, A rows first.
+      if constexpr (MX) {
+        // fp8 A codes: 128 bytes (128 elements) per row, a K-major tile of
+        // 64 16-bit units per row; fp4 B codes: 64 bytes per row.
+        KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 2, k0 / 2, p.K / 2);
+        KMajorLoader<BN, NW, 64>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
+        // E8M0 scales: 4 bytes per row (one word), 64 rows per load, A rows first.
 #pragma unroll
-      for (int i = 0; i < SC_INSTR; ++i) {
-        const int idx = wid + NW * i;
-        const bool is_a = idx * 64 < BM;
-        const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-        const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
-        dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
+        for (int i = 0; i < SC_INSTR; ++i) {
+          const int idx = wid + NW * i;
+          const bool is_a = idx * 64 < BM;
+          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
+          dma4(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 256, (uint32_t)(grow * (p.K / 32) + k0 / 32));
+        }
+      } else {
+        // Codes: 128 bytes (256 elements) per row, laid out like a K-major
+        // bf16 tile of 64 16-bit units per row.
+        KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 4, k0 / 4, p.K / 4);
+        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
+        // Scales: 16 bytes per row, 64 rows per load, A rows first.
+#pragma unroll
+        for (int i = 0; i < SC_INSTR; ++i) {
+          const int idx = wid + NW * i;
+          const bool is_a = idx * 64 < BM;
+          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
+          dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
+        }
       }
     };
     auto load_step = [&](int64_t kt, int stage) {
@@ -751,8 +814,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
             nx_r0 = uniform64(r0);
             nx_r1 = uniform64(r1);
             __amdgpu_buffer_rsrc_t na, nb, nsa, nsb;
-            nv_a_regions(p, nx_r0, nx_r1, na, nsa);
-            nv_b_regions<BN, SILU>(p, nx_e, (int64_t)nx_nt * BN, nb, nsb);
+            nv_a_regions<MX>(p, nx_r0, nx_r1, na, nsa);
+            nv_b_regions<BN, SILU, MX>(p, nx_e, (int64_t)nx_nt * BN, nb, nsb);
             nv_load(na, nb, nsa, nsb, (int64_t)nx_nt * BN / 2, 0, smem_lds + (uint32_t)((slot0 + nk) % S) * STAGE);
             pre_next = true;
           }
@@ -799,6 +862,44 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
                   if (kk + 1 < BK / 16) interleave_mfma_valu<NA * FN, (8 * (NA + FN) + NA * FN - 1) / (NA * FN)>();
                 }
               }
+            }
+          } else if constexpr (MX) {
+            // Two 64-element chunks per stage (K % 128 == 0); the fragments
+            // and scales of chunk c+1 are read while the MFMAs of c run.
+            // The B (fp4) fragment is the MFMA's first operand, as in the
+            // other layouts, so the result is the transposed tile.
+            i32x8_t fa[2][NA], fb[2][FN];
+            int sa[2][NA], sb[2][FN];
+            const uint8_t* sca = st + A_BYTES + B_BYTES;
+            auto read_frags = [&](int c, int buf) {
+#pragma unroll
+              for (int i = 0; i < NA; ++i) {
+                fa[buf][i] = frag_mx_a(st, wm * WTM + i * 32, c, lane);
+                sa[buf][i] = scale_mx(sca, wm * WTM + i * 32, c, lane);
+              }
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                fb[buf][j] = frag_mx_b(st + A_BYTES, wn * WTN + j * 32, c, lane);
+                sb[buf][j] = scale_mx(sca + BM * 4, wn * WTN + j * 32, c, lane);
+              }
+            };
+            constexpr int NRD = 3 * NA + 2 * FN;  // LDS reads per chunk: 2 + 1 per A, 1 + 1 per B
+            read_frags(0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+            for (int c = 0; c < KS / BK; ++c) {
+              if (c + 1 < KS / BK) read_frags(c + 1, (c + 1) & 1);
+#pragma unroll
+              for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                      fb[c & 1][j], fa[c & 1][i], acc[i][j], 4 /* first operand: fp4 E2M1 */,
+                      0 /* second operand: fp8 E4M3 */, 0, sb[c & 1][j], 0, sa[c & 1][i]);
+              if (c + 1 < KS / BK)
+                interleave_mfma_ds<NA * FN, NRD>();
+              else
+                interleave_mfma_ds<NA * FN, 0>();
             }
           } else {
             // Fragments of sub-step kk+1 are read while the MFMAs of kk run.
@@ -1093,7 +1194,8 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   X(10, 256, 128, 4, 1, 3, 32)   \
   X(11, 128, 256, 2, 2, 3, 32)   \
   X(12, 256, 256, 4, 2, 3, 32)   \
-  X(13, 256, 256, 2, 2, 4, 32)
+  X(13, 256, 256, 2, 2, 4, 32)   \
+  X(14, 256, 256, 4, 2, 3, 64)
 
 // Measured on the MoE shapes (expert rows ~512, N 768..2048, K 768..2048):
 // 256 x 256 tiles on 8 waves (4 x 2); two 64-k stages for the NT and W4A4
@@ -1101,7 +1203,9 @@ int launch_cfg(const Params& p0, hipStream_t st) {
 // whose MN-major operands come through transposed LDS reads (NN -9..-12%,
 // TN -2..-4% against two 64-k stages).  Two 4-wave workgroups per CU
 // (config 10), to overlap one's epilogue with the other's loop, was slower.
-constexpr int default_config(int mode) { return mode == NN_BF16 || mode == TN_BF16 ? 9 : 1; }
+constexpr int default_config(int mode) {
+  return mode == NN_BF16 || mode == TN_BF16 ? 9 : is_mx(mode) ? 14 : 1;
+}
 #ifdef NVFP4MOE_GEMM_FORCE_CONFIG
 constexpr int kForcedConfig = NVFP4MOE_GEMM_FORCE_CONFIG;
 #else
@@ -1115,8 +1219,10 @@ constexpr int built_config(int mode) { return kForcedConfig >= 0 ? kForcedConfig
 // multiples of 64 columns.
 constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s, int bkb) {
   const int nw = wm * wn;
-  if (is_nv(mode) && bkb != 64) return false;
-  if (!is_nv(mode)) {
+  if (is_q(mode) && bkb != 64) return false;
+  // MX: whole loads of 128-byte A rows (8 per load) and 64-byte B rows (16 per load) per wave
+  if (is_mx(mode) && (bm % (8 * nw) != 0 || bn % (16 * nw) != 0)) return false;
+  if (!is_q(mode)) {
     // whole K-major loads (512 / bkb rows each) and MN-major loads (512 / cols rows each) per wave
     const bool kmaj_a = mode != TN_BF16, kmaj_b = mode == NT_BF16;
     if (kmaj_a && bm % ((512 / bkb) * nw) != 0) return false;
@@ -1125,9 +1231,11 @@ constexpr bool cfg_ok(int mode, int bm, int bn, int wm, int wn, int s, int bkb) 
     if (!kmaj_b && (bn != 128 && bn != 256 || (bkb / (512 / bn)) % nw != 0)) return false;
     if ((bm / wm) % 32 != 0 || (bn / wn) % 32 != 0) return false;
   }
-  return s * (bm + bn) * (is_nv(mode) ? 144 : bkb * 2) <= 160 * 1024 &&
-         (!is_nv(mode) || (bm + bn) % (64 * wm * wn) == 0) &&
-         (mode != W4A4_SILU || (bn == 256 && (bn / wn) % 64 == 0));
+  const int stage = is_nv(mode) ? (bm + bn) * 144 : is_mx(mode) ? bm * 128 + bn * 64 + (bm + bn) * 4
+                                                                : (bm + bn) * bkb * 2;
+  return s * stage <= 152 * 1024 &&   // 160 KiB of LDS less the offsets copy and tile state
+         (!is_q(mode) || (bm + bn) % (64 * wm * wn) == 0) &&
+         (!is_silu(mode) || (bn == 256 && (bn / wn) % 64 == 0));
 }
 
 template <int MODE>
@@ -1137,7 +1245,7 @@ int launch_mode(int cfg, const Params& p, hipStream_t st) {
   case I:                                                                                      \
     if constexpr (built_config(MODE) == I && cfg_ok(MODE, BM_, BN_, WM_, WN_, S_, BK_)) {       \
       if (p.c_f32) {                                                                           \
-        if constexpr (MODE != W4A4_SILU) return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, BK_, true>(p, st); \
+        if constexpr (!is_silu(MODE)) return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, BK_, true>(p, st); \
       } else {                                                                                 \
         return launch_cfg<MODE, BM_, BN_, WM_, WN_, S_, BK_, false>(p, st);                    \
       }                                                                                        \
@@ -1163,6 +1271,8 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case NN_BF16: return launch_mode<NN_BF16>(cfg, p, st);
     case TN_BF16: return launch_mode<TN_BF16>(cfg, p, st);
     case W4A4_SILU: return launch_mode<W4A4_SILU>(cfg, p, st);
+    case W4A8: return launch_mode<W4A8>(cfg, p, st);
+    case W4A8_SILU: return launch_mode<W4A8_SILU>(cfg, p, st);
     default: return launch_mode<W4A4>(cfg, p, st);
   }
 }
@@ -1236,6 +1346,61 @@ extern "C" int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_
   if (F < 0) return NVFP4MOE_EINVAL;
   return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h,
                     amax_out, as_stream(stream));
+}
+
+namespace {
+
+// Shared by both W4A8 entry points.  silu: c = Y1 (NULL: not stored), h = H.
+int w4a8_entry(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+               const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K, void* c, int c_dtype,
+               int silu, void* h, float* amax_out, hipStream_t st) {
+  if (E < 1 || M_total < 0 || N < 0 || K < 0) return NVFP4MOE_EINVAL;
+  if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (silu && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (!expert_offsets) return NVFP4MOE_EINVAL;
+  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h : !c))) return NVFP4MOE_EINVAL;
+  if (K % 128 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (silu && N % 256 != 0) return NVFP4MOE_ESHAPE;
+  if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) ||
+      !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, 16) || !aligned(h, 16))
+    return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (silu && amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+  if (M_total == 0 || N == 0) return launch_status();
+  Params p = {};
+  p.a = a_q;
+  p.b = b_q;
+  p.as = a_s;
+  p.bs = b_s;
+  p.offsets = expert_offsets;
+  p.c = c;
+  p.M = M_total;
+  p.N = N;
+  p.K = K;
+  p.E = E;
+  p.c_f32 = c_dtype == NVFP4MOE_F32;
+  p.h = h;
+  p.amax = amax_out;
+  return launch(silu ? W4A8_SILU : W4A8, p, st);
+}
+
+}  // namespace
+
+extern "C" int grouped_gemm_w4a8(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                                 const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
+                                 void* c, int c_dtype, nvfp4moe_stream_t stream) {
+  return w4a8_entry(a_q, a_s, b_q, b_s, expert_offsets, E, M_total, N, K, c, c_dtype, 0, nullptr, nullptr,
+                    as_stream(stream));
+}
+
+extern "C" int grouped_gemm_w4a8_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
+                                           const uint8_t* b_s, const int32_t* expert_offsets, int E, int64_t M_total,
+                                           int64_t F, int64_t K, void* y1, void* h, float* amax_out,
+                                           nvfp4moe_stream_t stream) {
+  if (F < 0) return NVFP4MOE_EINVAL;
+  return w4a8_entry(a_q, a_s, b_q, b_s, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h, amax_out,
+                    as_stream(stream));
 }
 
 extern "C" int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,

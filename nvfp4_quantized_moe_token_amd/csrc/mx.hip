@@ -1,0 +1,152 @@
+// MX quantization for the W4A8 variant: MXFP8 (E4M3 elements) activations
+// and MXFP4 (E2M1 elements) weights, each 32 consecutive elements along K
+// sharing one E8M0 (power-of-two) scale.
+//
+// The W4A8 activation-precision variant is the one the report's ablation
+// sets between W4A16 and W4A4 ("miniTE報告、NVFP4強化学習の安定性を検証",
+// third paragraph).  The pages do not define MX; the library follows the
+// published microscaling rule: for a block with amax a > 0 the shared scale
+// is X = 2^(floor(log2 a) - emax) (emax = 8 for E4M3, 2 for E2M1), clamped to
+// 2^[-127, 127], and 2^-127 for an all-zero block; every element is V / X
+// rounded to nearest, ties to even, saturated to 448 (E4M3) or 6 (E2M1), its
+// sign bit the sign of V.  V / X is a power-of-two scaling, exact in fp32
+// except where it falls below the normal range, where the element rounds to
+// zero in both formats anyway.
+//
+// Layout: two lanes per 32-block, each reading 16 consecutive elements (32
+// bytes of bf16 or 64 of fp32); the block amax is the max of the pair, taken
+// with one lane shuffle.  Codes: 16 bytes (E4M3) or 8 bytes (E2M1) per lane,
+// so a wave stores one contiguous run; the even lane of a pair stores the
+// scale byte.  The grid covers the tensor once (grid-stride only past the
+// launch limit), as the NVFP4 quantizer does.
+#include "common.hpp"
+
+namespace nvfp4moe {
+namespace {
+
+typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+
+// Unbiased shared exponent of a block with amax a: floor(log2 a) - emax,
+// clamped to [-127, 127]; -127 when a == 0 (also when a is an fp32
+// subnormal, whose exponent is below -126: the clamp gives -127 there).
+template <int EMAX>
+__device__ __forceinline__ int shared_exp(float a) {
+  if (!(a > 0.0f)) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(a) - 1 - EMAX;  // a = m * 2^(e+1), m in [0.5, 1)
+  return e < -127 ? -127 : e > 127 ? 127 : e;
+}
+
+// 16 fp32 values of a half-block to E4M3 codes (16 bytes): scaled by
+// 2^-se (exact), clamped to +-448 (the format saturates; the converter
+// would otherwise overflow), then rounded to nearest even by the hardware
+// converter with a unit scale.
+__device__ __forceinline__ uint4 encode16_e4m3(const float (&v)[16], int se) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = __builtin_ldexpf(v[4 * q + i], -se);
+      r[i] = __builtin_copysignf(fminf(fabsf(s), 448.0f), s);
+    }
+    s16x2_t p = {0, 0};
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, r[0], r[1], 1.0f, false);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, r[2], r[3], 1.0f, true);
+    w[q] = __builtin_bit_cast(uint32_t, p);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 16 fp32 values to E2M1 codes (8 bytes, element 2j in the low nibble of
+// pair j): scaled by 2^-se, rounded by the hardware converter with a unit
+// scale (RNE, saturating to 6, sign kept).
+__device__ __forceinline__ uint2 encode16_e2m1(const float (&v)[16], int se) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#define MXQ_PAIR(I, SEL)                                                                                       \
+  w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], __builtin_ldexpf(v[8 * h + (I)], -se),                  \
+                                                  __builtin_ldexpf(v[8 * h + (I) + 1], -se), 1.0f, SEL)
+    MXQ_PAIR(0, 0);
+    MXQ_PAIR(2, 1);
+    MXQ_PAIR(4, 2);
+    MXQ_PAIR(6, 3);
+#undef MXQ_PAIR
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// One thread per 16-element half-block; half-blocks 2b and 2b+1 (lanes of
+// one wave: the count is even) form block b.
+template <int NT, bool BF16, bool E4M3>
+__global__ __launch_bounds__(NT) void mx_quantize_kernel(const uint4* __restrict__ x, int64_t nhalf,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+  constexpr int EMAX = E4M3 ? 8 : 2;
+  for (int64_t hb = blockIdx.x * (int64_t)NT + threadIdx.x; hb < nhalf; hb += (int64_t)gridDim.x * NT) {
+    float v[16];
+    if (BF16) {
+      const uint4 w0 = x[2 * hb], w1 = x[2 * hb + 1];
+      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_lo(ws[i]);
+        v[2 * i + 1] = bf16_hi(ws[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 w = x[4 * hb + i];
+        v[4 * i] = __uint_as_float(w.x);
+        v[4 * i + 1] = __uint_as_float(w.y);
+        v[4 * i + 2] = __uint_as_float(w.z);
+        v[4 * i + 3] = __uint_as_float(w.w);
+      }
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));  // the partner half of the block
+    const int se = shared_exp<EMAX>(a);
+    if (E4M3)
+      reinterpret_cast<uint4*>(q)[hb] = encode16_e4m3(v, se);
+    else
+      reinterpret_cast<uint2*>(q)[hb] = encode16_e2m1(v, se);
+    if ((hb & 1) == 0) scales[hb >> 1] = (uint8_t)(se + 127);
+  }
+}
+
+}  // namespace
+
+// Enqueue the MX quantizer (arguments validated; rows * K > 0).
+int mx_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q, uint8_t* scales,
+                       hipStream_t st) {
+  constexpr int NT = 256;
+  const int64_t nhalf = rows * (K / 16);
+  int64_t grid = cdiv(nhalf, NT);
+  if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const bool bf = x_dtype == NVFP4MOE_BF16, e4 = elem == NVFP4MOE_MX_E4M3;
+  if (bf && e4) mx_quantize_kernel<NT, true, true><<<(unsigned)grid, NT, 0, st>>>(xv, nhalf, q, scales);
+  else if (bf) mx_quantize_kernel<NT, true, false><<<(unsigned)grid, NT, 0, st>>>(xv, nhalf, q, scales);
+  else if (e4) mx_quantize_kernel<NT, false, true><<<(unsigned)grid, NT, 0, st>>>(xv, nhalf, q, scales);
+  else mx_quantize_kernel<NT, false, false><<<(unsigned)grid, NT, 0, st>>>(xv, nhalf, q, scales);
+  return launch_status();
+}
+
+}  // namespace nvfp4moe
+
+extern "C" int mx_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q,
+                           uint8_t* scales, nvfp4moe_stream_t stream) {
+  using namespace nvfp4moe;
+  if (rows < 0 || K < 0) return NVFP4MOE_EINVAL;
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (elem != NVFP4MOE_MX_E4M3 && elem != NVFP4MOE_MX_E2M1) return NVFP4MOE_EINVAL;
+  if (rows * K > 0 && (!x || !q || !scales)) return NVFP4MOE_EINVAL;
+  if (K % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (rows * K > 0 && (!aligned(x, 16) || !aligned(q, elem == NVFP4MOE_MX_E4M3 ? 16 : 8))) return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (rows * K == 0) return NVFP4MOE_OK;
+  return mx_quantize_launch(x, x_dtype, rows, K, elem, q, scales, as_stream(stream));
+}

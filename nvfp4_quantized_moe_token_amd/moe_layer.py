@@ -18,6 +18,14 @@ Backward in BF16 (same page, first paragraph), no amax reduction at all:
   on the kept permuted rows, or with its activation rows gathered from X
   through the routing's src (grouped_gemm_bf16_tn_gather: no 268 MB copy at
   8192 tokens, measured ~0.1 ms slower than the copy's TN plus its write).
+W4A8 forward (same page, third paragraph: the W4A8 variant with MXFP8
+activations; MXFP4 expert weights): MX scales are per 32-element block with
+no tensor amax, so X is quantized once per token and the packed rows are
+permuted afterwards (quantize(permute(X)) == permute(quantize(X)) row by
+row):
+  mx_quantize(X, E4M3)  ->  moe_permute (metadata + gather of the code rows)
+  + moe_gather (scale rows)  ->  grouped_gemm_w4a8_silu_gate  ->
+  mx_quantize(H, E4M3)  ->  grouped_gemm_w4a8 (down)  ->  moe_unpermute.
 """
 
 import torch
@@ -132,3 +140,43 @@ def backward(dy, topk_w, w_gu, w_dn, meta, buf, wgrad_stream=None, x=None):
         done = torch.cuda.Event()
         done.record(wgrad_stream)
         main.wait_event(done)
+
+
+def quantize_expert_weights_mx(w):
+    """MXFP4 weights of stacked experts [E, N, K] (E8M0 scale per 32 along
+    K; no per-expert scale).  Once per optimizer step."""
+    E, N, K = w.shape
+    q, sc = ops.mx_quantize(w.reshape(E * N, K), ops.MX_E2M1)
+    return dict(q=q.view(E, N, K // 2), s=sc.view(E, N, K // 32))
+
+
+class BuffersW4A8:
+    """Device buffers of one W4A8 forward step, allocated once and reused."""
+
+    def __init__(self, T, k, E, D, F, device):
+        R = T * k
+        bf, u8 = torch.bfloat16, torch.uint8
+        e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        self.T, self.k, self.E, self.D, self.F = T, k, E, D, F
+        self.ws = e(max(ops.moe_permute_workspace_size(T, k, E), 1), dt=u8)
+        self.xq, self.xs = e(T, D, dt=u8), e(T, D // 32, dt=u8)
+        self.a1_q, self.a1_s = e(R, D, dt=u8), e(R, D // 32, dt=u8)
+        self.h = e(R, F)
+        self.a2_q, self.a2_s = e(R, F, dt=u8), e(R, F // 32, dt=u8)
+        self.y2 = e(R, D)
+        self.out = e(T, D)
+
+
+def forward_w4a8(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
+    """W4A8 MoE forward (MXFP8 activations, MXFP4 weights); returns the
+    routing metadata dict.  H is not kept (a forward-only path)."""
+    E = buf.E
+    ops.mx_quantize(x, ops.MX_E4M3, q=buf.xq, scales=buf.xs)
+    meta = ops.moe_permute(topk_ids, E, x=buf.xq, x_perm=buf.a1_q, workspace=buf.ws)
+    ops.moe_gather(buf.xs, meta["src"], buf.k, out=buf.a1_s)
+    ops.grouped_gemm_w4a8_silu_gate(buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], meta["offsets"], want_y1=False,
+                                    h=buf.h, want_amax=False)
+    ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)
+    ops.grouped_gemm_w4a8(buf.a2_q, buf.a2_s, wq_dn["q"], wq_dn["s"], meta["offsets"], out=buf.y2)
+    ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=topk_w, out=buf.out)
+    return meta

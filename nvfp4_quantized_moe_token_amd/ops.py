@@ -208,6 +208,57 @@ def grouped_gemm_w4a4_silu_gate(a_q, a_s, a_g, b_q, b_s, b_g, offsets, y1=None, 
     return y1, h, amax_out
 
 
+MX_E4M3, MX_E2M1 = _lib.MX_E4M3, _lib.MX_E2M1
+
+
+def mx_quantize(x, elem=MX_E4M3, q=None, scales=None):
+    """MX-quantize a [rows, K] fp32/bf16 tensor (E8M0 scale per 32 along K):
+    elem MX_E4M3 (MXFP8, one byte per element) or MX_E2M1 (MXFP4, packed
+    pairs).  Returns (q, scales)."""
+    _dev(x, q, scales)
+    rows, K = x.shape
+    dev = x.device
+    qcols = K if elem == MX_E4M3 else K // 2
+    q = torch.empty((rows, qcols), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+    rc = _lib.load().mx_quantize(_ptr(x), _DT[x.dtype], rows, K, elem, _ptr(q), _ptr(scales), _stream())
+    _check("mx_quantize", rc)
+    return q, scales
+
+
+def grouped_gemm_w4a8(a_q, a_s, b_q, b_s, offsets, out=None, out_dtype=torch.float32):
+    """C[r] = deq(A)[r] . deq(B_e)^T for rows r of expert e; A MXFP8 [M, K],
+    B MXFP4 [E, N, K/2], E8M0 scales per 32."""
+    _dev(a_q, a_s, b_q, b_s, offsets, out)
+    M, K = a_q.shape
+    E, N = b_q.shape[0], b_q.shape[1]
+    out = torch.empty((M, N), dtype=out_dtype, device=a_q.device) if out is None else out
+    rc = _lib.load().grouped_gemm_w4a8(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), E, M, N, K,
+                                       _ptr(out), _DT[out.dtype], _stream())
+    _check("grouped_gemm_w4a8", rc)
+    return out
+
+
+def grouped_gemm_w4a8_silu_gate(a_q, a_s, b_q, b_s, offsets, y1=None, want_y1=True, h=None, amax_out=None,
+                                want_amax=True):
+    """Gate+up W4A8 GEMM with the SiLU gate (and amax of H) in its epilogue.
+    Returns (y1 or None, h, amax or None)."""
+    _dev(a_q, a_s, b_q, b_s, offsets, y1, h, amax_out)
+    M, K = a_q.shape
+    E, N = b_q.shape[0], b_q.shape[1]
+    F = N // 2
+    dev = a_q.device
+    if y1 is None and want_y1:
+        y1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev) if h is None else h
+    if amax_out is None and want_amax:
+        amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rc = _lib.load().grouped_gemm_w4a8_silu_gate(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), E, M,
+                                                 F, K, _ptr(y1), _ptr(h), _ptr(amax_out), _stream())
+    _check("grouped_gemm_w4a8_silu_gate", rc)
+    return y1, h, amax_out
+
+
 def grouped_gemm_bf16(layout, a, b, offsets, num_experts=None, out=None, out_dtype=torch.float32, accumulate=False):
     """Grouped BF16 GEMM; layout NT / NN / TN as in the C header."""
     _dev(a, b, offsets, out)
