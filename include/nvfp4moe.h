@@ -176,6 +176,26 @@ int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int E, const vo
                       size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream);
 
 /*
+ * moe_permute_nvfp4_noalloc -- moe_permute_nvfp4 for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same results bit for bit.  The histograms and amax parts
+ * live in a library-owned device array of NVFP4MOE_NOALLOC_SCRATCH_BYTES
+ * per GPU, kept until the process ends; no allocation of any kind happens
+ * in the call.  Calls whose moe_permute_workspace_size(T, k, E) exceeds it
+ * return NVFP4MOE_EWORKSPACE before any HIP call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be ordered by the caller.  Nothing in
+ * the array needs clearing between calls.  Errors otherwise as
+ * moe_permute_nvfp4.
+ */
+#define NVFP4MOE_NOALLOC_SCRATCH_BYTES (2u << 20)
+int moe_permute_nvfp4_noalloc(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D,
+                              void* x_perm, const float* amax_in, float* amax_out, uint8_t* q,
+                              uint8_t* scales, float* gscale, int32_t* offsets, int32_t* dest, int32_t* src,
+                              int32_t* status, nvfp4moe_stream_t stream);
+
+/*
  * moe_gather -- out[p] = w[src[p]] * x[src[p] / k] for p < R (w = 1 when
  * topk_w is NULL); rows with src[p] < 0 are written as zeros.  With
  * topk_w == NULL any dtype is copied verbatim (NVFP4MOE_U8 row payloads,

@@ -22,6 +22,8 @@ SIGNATURES = {
                             c_vp, c_size, c_vp, c_vp]),
     "moe_permute_nvfp4": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_size, c_vp, c_vp]),
+    "moe_permute_nvfp4_noalloc": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_gather": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_vp]),
     "moe_scatter": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_int, c_i64, c_int, c_vp, c_int, c_vp]),
     "moe_unpermute": (c_int, [c_vp, c_int, c_vp, c_vp, c_i64, c_int, c_i64, c_vp, c_int, c_vp]),
@@ -48,6 +50,7 @@ NT, NN, TN = 0, 1, 2
 EPI_NONE, EPI_SILU_GATE = 0, 1
 MX_E4M3, MX_E2M1 = 0, 1
 ABI_VERSION = 1
+NOALLOC_SCRATCH_BYTES = 2 << 20
 STATUS_BAD_EXPERT = 1
 
 _LIB = None

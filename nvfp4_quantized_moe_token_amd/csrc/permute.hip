@@ -19,6 +19,8 @@
 //                       assignment is a popcount, never an atomic: the
 //                       result does not depend on scheduling.
 // Out-of-range ids are skipped (dest = -1) and flagged in the status word.
+#include <mutex>
+
 #include "nvfp4_codec.hpp"
 
 namespace nvfp4moe {
@@ -705,10 +707,66 @@ extern "C" int moe_unpermute(const void* y_perm, int y_dtype, const int32_t* des
   return launch_status();
 }
 
+namespace {
+
+// Scratch memory of the allocation-free fused permute-quantize: the
+// per-chunk histograms and the activation-amax parts that the caller's
+// workspace holds otherwise.  Every GPU the library runs on keeps its own
+// copy until the process ends.  Nothing in it must start at zero: each
+// call writes every histogram entry and every amax part it reads.
+constexpr size_t kScratchBytes = NVFP4MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on each device, taken once per device (with
+// that device current) by hipGetSymbolAddress.  The array's own name is a
+// host-side stand-in and is never passed to a kernel.
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4MOE_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4MOE_ELAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return NVFP4MOE_OK;
+}
+
+// The fused permute-quantize with the caller's workspace, or (workspace ==
+// nullptr, use_scratch) with the library's scratch array of this device.
+int permute_nvfp4_impl(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D, void* x_perm,
+                       const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales, float* gscale,
+                       int32_t* offsets, int32_t* dest, int32_t* src, void* workspace, size_t ws_bytes,
+                       bool use_scratch, int32_t* status, nvfp4moe_stream_t stream);
+
+}  // namespace
+
 extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D,
                                  void* x_perm, const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales,
                                  float* gscale, int32_t* offsets, int32_t* dest, int32_t* src, void* workspace,
                                  size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream) {
+  return permute_nvfp4_impl(topk_ids, T, k, E, x, D, x_perm, amax_in, amax_out, q, scales, gscale, offsets, dest,
+                            src, workspace, ws_bytes, false, status, stream);
+}
+
+extern "C" int moe_permute_nvfp4_noalloc(const int32_t* topk_ids, int64_t T, int k, int E, const void* x,
+                                         int64_t D, void* x_perm, const float* amax_in, float* amax_out,
+                                         uint8_t* q, uint8_t* scales, float* gscale, int32_t* offsets,
+                                         int32_t* dest, int32_t* src, int32_t* status, nvfp4moe_stream_t stream) {
+  return permute_nvfp4_impl(topk_ids, T, k, E, x, D, x_perm, amax_in, amax_out, q, scales, gscale, offsets, dest,
+                            src, nullptr, kScratchBytes, true, status, stream);
+}
+
+namespace {
+int permute_nvfp4_impl(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D, void* x_perm,
+                       const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales, float* gscale,
+                       int32_t* offsets, int32_t* dest, int32_t* src, void* workspace, size_t ws_bytes,
+                       bool use_scratch, int32_t* status, nvfp4moe_stream_t stream) {
   if (T < 0 || k < 1 || E < 1 || D < 0) return NVFP4MOE_EINVAL;
   if (E > kMaxExperts || k > 64) return NVFP4MOE_ESHAPE;
   if (!offsets || !gscale || (!amax_in && !amax_out)) return NVFP4MOE_EINVAL;
@@ -721,9 +779,16 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
     return NVFP4MOE_ESHAPE;
   const int64_t R = T * k;
   if (R > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
-  if (ws_bytes < moe_permute_workspace_size(T, k, E) || (R > 0 && !workspace)) return NVFP4MOE_EWORKSPACE;
+  // With the scratch array, a size beyond it is rejected here (EWORKSPACE),
+  // before any HIP call.
+  if (ws_bytes < moe_permute_workspace_size(T, k, E) || (R > 0 && !workspace && !use_scratch))
+    return NVFP4MOE_EWORKSPACE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
+  if (use_scratch && R > 0) {
+    const int rc = scratch_address(&workspace);
+    if (rc != NVFP4MOE_OK) return rc;
+  }
   hipStream_t st = as_stream(stream);
   const float* amax = amax_in ? amax_in : amax_out;
   if (R == 0) {
@@ -752,3 +817,4 @@ extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int 
       reinterpret_cast<uint2*>(q), scales, gscale);
   return launch_status();
 }
+}  // namespace

@@ -132,6 +132,37 @@ def moe_permute_nvfp4(topk_ids, num_experts, x, x_perm=None, want_x_perm=True, a
                 amax=amax_in if amax_in is not None else amax_out)
 
 
+def moe_permute_nvfp4_noalloc(topk_ids, num_experts, x, x_perm=None, want_x_perm=True, amax_in=None,
+                              amax_out=None, q=None, scales=None, gscale=None, status=None):
+    """moe_permute_nvfp4 without a workspace: the library's own per-GPU
+    scratch array holds the histograms (for callers that cannot allocate;
+    every output buffer passed in is written, nothing else is allocated by
+    the library).  Calls on one GPU must not overlap in time."""
+    _dev(topk_ids, x, x_perm, amax_in, amax_out, q, scales, gscale, status)
+    T, k = topk_ids.shape
+    D = x.shape[1]
+    dev = x.device
+    R = T * k
+    offsets = torch.empty((num_experts + 1,), dtype=torch.int32, device=dev)
+    dest = torch.empty((R,), dtype=torch.int32, device=dev)
+    src = torch.empty((R,), dtype=torch.int32, device=dev)
+    if x_perm is None and want_x_perm:
+        x_perm = torch.empty((R, D), dtype=x.dtype, device=dev)
+    q = torch.empty((R, D // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((R, D // 16), dtype=torch.uint8, device=dev) if scales is None else scales
+    gscale = torch.empty((1,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    if amax_in is None and amax_out is None:
+        amax_out = torch.empty((1,), dtype=torch.float32, device=dev)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("moe_permute_nvfp4_noalloc takes bf16 activations")
+    rc = _lib.load().moe_permute_nvfp4_noalloc(_ptr(topk_ids), T, k, num_experts, _ptr(x), D, _ptr(x_perm),
+                                               _ptr(amax_in), _ptr(amax_out), _ptr(q), _ptr(scales), _ptr(gscale),
+                                               _ptr(offsets), _ptr(dest), _ptr(src), _ptr(status), _stream())
+    _check("moe_permute_nvfp4_noalloc", rc)
+    return dict(offsets=offsets, dest=dest, src=src, x_perm=x_perm, q=q, scales=scales, gscale=gscale,
+                amax=amax_in if amax_in is not None else amax_out)
+
+
 def moe_gather(x, src, k, topk_w=None, out=None, out_dtype=None):
     """out[p] = w[src[p]] * x[src[p] // k] (a verbatim row copy when no weights)."""
     _dev(x, src, topk_w, out)

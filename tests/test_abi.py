@@ -212,3 +212,21 @@ def test_ops_refuse_cpu_tensors():
 
 def test_ctypes_pointer_width():
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_noalloc_rejects_sizes_beyond_scratch(lib):
+    # The allocation-free permute-quantize refuses a call whose histograms
+    # would not fit its scratch array, before any HIP call.
+    from nvfp4_quantized_moe_token_amd import _lib
+    T, k, E = 1 << 20, 8, 4096
+    assert lib.moe_permute_workspace_size(T, k, E) > _lib.NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_permute_nvfp4_noalloc(FAKE, T, k, E, FAKE, 64, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, None, None)
+    assert rc == _lib.EWORKSPACE
+    # within the limit the same call passes validation and stops at the
+    # architecture check (no GPU here) or at a NULL pointer
+    assert lib.moe_permute_nvfp4_noalloc(None, 64, 8, 128, FAKE, 64, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, None, None) == _lib.EINVAL
+    text = open(HEADER).read()
+    assert int(re.search(r"#define NVFP4MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(1)) << 20 \
+        == _lib.NOALLOC_SCRATCH_BYTES
