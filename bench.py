@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.0   # dense fp4 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 MFMA (the rate of the scaled MFMA with an 8-bit operand)
 PEAK_HBM_GBS = 8000.0
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP/byte where the two ceilings meet
 PEAK_CLOCK_GHZ = 2.4        # the clock the published MFMA peaks assume
@@ -167,6 +168,86 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
 # faster, but kernels that share the GPU report inflated durations, so the
 # default keeps the step serial for per-kernel rooflines.
 WGRAD_DEPS = {"bf16_tn_down": "gather_dy", "bf16_tn_gate_up": "silu_gate_bwd"}
+
+
+def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
+    """The W4A8 variant (MXFP8 activations x MXFP4 weights on the scaled
+    MFMA) on the same routing and shapes: its forward ops, each bracketed by
+    HIP events over nrep forward passes, and the plain W4A8 gate+up GEMM
+    (bf16 Y1, no epilogue) timed alone.  Expert weights are MX-quantized
+    before the timer (once per optimizer step)."""
+    dev = inp["x"].device
+    wq_gu = moe_layer.quantize_expert_weights_mx(inp["w_gu"])
+    wq_dn = moe_layer.quantize_expert_weights_mx(inp["w_dn"])
+    buf = moe_layer.BuffersW4A8(T, k, E, D, F, dev)
+    box = {}
+
+    def permute():
+        box["m"] = ops.moe_permute(inp["ids"], E, x=buf.xq, x_perm=buf.a1_q, workspace=buf.ws)
+
+    m = lambda: box["m"]  # noqa: E731
+    seq = [
+        ("mx_quantize_x", lambda: ops.mx_quantize(inp["x"], ops.MX_E4M3, q=buf.xq, scales=buf.xs)),
+        ("permute_codes", permute),
+        ("gather_scales", lambda: ops.moe_gather(buf.xs, m()["src"], k, out=buf.a1_s)),
+        ("w4a8_gate_up_silu", lambda: ops.grouped_gemm_w4a8_silu_gate(
+            buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], m()["offsets"], want_y1=False, h=buf.h, want_amax=False)),
+        ("mx_quantize_h", lambda: ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)),
+        ("w4a8_down", lambda: ops.grouped_gemm_w4a8(buf.a2_q, buf.a2_s, wq_dn["q"], wq_dn["s"], m()["offsets"],
+                                                    out=buf.y2)),
+        ("unpermute", lambda: ops.moe_unpermute(buf.y2, m()["dest"], T, k, topk_w=inp["tw"], out=buf.out)),
+    ]
+    for _ in range(3):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    times = {}
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    evs = []
+    t0.record()
+    for _ in range(nrep):
+        for name, fn in seq:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((name, e0, e1))
+    t1.record()
+    torch.cuda.synchronize()
+    for name, e0, e1 in evs:
+        times.setdefault(name, []).append(e0.elapsed_time(e1))
+    times = {n: sum(v) / len(v) for n, v in times.items()}
+    fwd_ms = t0.elapsed_time(t1) / nrep
+    # plain gate+up (bf16 Y1) alone
+    y1 = torch.empty(T * k, 2 * F, dtype=torch.bfloat16, device=dev)
+    plain = lambda: ops.grouped_gemm_w4a8(buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], m()["offsets"], out=y1)  # noqa: E731
+    for _ in range(3):
+        plain()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for _ in range(nrep):
+        plain()
+    b1.record()
+    torch.cuda.synchronize()
+    times["w4a8_gate_up"] = b0.elapsed_time(b1) / nrep
+    f1, f2 = gemm_flops(T * k, D, F)
+    gemm_ms = times["w4a8_gate_up_silu"] + times["w4a8_down"]
+    out = {"forward_ms": round(fwd_ms, 4), "tokens_per_s_forward": round(T / (fwd_ms * 1e-3), 1),
+           "gemm_ms": round(gemm_ms, 4), "tflops": round((f1 + f2) / (gemm_ms * 1e-3) / 1e12, 1)}
+    out["frac_fp8_mfma_peak"] = round(out["tflops"] / PEAK_FP8_TFLOPS, 4)
+    out["frac_bf16_mfma_peak"] = round(out["tflops"] / PEAK_BF16_TFLOPS, 4)
+    ops_out = {}
+    for name, ms in times.items():
+        fl = {"w4a8_gate_up_silu": f1, "w4a8_gate_up": f1, "w4a8_down": f2}.get(name)
+        ent = {"ms": round(ms, 4)}
+        if fl:
+            tf = fl / (ms * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_fp8_mfma_peak=round(tf / PEAK_FP8_TFLOPS, 4),
+                       frac_bf16_mfma_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        ops_out[name] = ent
+    out["ops"] = ops_out
+    return out
 
 
 def run_step(torch, seq, wstream, timed):
@@ -534,6 +615,7 @@ def main():
     ap.add_argument("--workload", default="moe_8k_update",
                     choices=["moe_8k_update", "moe_4k", "moe_16k_skew", "qwen3_4b_up"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 x MXFP4) side measurement")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense qwen3_4b_up W4A4 vs BF16 GEMM side measurement")
     ap.add_argument("--overlap", action="store_true",
@@ -856,6 +938,13 @@ def main():
     w4_ms = sum(per_op[o] for o in w4_ops)
     w4_tflops = (f1 + f2) / (w4_ms * 1e-3) / 1e12
     dense = dense_side(args) if not args.no_dense else None
+    w4a8 = None
+    if not args.no_w4a8:
+        log("w4a8 variant")
+        w4a8 = w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep)
+        w4a8["speedup_gate_up_vs_w4a4"] = round(w4["ms"] / w4a8["ops"]["w4a8_gate_up"]["ms"], 3)
+        w4a8["speedup_gate_up_vs_bf16"] = round(bl["ms"] / w4a8["ops"]["w4a8_gate_up"]["ms"], 3)
+        w4a8["speedup_gemms_vs_w4a4_in_step"] = round(w4_ms / w4a8["gemm_ms"], 3)
     res = {
         "metric": "W4A4 MoE grouped-GEMM TFLOP/s + % MI355X MFMA peak; quantize GB/s",
         "value": round(w4_tflops, 2),
@@ -888,6 +977,7 @@ def main():
                       "bf16_same_shape_tflops": bl.get("tflops"),
                       "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3)},
         "dense_qwen3_4b_up": dense,
+        "w4a8": w4a8,
         "quantize": roofline_of("quantize_x_perm_cold"),
         "quantize_16k": roofline_of("quantize_x_perm_16k_cold"),
         "permute_quantize": roofline_of("permute_quantize_x"),
