@@ -170,6 +170,64 @@ def step_ops(ops, inp, wq_gu, wq_dn, buf, meta_box, backward):
 WGRAD_DEPS = {"bf16_tn_down": "gather_dy", "bf16_tn_gate_up": "silu_gate_bwd"}
 
 
+def delayed_amax_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, T, k, E, D, F, nrep, keep_bf16):
+    """The W4A4 forward with a delayed amax of H (the previous pass's, in a
+    two-slot ping-pong): H is requantized in the gate+up GEMM's epilogue
+    (grouped_gemm_w4a4_silu_gate_nvfp4), so no quantize launch and no bf16 H
+    round trip (bf16 Y1 and H are still stored when keep_bf16, as the BF16
+    backward needs them).  Per-op HIP events over nrep forward passes."""
+    dev = inp["x"].device
+    buf = moe_layer.Buffers(T, k, E, D, F, dev)
+    slots = torch.zeros(2, dtype=torch.float32, device=dev)
+    box = {"i": 0}
+
+    def permute():
+        box["m"] = ops.moe_permute_nvfp4(inp["ids"], E, inp["x"], x_perm=buf.x_perm if keep_bf16 else None,
+                                         want_x_perm=keep_bf16, amax_out=buf.amax[0:1], q=buf.a1_q,
+                                         scales=buf.a1_s, gscale=buf.a1_g, workspace=buf.ws)
+
+    def gate_up():
+        i = box["i"]
+        box["i"] = i + 1
+        ops.grouped_gemm_w4a4_silu_gate_nvfp4(
+            buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], box["m"]["offsets"],
+            slots[i % 2:i % 2 + 1], y1=buf.y1 if keep_bf16 else None, h=buf.h if keep_bf16 else None,
+            amax_out=slots[(i + 1) % 2:(i + 1) % 2 + 1], q_h=buf.a2_q, s_h=buf.a2_s, g_h=buf.a2_g)
+
+    seq = [
+        ("permute_quantize_x", permute),
+        ("w4a4_gate_up_silu_requant", gate_up),
+        ("w4a4_down", lambda: ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"],
+                                                    wq_dn["g"], box["m"]["offsets"], out=buf.y2)),
+        ("unpermute", lambda: ops.moe_unpermute(buf.y2, box["m"]["dest"], T, k, topk_w=inp["tw"], out=buf.out)),
+    ]
+    for _ in range(3):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    evs = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(nrep):
+        for name, fn in seq:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((name, e0, e1))
+    t1.record()
+    torch.cuda.synchronize()
+    times = {}
+    for name, e0, e1 in evs:
+        times.setdefault(name, []).append(e0.elapsed_time(e1))
+    f1, _ = gemm_flops(T * k, D, F)
+    out = {"forward_ms": round(t0.elapsed_time(t1) / nrep, 4), "bf16_y1_h_stored": keep_bf16,
+           "ops": {n: {"ms": round(sum(v) / len(v), 4)} for n, v in times.items()}}
+    g = out["ops"]["w4a4_gate_up_silu_requant"]
+    g["tflops"] = round(f1 / (g["ms"] * 1e-3) / 1e12, 1)
+    return out
+
+
 def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
     """The W4A8 variant (MXFP8 activations x MXFP4 weights on the scaled
     MFMA) on the same routing and shapes: its forward ops, each bracketed by
@@ -938,6 +996,10 @@ def main():
     w4_ms = sum(per_op[o] for o in w4_ops)
     w4_tflops = (f1 + f2) / (w4_ms * 1e-3) / 1e12
     dense = dense_side(args) if not args.no_dense else None
+    log("delayed amax of H")
+    delayed = delayed_amax_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, T, k, E, D, F, nrep, backward)
+    fwd_names = ["permute_quantize_x", "w4a4_gate_up_silu", "quantize_h", "w4a4_down", "unpermute"]
+    delayed["forward_ms_amax_computed"] = round(sum(per_op[n] for n in fwd_names), 4)
     w4a8 = None
     if not args.no_w4a8:
         log("w4a8 variant")
@@ -978,6 +1040,7 @@ def main():
                       "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3)},
         "dense_qwen3_4b_up": dense,
         "w4a8": w4a8,
+        "forward_delayed_amax_h": delayed,
         "quantize": roofline_of("quantize_x_perm_cold"),
         "quantize_16k": roofline_of("quantize_x_perm_16k_cold"),
         "permute_quantize": roofline_of("permute_quantize_x"),

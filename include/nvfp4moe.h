@@ -286,6 +286,31 @@ int grouped_gemm_w4a4_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const fl
                                 nvfp4moe_stream_t stream);
 
 /*
+ * grouped_gemm_w4a4_silu_gate_nvfp4 -- grouped_gemm_w4a4_silu_gate with the
+ * NVFP4 requantization of H in the same epilogue ([JA], fourth paragraph:
+ * op fusion and amax reuse), for a caller that hands in the amax of H (a
+ * delayed amax, e.g. the previous step's, or one agreed otherwise): q_h,
+ * s_h and g_h equal nvfp4_quantize(H, groups = 1, amax_in = amax_h_in) bit
+ * for bit, H being the bf16 SiLU gate that h would receive, so neither Y1
+ * nor H needs to be stored or re-read.  A stale amax saturates, as in
+ * nvfp4_quantize.
+ *   operands, F, K, y1 (nullable) as grouped_gemm_w4a4_silu_gate
+ *   h         [M_total][F] bf16 or NULL (not stored)
+ *   amax_out  [1] fp32 or NULL: max |H| of this call (the next step's
+ *             delayed amax); must not alias amax_h_in
+ *   amax_h_in [1] fp32, device: the amax used for H's global scale
+ *   q_h [M_total][F/2], s_h [M_total][F/16], g_h [1] out (4-byte aligned)
+ * Errors as grouped_gemm_w4a4_silu_gate; EINVAL also for a NULL q_h, s_h,
+ * g_h or amax_h_in, or amax_out == amax_h_in.
+ */
+int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                      const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                      const int32_t* expert_offsets, int E, int64_t M_total, int64_t F,
+                                      int64_t K, void* y1, void* h, float* amax_out,
+                                      const float* amax_h_in, uint8_t* q_h, uint8_t* s_h, float* g_h,
+                                      nvfp4moe_stream_t stream);
+
+/*
  * mx_quantize -- MX quantization for the W4A8 variant, whose activations are
  * MXFP8 ([JA], third paragraph: the activation-precision comparison of
  * W4A16, W4A8 with MXFP8 activations, and W4A4).  The pages do not define MX;

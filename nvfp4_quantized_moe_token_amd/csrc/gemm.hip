@@ -44,7 +44,7 @@
 // at kernel start (up to 1024 experts) for the per-tile lookups.  The plain
 // W4A4 GEMM with bf16 output also loads the next tile's first stage during
 // the current tile's last step (see the kernel).
-#include "common.hpp"
+#include "nvfp4_codec.hpp"
 
 namespace nvfp4moe {
 namespace {
@@ -72,11 +72,14 @@ constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data for
 // W4A4_SILU: the W4A4 gate+up GEMM with the SiLU-gate epilogue.  W4A8:
 // MXFP8 activations x MXFP4 weights on the scaled MFMA (W4A8_SILU: with the
 // SiLU-gate epilogue).
-enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6 };
-constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU; }
+// W4A4_SILU_Q: W4A4_SILU that also requantizes H to NVFP4 in the epilogue
+// (its own instantiation, so that the plain SiLU-gate kernel keeps its
+// registers).
+enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6, W4A4_SILU_Q = 7 };
+constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q; }
 constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU; }
 constexpr bool is_q(int mode) { return is_nv(mode) || is_mx(mode); }
-constexpr bool is_silu(int mode) { return mode == W4A4_SILU || mode == W4A8_SILU; }
+constexpr bool is_silu(int mode) { return mode == W4A4_SILU || mode == W4A8_SILU || mode == W4A4_SILU_Q; }
 
 struct Params {
   const void* a;       // NT/NN/TN: bf16 A; W4A4: packed codes of A
@@ -99,6 +102,12 @@ struct Params {
   int bk;
   int bk_shift;        // log2(bk) when bk is a power of two, else -1
   int64_t b_rows;      // TN with gathered B: rows of B
+  // W4A4_SILU with H requantized in the epilogue (hq != NULL): NVFP4 codes,
+  // scales and global scale of H with the handed-in amax h_amax_in[0].
+  uint8_t* hq;
+  uint8_t* hs;
+  float* hg;
+  const float* h_amax_in;
 };
 
 // ---- small device helpers ----
@@ -957,6 +966,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       // the same features.  Y1 is rounded to bf16 first, so H is the SiLU
       // gate of the stored Y1, as the standalone kernel computes it.
       uint16_t* Hp = reinterpret_cast<uint16_t*>(p.h);
+      // global scale of H for the in-epilogue requantization
+      const float h_g = MODE == W4A4_SILU_Q ? global_scale(p.h_amax_in[0]) : 1.0f;
       const int64_t F = p.N / 2;
       float m = 0.0f;
       // Gate and up of each 32-row block leave through a private LDS region
@@ -1010,7 +1021,33 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
               *reinterpret_cast<uint4*>(C16 + row * ldc + f) = vg;
               *reinterpret_cast<uint4*>(C16 + row * ldc + F + f) = vu;
             }
-            *reinterpret_cast<uint4*>(Hp + row * F + f) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            if (Hp) *reinterpret_cast<uint4*>(Hp + row * F + f) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          }
+          if constexpr (MODE == W4A4_SILU_Q) {
+            {
+              // NVFP4 of H with the handed-in amax, from the stored bf16
+              // values: lanes ch and ch ^ 1 (one row) hold the 16 features
+              // of one block, 8 each; their amax is combined by a shuffle
+              // (every lane of the pair takes it: same row, same validity).
+              float hv[8];
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                hv[2 * w] = bf16_lo(hw[w]);
+                hv[2 * w + 1] = bf16_hi(hw[w]);
+              }
+              float a = 0.0f;
+#pragma unroll
+              for (int i2 = 0; i2 < 8; ++i2) a = fmaxf(a, fabsf(hv[i2]));
+              a = fmaxf(a, __shfl_xor(a, 1, 64));
+              uint32_t sbyte;
+              float d;
+              block_scale(a, h_g, sbyte, d);
+              const uint32_t codes = encode8(hv, d);
+              if (valid) {
+                *reinterpret_cast<uint32_t*>(p.hq + row * (F / 2) + f / 2) = codes;
+                if ((ch & 1) == 0) p.hs[row * (F / 16) + f / 16] = (uint8_t)sbyte;
+              }
+            }
           }
         }
       }
@@ -1124,6 +1161,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   // W4A4_SILU: one atomic per workgroup for the amax of H (every wave of the
   // workgroup leaves the tile loop together).
   if constexpr (SILU) {
+    if (MODE == W4A4_SILU_Q && blockIdx.x == 0 && threadIdx.x == 0) p.hg[0] = global_scale(p.h_amax_in[0]);
     if (p.amax) {
       __shared__ float red[NW];
       const float m = wave_max(silu_amax);
@@ -1138,6 +1176,9 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     }
   }
 }
+
+// Global scale of the in-epilogue requantized H when the GEMM has no rows.
+__global__ void h_gscale_kernel(const float* amax, float* g) { g[0] = global_scale(amax[0]); }
 
 // Resident workgroups per CU of one kernel instantiation (cached; the same on
 // every gfx950 device).
@@ -1273,6 +1314,7 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case W4A4_SILU: return launch_mode<W4A4_SILU>(cfg, p, st);
     case W4A8: return launch_mode<W4A8>(cfg, p, st);
     case W4A8_SILU: return launch_mode<W4A8_SILU>(cfg, p, st);
+    case W4A4_SILU_Q: return launch_mode<W4A4_SILU_Q>(cfg, p, st);
     default: return launch_mode<W4A4>(cfg, p, st);
   }
 }
@@ -1287,22 +1329,28 @@ namespace {
 // Shared by both W4A4 entry points.  silu: c = Y1 (NULL: not stored), h = H.
 int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q, const uint8_t* b_s,
                const float* b_g, const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
-               void* c, int c_dtype, int silu, void* h, float* amax_out, hipStream_t st) {
+               void* c, int c_dtype, int silu, void* h, float* amax_out, hipStream_t st,
+               const float* h_amax_in = nullptr, uint8_t* hq = nullptr, uint8_t* hs = nullptr, float* hg = nullptr) {
+  const bool qh = hq != nullptr;
   if (E < 1 || M_total < 0 || N < 0 || K < 0) return NVFP4MOE_EINVAL;
   if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
   if (silu && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
   if (!expert_offsets || !a_g || !b_g) return NVFP4MOE_EINVAL;
-  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h : !c))) return NVFP4MOE_EINVAL;
+  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h && !qh : !c))) return NVFP4MOE_EINVAL;
+  if (qh && (!h_amax_in || !hs || !hg || (amax_out && amax_out == h_amax_in))) return NVFP4MOE_EINVAL;
   if (K % 64 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
   if (silu && N % 256 != 0) return NVFP4MOE_ESHAPE;
   if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) ||
       !aligned(a_s, 4) || !aligned(b_s, 4) ||
-      !aligned(c, 16) || !aligned(h, 16))
+      !aligned(c, 16) || !aligned(h, 16) || !aligned(hq, 4) || !aligned(hg, 4) || !aligned(h_amax_in, 4))
     return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   if (silu && amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
-  if (M_total == 0 || N == 0) return launch_status();
+  if (M_total == 0 || N == 0) {
+    if (qh) h_gscale_kernel<<<1, 1, 0, st>>>(h_amax_in, hg);
+    return launch_status();
+  }
   Params p = {};
   p.a = a_q;
   p.b = b_q;
@@ -1319,7 +1367,11 @@ int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const u
   p.c_f32 = c_dtype == NVFP4MOE_F32;
   p.h = h;
   p.amax = amax_out;
-  return launch(silu ? W4A4_SILU : W4A4, p, st);
+  p.hq = hq;
+  p.hs = hs;
+  p.hg = hg;
+  p.h_amax_in = h_amax_in;
+  return launch(silu ? (qh ? W4A4_SILU_Q : W4A4_SILU) : W4A4, p, st);
 }
 
 }  // namespace
@@ -1401,6 +1453,18 @@ extern "C" int grouped_gemm_w4a8_silu_gate(const uint8_t* a_q, const uint8_t* a_
   if (F < 0) return NVFP4MOE_EINVAL;
   return w4a8_entry(a_q, a_s, b_q, b_s, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h, amax_out,
                     as_stream(stream));
+}
+
+extern "C" int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                                 const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                                 const int32_t* expert_offsets, int E, int64_t M_total, int64_t F,
+                                                 int64_t K, void* y1, void* h, float* amax_out,
+                                                 const float* amax_h_in, uint8_t* q_h, uint8_t* s_h, float* g_h,
+                                                 nvfp4moe_stream_t stream) {
+  if (F < 0) return NVFP4MOE_EINVAL;
+  if (!q_h) return NVFP4MOE_EINVAL;
+  return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h,
+                    amax_out, as_stream(stream), amax_h_in, q_h, s_h, g_h);
 }
 
 extern "C" int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,

@@ -68,16 +68,33 @@ class Buffers:
             self.dw_gu = e(E, 2 * F, D, dt=f32)
 
 
-def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_y1=True, keep_x_perm=True, fuse_silu=True):
+def forward(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_y1=True, keep_x_perm=True, fuse_silu=True,
+            amax_h_in=None, amax_x_in=None):
     """W4A4 MoE forward; returns the routing metadata dict.  Y1 (buf.y1) is
     written when keep_y1 and the bf16 permuted rows (buf.x_perm) when
     keep_x_perm (the BF16 backward needs Y1, and X_perm unless it gathers
-    from X)."""
+    from X).
+
+    With ``amax_h_in`` (a [1] fp32 device tensor: a delayed amax of H, e.g.
+    the previous step's buf.amax[1]) H is requantized inside the gate+up
+    GEMM's epilogue with that amax; bf16 H is then stored only when keep_y1
+    (the backward needs it), and buf.amax[1] still receives this step's
+    max |H|.  With ``amax_x_in`` ([1] fp32 device) X is quantized with that
+    amax instead of its own (buf.amax[0] is then not written)."""
     E = buf.E
     meta = ops.moe_permute_nvfp4(topk_ids, E, x, x_perm=buf.x_perm if keep_x_perm else None,
-                                 want_x_perm=keep_x_perm, amax_out=buf.amax[0:1], q=buf.a1_q, scales=buf.a1_s,
-                                 gscale=buf.a1_g, workspace=buf.ws)
+                                 want_x_perm=keep_x_perm, amax_in=amax_x_in,
+                                 amax_out=None if amax_x_in is not None else buf.amax[0:1], q=buf.a1_q,
+                                 scales=buf.a1_s, gscale=buf.a1_g, workspace=buf.ws)
     wgu = (wq_gu["q"], wq_gu["s"], wq_gu["g"])
+    if amax_h_in is not None and buf.F % 128 == 0:
+        ops.grouped_gemm_w4a4_silu_gate_nvfp4(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"], amax_h_in,
+                                              y1=buf.y1 if keep_y1 else None, h=buf.h if keep_y1 else None,
+                                              amax_out=buf.amax[1:2], q_h=buf.a2_q, s_h=buf.a2_s, g_h=buf.a2_g)
+        ops.grouped_gemm_w4a4(buf.a2_q, buf.a2_s, buf.a2_g, wq_dn["q"], wq_dn["s"], wq_dn["g"], meta["offsets"],
+                              out=buf.y2)
+        ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=topk_w, out=buf.out)
+        return meta
     if fuse_silu and buf.F % 128 == 0:
         ops.grouped_gemm_w4a4_silu_gate(buf.a1_q, buf.a1_s, buf.a1_g, *wgu, meta["offsets"],
                                         y1=buf.y1 if keep_y1 else None, want_y1=keep_y1, h=buf.h,

@@ -239,6 +239,29 @@ def grouped_gemm_w4a4_silu_gate(a_q, a_s, a_g, b_q, b_s, b_g, offsets, y1=None, 
     return y1, h, amax_out
 
 
+def grouped_gemm_w4a4_silu_gate_nvfp4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, amax_h_in, y1=None, h=None,
+                                      amax_out=None, want_amax=True, q_h=None, s_h=None, g_h=None):
+    """Gate+up W4A4 GEMM with the SiLU gate and the NVFP4 requantization of
+    H (with the handed-in amax_h_in) in its epilogue.  Returns (q_h, s_h,
+    g_h, amax or None); y1 and h are stored only when given."""
+    _dev(a_q, a_s, a_g, b_q, b_s, b_g, offsets, amax_h_in, y1, h, amax_out, q_h, s_h, g_h)
+    M = a_q.shape[0]
+    K = a_q.shape[1] * 2
+    E, N = b_q.shape[0], b_q.shape[1]
+    F = N // 2
+    dev = a_q.device
+    q_h = torch.empty((M, F // 2), dtype=torch.uint8, device=dev) if q_h is None else q_h
+    s_h = torch.empty((M, F // 16), dtype=torch.uint8, device=dev) if s_h is None else s_h
+    g_h = torch.empty((1,), dtype=torch.float32, device=dev) if g_h is None else g_h
+    if amax_out is None and want_amax:
+        amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    rc = _lib.load().grouped_gemm_w4a4_silu_gate_nvfp4(
+        _ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), _ptr(offsets), E, M, F, K, _ptr(y1),
+        _ptr(h), _ptr(amax_out), _ptr(amax_h_in), _ptr(q_h), _ptr(s_h), _ptr(g_h), _stream())
+    _check("grouped_gemm_w4a4_silu_gate_nvfp4", rc)
+    return q_h, s_h, g_h, amax_out
+
+
 MX_E4M3, MX_E2M1 = _lib.MX_E4M3, _lib.MX_E2M1
 
 

@@ -100,3 +100,69 @@ def test_silu_epilogue_no_rows():
     torch.cuda.synchronize()
     assert to_np(amax)[0] == 0.0
     assert (to_np(h) == 3.0).all()
+
+
+@pytest.mark.parametrize("M,F,K,counts", CASES)
+def test_silu_epilogue_requantizes_h_with_handed_in_amax(M, F, K, counts):
+    """H requantized inside the epilogue with a handed-in amax equals
+    nvfp4_quantize(H, amax_in) of the unfused chain, bit for bit -- with the
+    exact amax of H, a larger (stale) one, a smaller one that saturates, and
+    with or without the bf16 Y1 and H stored -- and the oracle's quantize of
+    that H.  amax_out receives max |H| of the call either way."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    a, b, offs, t = _operands(M * 3 + F + K, M, F, K, counts)
+    R = int(offs[-1])
+    y1, h_ref, amax_ref = ops.grouped_gemm_w4a4_silu_gate(*_w(t))
+    torch.cuda.synchronize()
+    amax_h = float(to_np(amax_ref)[0])
+    h_np = to_np(h_ref)[:R]
+    for factor, store in ((1.0, True), (1.5, False), (0.25, False), (1.0, False)):
+        amax_in = torch.tensor([amax_h * factor], dtype=torch.float32, device="cuda")
+        y1s = torch.full_like(y1, 3.0) if store else None
+        hs = torch.full_like(h_ref, 3.0) if store else None
+        q_ref, s_ref, g_ref, _ = ops.nvfp4_quantize(h_ref[:R].contiguous(), amax_in=amax_in)
+        q, s, g, am = ops.grouped_gemm_w4a4_silu_gate_nvfp4(*_w(t), amax_in, y1=y1s, h=hs)
+        torch.cuda.synchronize()
+        assert torch.equal(q[:R], q_ref), (factor, "codes")
+        assert torch.equal(s[:R], s_ref), (factor, "scales")
+        assert to_np(g)[0] == to_np(g_ref)[0]
+        assert to_np(am)[0] == amax_h
+        rq, rs, rg, _ = nvfp4.quantize(h_np, amax=[np.float32(amax_h * factor)])
+        np.testing.assert_array_equal(to_np(q)[:R], rq)
+        np.testing.assert_array_equal(to_np(s)[:R], rs)
+        if store:
+            assert torch.equal(y1s[:R].view(torch.int16), y1[:R].view(torch.int16))
+            assert torch.equal(hs[:R].view(torch.int16), h_ref[:R].view(torch.int16))
+
+
+def test_layer_forward_with_delayed_amax():
+    """moe_layer.forward with amax_h_in: the down GEMM's input is the
+    epilogue's NVFP4 of H, equal to the two-launch path's with the same amax;
+    the output equals that path's output bit for bit."""
+    require_gpu()
+    import workloads
+    from nvfp4_quantized_moe_token_amd import moe_layer, ops
+    T, k, E, D, F = 300, 4, 12, 256, 128
+    d = workloads.moe(T, 1.1, 0.01, 16.0, E=E, k=k, D=D, F=F, name="delayed")
+    x, ids = to_gpu(d["x"], torch.bfloat16), to_gpu(d["topk_ids"], torch.int32)
+    tw = to_gpu(d["topk_w"], torch.float32)
+    wq_gu = moe_layer.quantize_expert_weights(to_gpu(d["w_gu"], torch.bfloat16))
+    wq_dn = moe_layer.quantize_expert_weights(to_gpu(d["w_dn"], torch.bfloat16))
+    dev = torch.device("cuda:0")
+    ref = moe_layer.Buffers(T, k, E, D, F, dev)
+    moe_layer.forward(x, ids, tw, wq_gu, wq_dn, ref, keep_y1=True, keep_x_perm=False)
+    stale = (ref.amax[1:2] * 1.25).contiguous()
+    # the two-launch path with the stale amax
+    q2, s2, g2, _ = ops.nvfp4_quantize(ref.h, amax_in=stale)
+    fused = moe_layer.Buffers(T, k, E, D, F, dev)
+    moe_layer.forward(x, ids, tw, wq_gu, wq_dn, fused, keep_y1=False, keep_x_perm=False, amax_h_in=stale)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.a2_q, q2) and torch.equal(fused.a2_s, s2) and torch.equal(fused.a2_g, g2)
+    assert to_np(fused.amax)[1] == to_np(ref.amax)[1]
+    meta = ops.moe_permute(ids, E)
+    y2 = ops.grouped_gemm_w4a4(q2, s2, g2, wq_dn["q"], wq_dn["s"], wq_dn["g"], meta["offsets"],
+                               out_dtype=torch.bfloat16)
+    out = ops.moe_unpermute(y2, meta["dest"], T, k, topk_w=tw)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.out.view(torch.int16), out.view(torch.int16))
