@@ -69,3 +69,59 @@ def test_token_outputs_do_not_depend_on_the_batch():
     assert torch.equal(m_a["q"][dest_a], m_b["q"][dest_b])
     assert torch.equal(m_a["scales"][dest_a], m_b["scales"][dest_b])
     assert torch.equal(h_a[dest_a].view(torch.int16), h_b[dest_b].view(torch.int16))
+
+
+def test_probe_tokens_bit_identical_across_workload_routings():
+    """64 probe tokens (their rows, routing and upstream gradient) embedded
+    at seeded positions in the moe_4k, moe_16k_skew and moe_8k_update
+    batches -- unbiased, Zipf 1.1 and Zipf 1.6 routings of 4096, 16384 and
+    8192 tokens over the same 128 experts -- with amax_X and amax_H held
+    fixed: the probes' NVFP4 codes and scales of X and H, their bf16 H rows,
+    their layer outputs and their dX rows from the BF16 backward are
+    identical bit for bit in the three runs, although their rows land at
+    other offsets, in other row blocks and tiles.  The full layer step runs
+    as the benchmark launches it (fused permute-quantize with amax_in, the
+    gate+up GEMM with the SiLU gate and the NVFP4 of H in its epilogue, the
+    BF16 backward)."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import moe_layer
+    P = 64
+    base = workloads.moe_8k_update()
+    E, k, D, F = base["E"], base["k"], base["D"], base["F"]
+    rng = np.random.default_rng(11)
+    probe = workloads.moe(P, 0.0, 0.02, 24.0, with_dy=True, seed=99, E=E, k=k, D=D, F=F, weights=False,
+                          name="probe")
+    batches = [workloads.moe_4k(weights=False), workloads.moe_16k_skew(weights=False), base]
+    w_gu, w_dn = to_gpu(base["w_gu"], torch.bfloat16), to_gpu(base["w_dn"], torch.bfloat16)
+    wq_gu = moe_layer.quantize_expert_weights(w_gu)
+    wq_dn = moe_layer.quantize_expert_weights(w_dn)
+    amax_x = torch.tensor([256.0], dtype=torch.float32, device="cuda")   # above every |x| of the batches
+    amax_h = torch.tensor([2.0], dtype=torch.float32, device="cuda")
+    dev = torch.device("cuda:0")
+    seen = []
+    for d in batches:
+        T = d["T"]
+        assert np.abs(d["x"]).max() <= 256.0
+        pos = np.sort(rng.choice(T, P, replace=False))
+        x, ids, tw = d["x"].copy(), d["topk_ids"].copy(), d["topk_w"].copy()
+        dy = d["dy"].copy() if "dy" in d else np.zeros((T, D), np.float32)
+        x[pos], ids[pos], tw[pos], dy[pos] = probe["x"], probe["topk_ids"], probe["topk_w"], probe["dy"]
+        buf = moe_layer.Buffers(T, k, E, D, F, dev, backward=True)
+        xg, twg = to_gpu(x, torch.bfloat16), to_gpu(tw, torch.float32)
+        meta = moe_layer.forward(xg, to_gpu(ids, torch.int32), twg, wq_gu, wq_dn, buf, amax_x_in=amax_x,
+                                 amax_h_in=amax_h)
+        moe_layer.backward(to_gpu(dy, torch.bfloat16), twg, w_gu, w_dn, meta, buf)
+        torch.cuda.synchronize()
+        p = torch.from_numpy(pos).cuda()
+        rows = meta["dest"].view(T, k)[p].reshape(-1).long()
+        seen.append(dict(rows=rows.cpu(), a1_q=buf.a1_q[rows].cpu(), a1_s=buf.a1_s[rows].cpu(),
+                         h=buf.h[rows].view(torch.int16).cpu(), a2_q=buf.a2_q[rows].cpu(),
+                         a2_s=buf.a2_s[rows].cpu(), out=buf.out[p].view(torch.int16).cpu(),
+                         dx=buf.dx[p].view(torch.int16).cpu(), gs=(buf.a1_g.cpu(), buf.a2_g.cpu())))
+        del buf
+    ref = seen[0]
+    for other in seen[1:]:
+        assert not torch.equal(other["rows"], ref["rows"]), "probe rows must land elsewhere"
+        for key in ("a1_q", "a1_s", "h", "a2_q", "a2_s", "out", "dx"):
+            assert torch.equal(other[key], ref[key]), key
+        assert torch.equal(other["gs"][0], ref["gs"][0]) and torch.equal(other["gs"][1], ref["gs"][1])
