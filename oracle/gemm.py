@@ -134,3 +134,26 @@ def brute_force_matmul_nt(A, B):
                 acc += float(A[i][kk]) * float(B[j][kk])
             C[i][j] = acc
     return np.array(C, dtype=np.float64).reshape(M, N)
+
+
+def grouped_gemm_w4a4_wgrad(a_cols, a_g, b_cols, b_g):
+    """The NVFP4 weight gradient: for each expert e,
+    C_e[i, j] = a_g * b_g * sum_r deq(A_e^T)[i, r] * deq(B_e^T)[j, r],
+    the reduction over the expert's rows r, both operands quantized column-
+    wise (nvfp4.quantize_colwise: blocks of 16 rows of one column, a
+    segment's padding encodes zeros).  a_cols / b_cols: per-expert lists of
+    (q [N1 or N2, L_e/2], s [., L_e/16]).  An empty expert gives zeros.
+    Returns (C fp64 [E, N1, N2], absbound)."""
+    E = len(a_cols)
+    N1, N2 = a_cols[0][0].shape[0], b_cols[0][0].shape[0]
+    C = np.zeros((E, N1, N2))
+    AB = np.zeros_like(C)
+    for e in range(E):
+        (aq, as_), (bq, bs) = a_cols[e], b_cols[e]
+        if aq.shape[1] == 0:
+            continue
+        A = nvfp4.dequantize(aq, as_, np.asarray(a_g, np.float32).reshape(1))
+        B = nvfp4.dequantize(bq, bs, np.asarray(b_g, np.float32).reshape(1))
+        C[e] = A @ B.T
+        AB[e] = np.abs(A) @ np.abs(B).T
+    return C, AB

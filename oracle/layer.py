@@ -197,3 +197,74 @@ def backward(fwd, dy, topk_w, w_gu, w_dn):
         v, _ = backward_stage(name, s, dy, topk_w, w_gu, w_dn, off, dest, src)
         s[name] = _store(name, v)
     return {n: s[n] for n in BACKWARD_STAGES}
+
+
+# ---- the NVFP4 backward variant ----
+#
+# The learner's backward of the pages runs in BF16 ("miniTE報告、NVFP4強化学
+# 習の安定性を検証", first paragraph); the headline 1.39x of "miniTE ускоряет
+# RL в NVFP4 на B300" is read as possibly including quantized backward GEMMs.
+# This variant keeps the BF16 backward's wiring and replaces its four grouped
+# GEMMs with W4A4 ones:
+#   data gradients  dh = dy2 . Wdn_e, dx_perm = dy1 . Wgu_e: NT W4A4 with
+#                   the gradient quantized row-wise (along the contraction
+#                   over the projection's output features) and the weight
+#                   quantized along its input dimension (Wdn_e^T, Wgu_e^T);
+#   weight grads    dw_dn_e = dy2_e^T . h_e, dw_gu_e = dy1_e^T . x_perm_e:
+#                   both operands quantized column-wise (16 consecutive rows
+#                   of one column per block, inside the expert's segment).
+# Amax reuse: each gradient's amax is taken once (at its row-wise
+# quantization) and reused by its column-wise one; h and x_perm reuse the
+# forward's amax_h and amax_x; the transposed weights reuse the per-expert
+# amax of the forward's weights (the same values).
+
+NVFP4_BACKWARD_STAGES = ("dy2", "a_dy2", "dh", "dw_dn", "dy1", "a_dy1", "dx_perm", "dw_gu", "dx")
+
+
+def quantize_weights_t(w):
+    """NVFP4 of stacked expert weights transposed per expert ([E, N, K] ->
+    codes of [E, K, N], blocks along N), one global scale per expert from
+    the expert's amax (the same as the untransposed weight's)."""
+    return quantize_weights(np.ascontiguousarray(np.transpose(np.asarray(w, np.float32), (0, 2, 1))))
+
+
+def backward_nvfp4_stage(name, s, dy, topk_w, wt_gu, wt_dn, offsets, dest, src, rows=None):
+    """One stage of the NVFP4 backward from the stored tensors in ``s``
+    (forward: x_perm, y1, h, amax_x, amax_h; backward: dy2, amax_dy2, a_dy2,
+    dh, dy1, amax_dy1, a_dy1, dx_perm).  wt_gu / wt_dn: quantize_weights_t of
+    the bf16 weights.  ``rows`` as in backward_stage.  Returns (value,
+    bound) like backward_stage; the quantize stages return (q, scales, g)."""
+    k = np.asarray(topk_w).shape[1]
+    if name in ("dy2", "dy1", "dx"):
+        return backward_stage(name, s, dy, topk_w, None, None, offsets, dest, src, rows=rows)
+    if name == "a_dy2":
+        q, sc, g, _ = nvfp4.quantize(s["dy2"], amax=[s["amax_dy2"]])
+        return (q, sc, g), None
+    if name == "a_dy1":
+        q, sc, g, _ = nvfp4.quantize(s["dy1"], amax=[s["amax_dy1"]])
+        return (q, sc, g), None
+    if name == "dh":
+        return _rowwise_w4a4(s["a_dy2"], wt_dn, offsets, rows)
+    if name == "dx_perm":
+        return _rowwise_w4a4(s["a_dy1"], wt_gu, offsets, rows)
+    if name in ("dw_dn", "dw_gu"):
+        ga, gb = ("dy2", "h") if name == "dw_dn" else ("dy1", "x_perm")
+        amax_a = s["amax_" + ga]
+        amax_b = s["amax_h"] if gb == "h" else s["amax_x"]
+        ca, g_a = nvfp4.quantize_colwise(s[ga], offsets, amax_a)
+        cb, g_b = nvfp4.quantize_colwise(s[gb], offsets, amax_b)
+        return gemm.grouped_gemm_w4a4_wgrad(ca, g_a, cb, g_b)
+    raise ValueError(name)
+
+
+def backward_nvfp4(fwd, dy, topk_w, wt_gu, wt_dn):
+    """NVFP4 backward of ``forward``: the stages above in order, each gradient's
+    amax taken from its bf16 values once."""
+    off, dest, src = fwd["offsets"], fwd["dest"], fwd["src"]
+    s = {n: fwd[n] for n in ("x_perm", "y1", "h", "amax_x", "amax_h")}
+    for name in NVFP4_BACKWARD_STAGES:
+        v, _ = backward_nvfp4_stage(name, s, dy, topk_w, wt_gu, wt_dn, off, dest, src)
+        s[name] = _store(name, v) if name not in ("a_dy2", "a_dy1") else v
+        if name in ("dy2", "dy1"):
+            s["amax_" + name] = np.float32(np.abs(s[name]).max()) if s[name].size else np.float32(0)
+    return {n: s[n] for n in NVFP4_BACKWARD_STAGES + ("amax_dy2", "amax_dy1")}

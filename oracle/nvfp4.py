@@ -170,3 +170,50 @@ def dequantize(q, scales, g, groups=1):
     g = np.asarray(g, dtype=np.float32).astype(np.float64).reshape(groups)
     g_row = np.repeat(g, rows // groups)[:, None]
     return e2m1_decode(codes) * np.repeat(s, BLOCK, axis=1) * g_row
+
+
+def segment_pad_offset(offsets):
+    """Column of each expert's segment in the transposed (column-wise)
+    layout: 64 * (floor(off_e / 64) + e), so that a segment padded to a
+    multiple of 64 never reaches the next one, with no prefix sum over the
+    padded counts.  Returns int64 [E]."""
+    off = np.asarray(offsets, dtype=np.int64)
+    e = np.arange(off.size - 1, dtype=np.int64)
+    return 64 * (off[:-1] // 64 + e)
+
+
+def padded_extent(M_total, E):
+    """Length of the transposed layout's rows: 64 * (floor(M_total / 64) + E)."""
+    return 64 * (int(M_total) // 64 + int(E))
+
+
+def quantize_colwise(x, offsets, amax):
+    """Column-wise NVFP4 of a row-grouped tensor (the reduction operand of a
+    weight-gradient GEMM): within each expert's row segment [off_e,
+    off_e+1), 16 consecutive rows of one column form a block, the segment's
+    tail block padded with zeros; one global scale from ``amax`` (the
+    tensor's amax, reused from its row-wise quantization).
+
+    The gradient tensors of the NVFP4 backward are rounded like every other
+    NVFP4 tensor here (the same Q1-Q7, round to nearest even): the pages do
+    not say how the gradients are rounded.
+
+    Equivalent, segment by segment, to quantize(X_e^T padded to a multiple
+    of 16 columns, amax).  Returns a list of (q_e [N, L_e/2], s_e [N,
+    L_e/16]) with L_e = cnt_e rounded up to 16, and g [1].
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    off = np.asarray(offsets, dtype=np.int64)
+    N = x.shape[1]
+    out = []
+    g = None
+    for e in range(off.size - 1):
+        seg = x[off[e]:off[e + 1]]
+        L = -(-seg.shape[0] // BLOCK) * BLOCK
+        xt = np.zeros((N, L), np.float32)
+        xt[:, :seg.shape[0]] = seg.T
+        q, s, g, _ = quantize(xt, amax=[amax])
+        out.append((q, s))
+    if g is None:
+        g = global_scale(np.float32(amax)).reshape(1)
+    return out, g
