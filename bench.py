@@ -228,6 +228,75 @@ def delayed_amax_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, T, k, E, D, F, n
     return out
 
 
+def nvfp4_backward_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, buf, meta_box, T, k, E, D, F, nrep):
+    """The NVFP4 backward variant after the step's forward (whose buffers it
+    reads): every op bracketed by HIP events over nrep backward passes.
+    Transposed weight quantization is done before the timer (once per
+    optimizer step)."""
+    dev = inp["x"].device
+    wt_gu = moe_layer.quantize_expert_weights_t(inp["w_gu"], amax=wq_gu["amax"])
+    wt_dn = moe_layer.quantize_expert_weights_t(inp["w_dn"], amax=wq_dn["amax"])
+    nb = moe_layer.NVFP4BackwardBuffers(T, k, E, D, F, dev)
+    m = meta_box["m"]
+    off = m["offsets"]
+    R = T * k
+    seq = [
+        ("gather_dy", lambda: ops.moe_scatter(inp["dy"], m["dest"], off, k, topk_w=inp["tw"], out=buf.dy2)),
+        ("quantize_dy2", lambda: ops.nvfp4_quantize(buf.dy2, amax_out=nb.amax[0:1], q=nb.a_dy2[0],
+                                                    scales=nb.a_dy2[1], gscale=nb.a_dy2[2])),
+        ("w4a4_dgrad_down", lambda: ops.grouped_gemm_w4a4(*nb.a_dy2, wt_dn["q"], wt_dn["s"], wt_dn["g"], off,
+                                                          out=buf.dh)),
+        ("silu_gate_bwd", lambda: ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)),
+        ("colwise_dy2", lambda: ops.nvfp4_quantize_colwise(buf.dy2, off, nb.amax[0:1], Kp=nb.Kp, q_t=nb.c_dy2[0],
+                                                           s_t=nb.c_dy2[1], gscale=nb.c_dy2[2])),
+        ("colwise_h", lambda: ops.nvfp4_quantize_colwise(buf.h, off, buf.amax[1:2], Kp=nb.Kp, q_t=nb.c_h[0],
+                                                         s_t=nb.c_h[1], gscale=nb.c_h[2])),
+        ("w4a4_wgrad_down", lambda: ops.grouped_gemm_w4a4_wgrad(nb.c_dy2, nb.c_h, off, R, out=buf.dw_dn)),
+        ("quantize_dy1", lambda: ops.nvfp4_quantize(buf.dy1, amax_out=nb.amax[1:2], q=nb.a_dy1[0],
+                                                    scales=nb.a_dy1[1], gscale=nb.a_dy1[2])),
+        ("w4a4_dgrad_gate_up", lambda: ops.grouped_gemm_w4a4(*nb.a_dy1, wt_gu["q"], wt_gu["s"], wt_gu["g"], off,
+                                                             out=buf.dx_perm)),
+        ("unpermute_dx", lambda: ops.moe_unpermute(buf.dx_perm, m["dest"], T, k, topk_w=None, out=buf.dx)),
+        ("colwise_dy1", lambda: ops.nvfp4_quantize_colwise(buf.dy1, off, nb.amax[1:2], Kp=nb.Kp, q_t=nb.c_dy1[0],
+                                                           s_t=nb.c_dy1[1], gscale=nb.c_dy1[2])),
+        ("colwise_x", lambda: ops.nvfp4_quantize_colwise(buf.x_perm, off, buf.amax[0:1], Kp=nb.Kp, q_t=nb.c_x[0],
+                                                         s_t=nb.c_x[1], gscale=nb.c_x[2])),
+        ("w4a4_wgrad_gate_up", lambda: ops.grouped_gemm_w4a4_wgrad(nb.c_dy1, nb.c_x, off, R, out=buf.dw_gu)),
+    ]
+    for _ in range(2):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    evs = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(nrep):
+        for name, fn in seq:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((name, e0, e1))
+    t1.record()
+    torch.cuda.synchronize()
+    times = {}
+    for name, e0, e1 in evs:
+        times.setdefault(name, []).append(e0.elapsed_time(e1))
+    f1, f2 = gemm_flops(R, D, F)
+    fl = {"w4a4_dgrad_down": f2, "w4a4_wgrad_down": f2, "w4a4_dgrad_gate_up": f1, "w4a4_wgrad_gate_up": f1}
+    ops_out = {}
+    for n, v in times.items():
+        ms = sum(v) / len(v)
+        ent = {"ms": round(ms, 4)}
+        if n in fl:
+            ent["tflops"] = round(fl[n] / (ms * 1e-3) / 1e12, 1)
+            ent["frac_bf16_mfma_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+        ops_out[n] = ent
+    gemm_ms = sum(ops_out[n]["ms"] for n in fl)
+    return {"backward_ms": round(t0.elapsed_time(t1) / nrep, 4), "gemm_ms": round(gemm_ms, 4),
+            "gemm_tflops": round(2 * (f1 + f2) / (gemm_ms * 1e-3) / 1e12, 1), "ops": ops_out}
+
+
 def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
     """The W4A8 variant (MXFP8 activations x MXFP4 weights on the scaled
     MFMA) on the same routing and shapes: its forward ops, each bracketed by
@@ -674,6 +743,7 @@ def main():
                     choices=["moe_8k_update", "moe_4k", "moe_16k_skew", "qwen3_4b_up"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8 (MXFP8 x MXFP4) side measurement")
+    ap.add_argument("--no-nvfp4-backward", action="store_true", help="skip the NVFP4 backward side measurement")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense qwen3_4b_up W4A4 vs BF16 GEMM side measurement")
     ap.add_argument("--overlap", action="store_true",
@@ -996,6 +1066,14 @@ def main():
     w4_ms = sum(per_op[o] for o in w4_ops)
     w4_tflops = (f1 + f2) / (w4_ms * 1e-3) / 1e12
     dense = dense_side(args) if not args.no_dense else None
+    nvbwd = None
+    if backward and not args.no_nvfp4_backward:
+        log("nvfp4 backward variant")
+        nvbwd = nvfp4_backward_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, buf, meta_box, T, k, E, D, F, nrep)
+        bwd_names = ["gather_dy", "bf16_nn_down", "silu_gate_bwd", "bf16_tn_down", "bf16_nn_gate_up",
+                     "unpermute_dx", "bf16_tn_gate_up"]
+        nvbwd["bf16_backward_ms_in_step"] = round(sum(per_op[n] for n in bwd_names), 4)
+        nvbwd["bf16_backward_gemm_ms_in_step"] = round(sum(per_op[n] for n in bwd_names if n.startswith("bf16_")), 4)
     log("delayed amax of H")
     delayed = delayed_amax_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, T, k, E, D, F, nrep, backward)
     fwd_names = ["permute_quantize_x", "w4a4_gate_up_silu", "quantize_h", "w4a4_down", "unpermute"]
@@ -1041,6 +1119,7 @@ def main():
         "dense_qwen3_4b_up": dense,
         "w4a8": w4a8,
         "forward_delayed_amax_h": delayed,
+        "nvfp4_backward": nvbwd,
         "quantize": roofline_of("quantize_x_perm_cold"),
         "quantize_16k": roofline_of("quantize_x_perm_16k_cold"),
         "permute_quantize": roofline_of("permute_quantize_x"),

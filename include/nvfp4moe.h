@@ -311,6 +311,71 @@ int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8_t* a_s, co
                                       nvfp4moe_stream_t stream);
 
 /*
+ * The NVFP4 backward variant.  The learner backward of [JA] (first
+ * paragraph) is BF16 (grouped_gemm_bf16 below); the headline learner speed-up
+ * of [RU] (intro, key-facts list) is read as possibly including quantized
+ * backward GEMMs.  This variant keeps the BF16 backward's dataflow and runs
+ * its four grouped GEMMs as W4A4:
+ *   dH = dY2 . Wdn_e, dX_perm = dY1 . Wgu_e   grouped_gemm_w4a4 with the
+ *        gradient quantized by nvfp4_quantize (along its columns) and the
+ *        weights by nvfp4_quantize_transposed;
+ *   dWdn_e = dY2_e^T . H_e, dWgu_e = dY1_e^T . X_perm_e   grouped_gemm_w4a4_wgrad
+ *        on operands quantized by nvfp4_quantize_colwise.
+ * Gradients are rounded like every NVFP4 tensor (RNE; the pages do not say).
+ *
+ * nvfp4_quantize_colwise -- column-wise NVFP4 of a row-grouped bf16 tensor:
+ * within each expert's row segment [offsets[e], offsets[e+1]), 16
+ * consecutive rows of one column form a block (E4M3 scale, E2M1 codes, the
+ * steps of nvfp4_quantize); the segment's tail is zero-padded.  Stored
+ * transposed: column n of x becomes row n of q_t / s_t, expert e's segment
+ * starting at column poff_e = 64 * (floor(offsets[e] / 64) + e), padded with
+ * zero blocks to a multiple of 64 (it never reaches poff_{e+1}).  One global
+ * scale g = amax_in[0] / 2688 (amax reuse: the tensor's amax, e.g. from its
+ * row-wise quantization; 1 when 0).
+ *   x        [M_total][N] bf16, 16-byte aligned; N % 8 == 0.
+ *   offsets  [E+1] int32 on the device (as produced by moe_permute).
+ *   q_t      [N][Kp/2] out (16-byte aligned), s_t [N][Kp/16] out (4-byte
+ *            aligned); columns outside the padded segments are not written.
+ *   Kp       row length of q_t/s_t: Kp % 64 == 0, Kp >= 64*(M_total/64 + E).
+ *   gscale   [1] out.
+ * Errors: EINVAL (NULL, negative, dtype other than BF16), ESHAPE (N % 8,
+ * Kp, alignment).
+ */
+int nvfp4_quantize_colwise(const void* x, int x_dtype, int64_t M_total, int64_t N,
+                           const int32_t* expert_offsets, int E, const float* amax_in, uint8_t* q_t,
+                           uint8_t* s_t, float* gscale, int64_t Kp, nvfp4moe_stream_t stream);
+
+/*
+ * nvfp4_quantize_transposed -- NVFP4 of stacked bf16 matrices quantized
+ * along their rows' index: x [groups][L][N] gives the codes of each
+ * transposed matrix, q_t [groups][N][L/2], s_t [groups][N][L/16], blocks of
+ * 16 consecutive rows of one column, one global scale per group (for the
+ * expert weights of the data-gradient GEMMs: W^T_e, whose amax is that of
+ * W_e, so amax_in may be the forward weights' amax).  amax_in [groups] or
+ * NULL (then computed into amax_out).  L % 64 == 0, N % 8 == 0; x, q_t
+ * 16-byte aligned.  Errors as nvfp4_quantize.
+ */
+int nvfp4_quantize_transposed(const void* x, int x_dtype, int64_t groups, int64_t L, int64_t N,
+                              const float* amax_in, float* amax_out, uint8_t* q_t, uint8_t* s_t,
+                              float* gscale, nvfp4moe_stream_t stream);
+
+/*
+ * grouped_gemm_w4a4_wgrad -- the NVFP4 weight gradient over the contiguous
+ * per-expert layout:
+ *   C_e[i][j] = a_g * b_g * sum over rows r of expert e of deq(A)[r][i] * deq(B)[r][j]
+ * with A and B given column-wise (nvfp4_quantize_colwise with the same
+ * offsets and Kp): a_q [N1][Kp/2], a_s [N1][Kp/16], a_g [1]; b_q [N2][Kp/2],
+ * b_s [N2][Kp/16], b_g [1].  c [E][N1][N2] F32 (or BF16); an empty expert
+ * gives zeros.  fp32 accumulation.  N1 % 32 == 0, N2 % 32 == 0, Kp as for
+ * nvfp4_quantize_colwise; N1*Kp/2 and N2*Kp/2 < 2^31.  Errors: EINVAL,
+ * ESHAPE.
+ */
+int grouped_gemm_w4a4_wgrad(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q,
+                            const uint8_t* b_s, const float* b_g, const int32_t* expert_offsets, int E,
+                            int64_t M_total, int64_t Kp, int64_t N1, int64_t N2, void* c, int c_dtype,
+                            nvfp4moe_stream_t stream);
+
+/*
  * mx_quantize -- MX quantization for the W4A8 variant, whose activations are
  * MXFP8 ([JA], third paragraph: the activation-precision comparison of
  * W4A16, W4A8 with MXFP8 activations, and W4A4).  The pages do not define MX;

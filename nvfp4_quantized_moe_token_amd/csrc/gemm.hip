@@ -75,8 +75,15 @@ constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data for
 // W4A4_SILU_Q: W4A4_SILU that also requantizes H to NVFP4 in the epilogue
 // (its own instantiation, so that the plain SiLU-gate kernel keeps its
 // registers).
-enum Mode { NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6, W4A4_SILU_Q = 7 };
-constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q; }
+// W4A4_TN: the NVFP4 weight gradient, C_e = A_e^T . B_e reduced over the
+// rows of expert e, both operands quantized column-wise (stored transposed:
+// K-major rows whose reduction index runs over the expert's padded segment).
+enum Mode {
+  NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6, W4A4_SILU_Q = 7,
+  W4A4_TN = 8
+};
+constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q || mode == W4A4_TN; }
+constexpr bool is_tn(int mode) { return mode == TN_BF16 || mode == W4A4_TN; }
 constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU; }
 constexpr bool is_q(int mode) { return is_nv(mode) || is_mx(mode); }
 constexpr bool is_silu(int mode) { return mode == W4A4_SILU || mode == W4A8_SILU || mode == W4A4_SILU_Q; }
@@ -90,7 +97,8 @@ struct Params {
   const float* bg;     // W4A4: global scales of B [E]
   const int32_t* offsets;
   void* c;
-  int64_t M, N, K;     // TN: K = columns of A (rows of C_e)
+  int64_t M, N, K;     // TN: K = columns of A (rows of C_e); W4A4_TN: K = rows of the transposed A
+  int64_t kp;          // W4A4_TN: row length (padded reduction extent) of both transposed operands
   int E;
   int c_f32;
   int accumulate;
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
 
   // Real tile count, then this XCD's contiguous share of it.
   int64_t total;
-  if (MODE == TN_BF16) {
+  if (is_tn(MODE)) {
     total = (int64_t)p.E * p.k_tiles_tn * p.n_tiles;
   } else {
     if (wid == 0) {
@@ -618,8 +626,9 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     int64_t n0;
     int64_t red;        // reduction length
     int lo = 0;         // TN: first row of the expert
+    int64_t poff = 0;   // W4A4_TN: the expert's first column in the transposed operands
     lds_barrier();      // previous tile: every wave is done with LDS and s_tile
-    if (MODE == TN_BF16) {
+    if (is_tn(MODE)) {
       const int per_e = p.k_tiles_tn * p.n_tiles;
       expert = (int)(L / per_e);
       const int rem = (int)(L % per_e);
@@ -632,6 +641,11 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       else
         expert_range(p.offsets, expert, p.M, lo, hi);
       red = hi - lo;
+      if (MODE == W4A4_TN) {
+        // the segment is zero-padded to a multiple of 64 columns
+        poff = 64 * ((int64_t)lo / 64 + expert);
+        red = (red + 63) / 64 * 64;
+      }
     } else if (PF && pre) {
       // Found (and its first stage loaded) during the previous tile.
       expert = nx_e;
@@ -667,6 +681,12 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + m0 * p.K, (m_end - m0) * p.K * 2);
     } else if constexpr (MODE == TN_BF16) {
       ra = make_rsrc(reinterpret_cast<const uint16_t*>(p.a) + (int64_t)lo * p.K, red * p.K * 2);
+    } else if constexpr (MODE == W4A4_TN) {
+      // rows m0.. of the transposed A from column poff: codes kp/2 and
+      // scales kp/16 bytes per row
+      ra = make_rsrc(reinterpret_cast<const uint8_t*>(p.a) + m0 * (p.kp / 2) + poff / 2,
+                     (p.K - m0) * (p.kp / 2) - poff / 2);
+      rsa = make_rsrc(p.as + m0 * (p.kp / 16) + poff / 16, (p.K - m0) * (p.kp / 16) - poff / 16);
     } else {
       nv_a_regions<MX>(p, m0, m_end, ra, rsa);
     }
@@ -678,6 +698,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     } else if constexpr (MODE == TN_BF16) {
       rb = p.bsrc ? make_rsrc(p.b, p.b_rows * p.N * 2)
                   : make_rsrc(reinterpret_cast<const uint16_t*>(p.b) + (int64_t)lo * p.N, red * p.N * 2);
+    } else if constexpr (MODE == W4A4_TN) {
+      rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + n0 * (p.kp / 2) + poff / 2,
+                     (p.N - n0) * (p.kp / 2) - poff / 2);
+      rsb = make_rsrc(p.bs + n0 * (p.kp / 16) + poff / 16, (p.N - n0) * (p.kp / 16) - poff / 16);
     } else {
       nv_b_regions<BN, SILU, MX>(p, expert, n0, rb, rsb);
     }
@@ -715,9 +739,13 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
       } else {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
-        // bf16 tile of 64 16-bit units per row.
-        KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 4, k0 / 4, p.K / 4);
-        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
+        // bf16 tile of 64 16-bit units per row.  W4A4_TN rows are kp long
+        // and hold `red` reduction elements of this expert.
+        const int64_t qld = MODE == W4A4_TN ? p.kp / 4 : p.K / 4;
+        const int64_t qlim = MODE == W4A4_TN ? red / 4 : p.K / 4;
+        KMajorLoader<BM, NW>::load(st, wid, ra_, qld, k0 / 4, qlim);
+        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, qld, k0 / 4, qlim, gate_f, j0_);
+        const int64_t sld = MODE == W4A4_TN ? p.kp / 16 : p.K / 16;
         // Scales: 16 bytes per row, 64 rows per load, A rows first.
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
@@ -725,7 +753,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
           const bool is_a = idx * 64 < BM;
           const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
           const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
-          dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * (p.K / 16) + k0 / 16));
+          dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * sld + k0 / 16));
         }
       }
     };
@@ -774,7 +802,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // of an expert is partly empty) skips its MFMAs; it still loads and
     // takes part in every barrier.
     int n_active = FM;
-    if (MODE != TN_BF16 && m_end - m0 <= wm * WTM) n_active = 0;
+    if (!is_tn(MODE) && m_end - m0 <= wm * WTM) n_active = 0;
     if (MODE == TN_BF16 && p.bsrc) {
       // Row indices of the first S - 1 steps (the wave's own LDS area).
 #pragma unroll
@@ -837,8 +865,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         constexpr int NA = decltype(na_tag)::value;
         if constexpr (NA > 0) {
           if constexpr (NV) {
-            // 64-element chunks of this stage inside K (K % 64 == 0).
-            const int64_t k_left = p.K - kt * KS;
+            // 64-element chunks of this stage inside the reduction (a multiple of 64).
+            const int64_t k_left = red - kt * KS;
             const int nchunk = k_left >= KS ? KS / BK : (int)(k_left / BK);
 #pragma unroll
             for (int c = 0; c < KS / BK; ++c) {
@@ -955,11 +983,12 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // 4g..4g+3 -- one 8-byte (bf16) or 16-byte (fp32) store each.
     float alpha = 1.0f;
     if (PF) alpha = alpha_t;
+    else if (MODE == W4A4_TN) alpha = p.ag[0] * p.bg[0];
     else if (NV) alpha = p.ag[0] * p.bg[expert];
     const int64_t ldc = p.N;
     float* C32 = reinterpret_cast<float*>(p.c);
     uint16_t* C16 = reinterpret_cast<uint16_t*>(p.c);
-    const int64_t cbase = MODE == TN_BF16 ? (int64_t)expert * p.K * p.N : 0;
+    const int64_t cbase = is_tn(MODE) ? (int64_t)expert * p.K * p.N : 0;
     if constexpr (SILU) {
       static_assert(BN == 256 && WTN % 64 == 0, "SiLU-gate tiles");
       // SiLU gate on the tile: block pair (2jj, 2jj+1) holds gate and up of
@@ -1201,7 +1230,7 @@ int launch_cfg(const Params& p0, hipStream_t st) {
   Params p = p0;
   p.n_tiles = (int)cdiv(p.N, BN);
   int64_t upper;
-  if (MODE == TN_BF16) {
+  if (is_tn(MODE)) {
     p.k_tiles_tn = (int)cdiv(p.K, BM);
     upper = (int64_t)p.E * p.k_tiles_tn * p.n_tiles;
   } else {
@@ -1315,6 +1344,7 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case W4A8: return launch_mode<W4A8>(cfg, p, st);
     case W4A8_SILU: return launch_mode<W4A8_SILU>(cfg, p, st);
     case W4A4_SILU_Q: return launch_mode<W4A4_SILU_Q>(cfg, p, st);
+    case W4A4_TN: return launch_mode<W4A4_TN>(cfg, p, st);
     default: return launch_mode<W4A4>(cfg, p, st);
   }
 }
@@ -1465,6 +1495,41 @@ extern "C" int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8
   if (!q_h) return NVFP4MOE_EINVAL;
   return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h,
                     amax_out, as_stream(stream), amax_h_in, q_h, s_h, g_h);
+}
+
+extern "C" int grouped_gemm_w4a4_wgrad(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q,
+                                       const uint8_t* b_s, const float* b_g, const int32_t* expert_offsets, int E,
+                                       int64_t M_total, int64_t Kp, int64_t N1, int64_t N2, void* c, int c_dtype,
+                                       nvfp4moe_stream_t stream) {
+  if (E < 1 || M_total < 0 || Kp < 0 || N1 < 0 || N2 < 0) return NVFP4MOE_EINVAL;
+  if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
+  if (!expert_offsets || !a_g || !b_g) return NVFP4MOE_EINVAL;
+  const bool has_out = N1 > 0 && N2 > 0;
+  if (has_out && (!c || (M_total > 0 && (!a_q || !a_s || !b_q || !b_s)))) return NVFP4MOE_EINVAL;
+  if (N1 % 32 != 0 || N2 % 32 != 0 || Kp % 64 != 0 || Kp < 64 * (M_total / 64 + (int64_t)E)) return NVFP4MOE_ESHAPE;
+  if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, 16))
+    return NVFP4MOE_ESHAPE;
+  // Operands are read through 32-bit buffer offsets.
+  if (N1 * (Kp / 2) >= (1LL << 31) || N2 * (Kp / 2) >= (1LL << 31) || M_total > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  if (!has_out) return NVFP4MOE_OK;
+  Params p = {};
+  p.a = a_q;
+  p.b = b_q;
+  p.as = a_s;
+  p.bs = b_s;
+  p.ag = a_g;
+  p.bg = b_g;
+  p.offsets = expert_offsets;
+  p.c = c;
+  p.M = M_total;
+  p.N = N2;
+  p.K = N1;
+  p.kp = Kp;
+  p.E = E;
+  p.c_f32 = c_dtype == NVFP4MOE_F32;
+  return launch(W4A4_TN, p, as_stream(stream));
 }
 
 extern "C" int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,

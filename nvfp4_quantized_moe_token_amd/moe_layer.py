@@ -197,3 +197,59 @@ def forward_w4a8(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
     ops.grouped_gemm_w4a8(buf.a2_q, buf.a2_s, wq_dn["q"], wq_dn["s"], meta["offsets"], out=buf.y2)
     ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=topk_w, out=buf.out)
     return meta
+
+
+def quantize_expert_weights_t(w, amax=None):
+    """NVFP4 of each expert weight transposed (W_e^T [K, N] of W [E, N, K]),
+    blocks along the weight's output dimension: the B operand of the NVFP4
+    backward's data gradients.  ``amax`` (the forward weights' per-expert
+    amax, the same values) is reused when given.  Once per optimizer step."""
+    q, sc, g, a = ops.nvfp4_quantize_transposed(w, amax_in=amax)
+    return dict(q=q, s=sc, g=g, amax=a)
+
+
+class NVFP4BackwardBuffers:
+    """Buffers of the NVFP4 backward variant (besides Buffers(backward=True))."""
+
+    def __init__(self, T, k, E, D, F, device):
+        R = T * k
+        Kp = ops.padded_extent(R, E)
+        u8, f32 = torch.uint8, torch.float32
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        self.Kp = Kp
+        self.amax = e(2, dt=f32)                      # [amax_dY2, amax_dY1]
+        self.a_dy2 = (e(R, D // 2), e(R, D // 16), e(1, dt=f32))
+        self.a_dy1 = (e(R, F), e(R, 2 * F // 16), e(1, dt=f32))
+        self.c_dy2 = (e(D, Kp // 2), e(D, Kp // 16), e(1, dt=f32))
+        self.c_h = (e(F, Kp // 2), e(F, Kp // 16), e(1, dt=f32))
+        self.c_dy1 = (e(2 * F, Kp // 2), e(2 * F, Kp // 16), e(1, dt=f32))
+        self.c_x = (e(D, Kp // 2), e(D, Kp // 16), e(1, dt=f32))
+
+
+def backward_nvfp4(dy, topk_w, wt_gu, wt_dn, meta, buf, nb, amax_x=None):
+    """The NVFP4 backward variant of ``backward``: the same dataflow with the
+    four grouped GEMMs in W4A4.  Each gradient's amax is taken once, by its
+    row-wise quantization, and reused by its column-wise one; H and X_perm
+    reuse the forward's amaxes (buf.amax, or ``amax_x`` when the forward
+    was given a fixed one).  wt_gu / wt_dn: quantize_expert_weights_t of the
+    bf16 weights.  Weight gradients fp32, activation gradients bf16."""
+    off = meta["offsets"]
+    R = buf.T * buf.k
+    amax_x = buf.amax[0:1] if amax_x is None else amax_x
+    ops.moe_scatter(dy, meta["dest"], off, buf.k, topk_w=topk_w, out=buf.dy2)
+    q, sc, g = nb.a_dy2
+    ops.nvfp4_quantize(buf.dy2, amax_out=nb.amax[0:1], q=q, scales=sc, gscale=g)
+    ops.grouped_gemm_w4a4(q, sc, g, wt_dn["q"], wt_dn["s"], wt_dn["g"], off, out=buf.dh)
+    ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
+    ops.nvfp4_quantize_colwise(buf.dy2, off, nb.amax[0:1], Kp=nb.Kp, q_t=nb.c_dy2[0], s_t=nb.c_dy2[1],
+                               gscale=nb.c_dy2[2])
+    ops.nvfp4_quantize_colwise(buf.h, off, buf.amax[1:2], Kp=nb.Kp, q_t=nb.c_h[0], s_t=nb.c_h[1], gscale=nb.c_h[2])
+    ops.grouped_gemm_w4a4_wgrad(nb.c_dy2, nb.c_h, off, R, out=buf.dw_dn)
+    q, sc, g = nb.a_dy1
+    ops.nvfp4_quantize(buf.dy1, amax_out=nb.amax[1:2], q=q, scales=sc, gscale=g)
+    ops.grouped_gemm_w4a4(q, sc, g, wt_gu["q"], wt_gu["s"], wt_gu["g"], off, out=buf.dx_perm)
+    ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
+    ops.nvfp4_quantize_colwise(buf.dy1, off, nb.amax[1:2], Kp=nb.Kp, q_t=nb.c_dy1[0], s_t=nb.c_dy1[1],
+                               gscale=nb.c_dy1[2])
+    ops.nvfp4_quantize_colwise(buf.x_perm, off, amax_x, Kp=nb.Kp, q_t=nb.c_x[0], s_t=nb.c_x[1], gscale=nb.c_x[2])
+    ops.grouped_gemm_w4a4_wgrad(nb.c_dy1, nb.c_x, off, R, out=buf.dw_gu)

@@ -262,6 +262,64 @@ def grouped_gemm_w4a4_silu_gate_nvfp4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, ama
     return q_h, s_h, g_h, amax_out
 
 
+def padded_extent(M_total, E):
+    """Row length of the column-wise layout: 64 * (M_total // 64 + E)."""
+    return 64 * (M_total // 64 + E)
+
+
+def nvfp4_quantize_colwise(x, offsets, amax_in, Kp=None, q_t=None, s_t=None, gscale=None):
+    """Column-wise NVFP4 of a row-grouped [M_total, N] bf16 tensor, stored
+    transposed ([N, Kp/2] codes, [N, Kp/16] scales; expert e's segment at
+    column 64 * (offsets[e] // 64 + e)).  Returns (q_t, s_t, gscale)."""
+    _dev(x, offsets, amax_in, q_t, s_t, gscale)
+    M, N = x.shape
+    E = offsets.numel() - 1
+    Kp = padded_extent(M, E) if Kp is None else Kp
+    dev = x.device
+    q_t = torch.empty((N, Kp // 2), dtype=torch.uint8, device=dev) if q_t is None else q_t
+    s_t = torch.empty((N, Kp // 16), dtype=torch.uint8, device=dev) if s_t is None else s_t
+    gscale = torch.empty((1,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    rc = _lib.load().nvfp4_quantize_colwise(_ptr(x), _DT[x.dtype], M, N, _ptr(offsets), E, _ptr(amax_in), _ptr(q_t),
+                                            _ptr(s_t), _ptr(gscale), Kp, _stream())
+    _check("nvfp4_quantize_colwise", rc)
+    return q_t, s_t, gscale
+
+
+def nvfp4_quantize_transposed(x, amax_in=None, amax_out=None, q_t=None, s_t=None, gscale=None):
+    """NVFP4 of each matrix of x [G, L, N] along its rows' index: codes of
+    the transposed matrices, q_t [G, N, L/2], s_t [G, N, L/16], gscale [G].
+    Returns (q_t, s_t, gscale, amax)."""
+    _dev(x, amax_in, amax_out, q_t, s_t, gscale)
+    G, L, N = x.shape
+    dev = x.device
+    q_t = torch.empty((G, N, L // 2), dtype=torch.uint8, device=dev) if q_t is None else q_t
+    s_t = torch.empty((G, N, L // 16), dtype=torch.uint8, device=dev) if s_t is None else s_t
+    gscale = torch.empty((G,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    if amax_in is None and amax_out is None:
+        amax_out = torch.empty((G,), dtype=torch.float32, device=dev)
+    rc = _lib.load().nvfp4_quantize_transposed(_ptr(x), _DT[x.dtype], G, L, N, _ptr(amax_in), _ptr(amax_out),
+                                               _ptr(q_t), _ptr(s_t), _ptr(gscale), _stream())
+    _check("nvfp4_quantize_transposed", rc)
+    return q_t, s_t, gscale, amax_in if amax_in is not None else amax_out
+
+
+def grouped_gemm_w4a4_wgrad(a, b, offsets, M_total, out=None, out_dtype=torch.float32):
+    """NVFP4 weight gradient: C_e = deq(A_e)^T . deq(B_e) over expert e's
+    rows, a and b the (q_t, s_t, gscale) of nvfp4_quantize_colwise.
+    Returns C [E, N1, N2]."""
+    (aq, as_, ag), (bq, bs, bg) = a, b
+    _dev(aq, as_, ag, bq, bs, bg, offsets, out)
+    E = offsets.numel() - 1
+    N1, Kp = aq.shape[0], aq.shape[1] * 2
+    N2 = bq.shape[0]
+    out = torch.empty((E, N1, N2), dtype=out_dtype, device=aq.device) if out is None else out
+    rc = _lib.load().grouped_gemm_w4a4_wgrad(_ptr(aq), _ptr(as_), _ptr(ag), _ptr(bq), _ptr(bs), _ptr(bg),
+                                             _ptr(offsets), E, M_total, Kp, N1, N2, _ptr(out), _DT[out.dtype],
+                                             _stream())
+    _check("grouped_gemm_w4a4_wgrad", rc)
+    return out
+
+
 MX_E4M3, MX_E2M1 = _lib.MX_E4M3, _lib.MX_E2M1
 
 
