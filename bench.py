@@ -82,6 +82,7 @@ def op_work(name, T, k, E, D, F, backward=True):
         # keeps one (the full update)
         "permute_quantize_x": (0.0, T * D * 2 + nv(R, D) + R * 4 * 3 + (R * D * 2 if backward else 0)),
         "w4a4_gate_up": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
+        "w4a4_gate_up_scaled_mfma": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2),
         # with the SiLU gate in the epilogue: Y1 (kept for the backward) and H written
         "w4a4_gate_up_silu": (f1, nv(R, D) + nv(E * 2 * F, D) + R * 2 * F * 2 + R * F * 2),
         "quantize_h": (0.0, R * F * 2 + nv(R, F)),
@@ -713,6 +714,100 @@ def dense_side(args):
             "quantize_x": quant_obj(ms_qx, M), "quantize_w": quant_obj(ms_qw, N)}
 
 
+AB_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+AB_KERNELS = [("gemm_kernel<3,", "W4A4 design A: E2M1 x E4M3 expanded exactly to fp16, fp16 MFMA 32x32x16"),
+              ("gemm_kernel<9,", "W4A4 design B: fp4 scaled MFMA 32x32x64, one 16-block per issue, fp32 rescale"),
+              ("gemm_kernel<5,", "W4A8 (MXFP8 x MXFP4): fp8 x fp4 scaled MFMA 32x32x64, native E8M0 scales"),
+              ("gemm_kernel<0,", "BF16 NT: bf16 MFMA 32x32x16")]
+
+
+def ab_run(args):
+    """The gate+up GEMM of the 8k-update step (65536 routed rows, 128
+    experts, 2F = 1536, K = 2048) in the four ways this library can run it,
+    three launches each, for rocprofv3 counter and trace runs: W4A4 by exact
+    fp16 expansion (the shipped design), W4A4 by scale factoring onto the
+    fp4 scaled MFMA, W4A8 on the scaled MFMA, and BF16."""
+    import torch
+    from nvfp4_quantized_moe_token_amd import moe_layer, ops
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = build_inputs("moe_8k_update", torch, dev)
+    d = inp["d"]
+    T, k, E, D, F = d["T"], d["k"], d["E"], d["D"], d["F"]
+    wq_gu = moe_layer.quantize_expert_weights(inp["w_gu"])
+    wx_gu = moe_layer.quantize_expert_weights_mx(inp["w_gu"])
+    m = ops.moe_permute_nvfp4(inp["ids"], E, inp["x"], want_x_perm=True)
+    xq, xs = ops.mx_quantize(inp["x"], ops.MX_E4M3)
+    pm = ops.moe_permute(inp["ids"], E, x=xq)
+    a8s = ops.moe_gather(xs, pm["src"], k)
+    y = torch.empty(T * k, 2 * F, dtype=torch.bfloat16, device=dev)
+    w4 = (m["q"], m["scales"], m["gscale"], wq_gu["q"], wq_gu["s"], wq_gu["g"], m["offsets"])
+    runs = [lambda: ops.grouped_gemm_w4a4(*w4, out=y),
+            lambda: ops.grouped_gemm_w4a4_scaled_mfma(*w4, out=y),
+            lambda: ops.grouped_gemm_w4a8(pm["x_perm"], a8s, wx_gu["q"], wx_gu["s"], pm["offsets"], out=y),
+            lambda: ops.grouped_gemm_bf16(ops.NT, m["x_perm"], inp["w_gu"], m["offsets"], out=y)]
+    for fn in runs:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+    log("ab run done")
+
+
+def ab_summary(trace_dir, pmc_dir):
+    """Per design of the gate+up GEMM (ab_run): average launch time from a
+    kernel-trace run, and the counters of a --pmc run (averaged over the
+    launches): VALU and LDS instructions per MFMA instruction, the MFMA
+    unit's busy fraction of SIMD cycles, LDS bank-conflict cycles."""
+    import csv
+    T, k, D, F = 8192, 8, 2048, 768
+    flops = 2.0 * T * k * 2 * F * D
+    dur = {}
+    for p in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                n = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("nvfp4moe::", "")
+                for key, _ in AB_KERNELS:
+                    if key in n.replace(" ", ""):
+                        dur.setdefault(key, []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    vals = {}
+    for p in sorted(glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                n = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("nvfp4moe::", "").replace(" ", "")
+                for key, _ in AB_KERNELS:
+                    if key in n:
+                        c = vals.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
+                        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# The gate+up GEMM of the 8k-update step (65536 routed rows, 128 experts, N = 1536, K = 2048;",
+             "# %.1f GFLOP) run four ways; time: average of 3 launches from a kernel-trace run; counters: one" % (flops / 1e9),
+             "# --pmc run, averaged over the 3 launches.  valu/mfma and lds/mfma: SQ_INSTS_VALU, SQ_INSTS_LDS per",
+             "# SQ_INSTS_MFMA; mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);",
+             "# valu_active: SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE / 8 x 1024) (wave-cycles on VALU per SIMD cycle);",
+             "# lds_conflict: SQ_LDS_BANK_CONFLICT cycles per launch.",
+             "# commands ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&",
+             "#   rocprofv3 --kernel-trace --output-format csv -d $OUT/ab_kt -o run -- python $REPO/bench.py --ab-run;",
+             "#   rocprofv3 --pmc %s --output-format csv -d $OUT/ab_pmc -o run --" % " ".join(AB_COUNTERS),
+             "#   python $REPO/bench.py --ab-run; then python $REPO/bench.py --ab-summary $OUT/ab_kt $OUT/ab_pmc",
+             "sources %s" % source_digest(),
+             "%-16s %9s %8s %8s %9s %9s %10s %10s %13s  %s" % ("kernel", "us", "TFLOP/s", "of_bf16", "valu/mfma",
+                                                             "lds/mfma", "mfma_busy", "valu_act", "lds_conflict",
+                                                             "design")]
+    for key, desc in AB_KERNELS:
+        ts = dur.get(key, [])
+        us = sum(ts) / len(ts) / 1e3 if ts else float("nan")
+        cs = list(vals.get(key, {}).values())
+        avg = {c: sum(v.get(c, 0.0) for v in cs) / max(len(cs), 1) for c in AB_COUNTERS}
+        mf = avg["SQ_INSTS_MFMA"] or float("nan")
+        cyc = avg["GRBM_GUI_ACTIVE"] / 8.0 * 1024
+        tf = flops / (us * 1e-6) / 1e12 if ts else float("nan")
+        lines.append("%-16s %9.1f %8.1f %7.1f%% %9.2f %9.2f %9.1f%% %9.1f%% %13.0f  %s" % (
+            key.rstrip(","), us, tf, 100 * tf / PEAK_BF16_TFLOPS, avg["SQ_INSTS_VALU"] / mf, avg["SQ_INSTS_LDS"] / mf,
+            100 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / cyc if cyc else float("nan"),
+            100 * avg["SQ_ACTIVE_INST_VALU"] * 4 / cyc if cyc else float("nan"), avg["SQ_LDS_BANK_CONFLICT"], desc))
+    print("\n".join(lines))
+
+
 def bench_dense(args):
     """One JSON line for the dense workload: `value` is the W4A4 GEMM's
     TFLOP/s (see dense_side)."""
@@ -755,9 +850,18 @@ def main():
     ap.add_argument("--kernel-stats-summary", metavar="DIR")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="per-op executed MFMA FLOPs and MFMA busy fraction from a --pmc-run counter run")
+    ap.add_argument("--ab-run", action="store_true",
+                    help="the gate+up GEMM run four ways (W4A4 A/B designs, W4A8, BF16), for rocprofv3")
+    ap.add_argument("--ab-summary", nargs=2, metavar=("TRACE_DIR", "PMC_DIR"))
     ap.add_argument("--dispatch-summary", nargs=2, metavar=("DIR", "KERNEL"),
                     help="per-launch durations of one kernel in a kernel-trace run, by grid size")
     args = ap.parse_args()
+    if args.ab_summary:
+        ab_summary(*args.ab_summary)
+        return
+    if args.ab_run:
+        ab_run(args)
+        return
     if args.dispatch_summary:
         dispatch_summary(*args.dispatch_summary)
         return
@@ -901,6 +1005,9 @@ def main():
         "w4a4_gate_up": lambda: ops.grouped_gemm_w4a4(buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"],
                                                       wq_gu["g"], offs, out=y1w),
         "bf16_nt_gate_up_baseline": lambda: ops.grouped_gemm_bf16(ops.NT, buf.x_perm, inp["w_gu"], offs, out=y1b),
+        # the same W4A4 product by scale factoring onto the fp4 scaled MFMA
+        "w4a4_gate_up_scaled_mfma": lambda: ops.grouped_gemm_w4a4_scaled_mfma(
+            buf.a1_q, buf.a1_s, buf.a1_g, wq_gu["q"], wq_gu["s"], wq_gu["g"], offs, out=y1w),
     }
     per_op_extra = {}
     nrep = max(5, min(args.steps, 20))
@@ -1115,7 +1222,9 @@ def main():
         "roofline": roofline_of_kernel(dominant) if dominant in KERNEL_OF_OP.values() else roofline_of(dominant),
         "w4a4_gemm": {**roofline_of("w4a4_gate_up"), "frac_fp4_peak": w4.get("frac_fp4_mfma_peak"),
                       "bf16_same_shape_tflops": bl.get("tflops"),
-                      "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3)},
+                      "speedup_vs_bf16": round(bl["ms"] / w4["ms"], 3),
+                      "scaled_mfma_design_tflops": kernels["w4a4_gate_up_scaled_mfma"].get("tflops"),
+                      "speedup_vs_scaled_mfma_design": round(kernels["w4a4_gate_up_scaled_mfma"]["ms"] / w4["ms"], 3)},
         "dense_qwen3_4b_up": dense,
         "w4a8": w4a8,
         "forward_delayed_amax_h": delayed,

@@ -267,6 +267,23 @@ int grouped_gemm_w4a4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
                       size_t ws_bytes, nvfp4moe_stream_t stream);
 
 /*
+ * grouped_gemm_w4a4_scaled_mfma -- the same product as grouped_gemm_w4a4
+ * (NVFP4MOE_EPI_NONE) computed the other way open on gfx950 ([RU] fast-kernels
+ * section: the scaling scheme's cost): NVFP4's E4M3 block scales are not
+ * E8M0, so the scaled fp4 MFMA runs one 16-element block per instruction
+ * with unit E8M0 scales and the other K slots zero, and each block's exact
+ * partial sums are multiplied by sA * sB and accumulated in fp32.  Kept to
+ * measure this design against the shipped one (exact fp16 expansion on the
+ * 16-bit MFMA, grouped_gemm_w4a4), which it loses to: the per-element fp32
+ * rescale and the 4x zero padding of the MFMA's K.  Arguments, layouts and
+ * errors as grouped_gemm_w4a4.
+ */
+int grouped_gemm_w4a4_scaled_mfma(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                  const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                  const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
+                                  void* c, int c_dtype, nvfp4moe_stream_t stream);
+
+/*
  * grouped_gemm_w4a4_silu_gate -- the gate+up W4A4 GEMM with the SiLU gate
  * and the amax of its output in the epilogue ([JA] fourth paragraph: op
  * fusion, amax reuse): the result equals grouped_gemm_w4a4 (N = 2F, bf16 C)

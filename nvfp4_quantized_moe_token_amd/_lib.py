@@ -38,6 +38,8 @@ SIGNATURES = {
     "nvfp4_quantize_transposed": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "grouped_gemm_w4a4_wgrad": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64,
                                         c_vp, c_int, c_vp]),
+    "grouped_gemm_w4a4_scaled_mfma": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
+                                              c_vp, c_int, c_vp]),
     "mx_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_int, c_vp, c_vp, c_vp]),
     "grouped_gemm_w4a8": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp]),
     "grouped_gemm_w4a8_silu_gate": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp,

@@ -78,11 +78,17 @@ constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data for
 // W4A4_TN: the NVFP4 weight gradient, C_e = A_e^T . B_e reduced over the
 // rows of expert e, both operands quantized column-wise (stored transposed:
 // K-major rows whose reduction index runs over the expert's padded segment).
+// W4A4_B: the same NVFP4 product by scale factoring onto the fp4 scaled MFMA
+// (one 16-element block per MFMA, unit E8M0 scales, the E4M3 block-scale
+// products applied to each partial sum in fp32) -- the alternative to the
+// exact fp16 expansion, kept to measure the two against each other.
 enum Mode {
   NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6, W4A4_SILU_Q = 7,
-  W4A4_TN = 8
+  W4A4_TN = 8, W4A4_B = 9
 };
-constexpr bool is_nv(int mode) { return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q || mode == W4A4_TN; }
+constexpr bool is_nv(int mode) {
+  return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q || mode == W4A4_TN || mode == W4A4_B;
+}
 constexpr bool is_tn(int mode) { return mode == TN_BF16 || mode == W4A4_TN; }
 constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU; }
 constexpr bool is_q(int mode) { return is_nv(mode) || is_mx(mode); }
@@ -864,7 +870,80 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       auto compute = [&](auto na_tag) {
         constexpr int NA = decltype(na_tag)::value;
         if constexpr (NA > 0) {
-          if constexpr (NV) {
+          if constexpr (MODE == W4A4_B) {
+            // Per 64-element chunk c and 16-element block j of it: the lane
+            // half h = j / 2 holds the block in half j % 2 of its 16 code
+            // bytes (the NVFP4 stage layout is the fp4 MFMA's operand
+            // layout); everything else is masked to zero, so the MFMA (unit
+            // scales) returns the block's exact partial sums, which are
+            // scaled by sA[m][b] * sB[n][b] and accumulated in fp32.
+            const int64_t k_left = red - kt * KS;
+            const int nchunk = k_left >= KS ? KS / BK : (int)(k_left / BK);
+            const uint8_t* sca = st + A_BYTES + B_BYTES;
+            const int h = lane >> 5;
+#pragma unroll
+            for (int c = 0; c < KS / BK; ++c) {
+              if (c < nchunk) {
+                uint4 qa[NA], qb[FN];
+                float sa[NA][4];
+#pragma unroll
+                for (int i = 0; i < NA; ++i) {
+                  const int row = wm * WTM + i * 32 + (lane & 31);
+                  qa[i] = *reinterpret_cast<const uint4*>(st + row * 128 + (((2 * c + h) ^ kswz(row)) << 4));
+                  const uint32_t w = *reinterpret_cast<const uint32_t*>(sca + row * 16 + 4 * c);
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) sa[i][j] = e4m3_decode((w >> (8 * j)) & 0xFF);
+                }
+#pragma unroll
+                for (int jf = 0; jf < FN; ++jf) {
+                  const int row = wn * WTN + jf * 32 + (lane & 31);
+                  qb[jf] = *reinterpret_cast<const uint4*>(st + A_BYTES + row * 128 + (((2 * c + h) ^ kswz(row)) << 4));
+                }
+#pragma unroll
+                for (int jf = 0; jf < FN; ++jf) {
+                  // B scale words of the 16 result rows n = 8g + 4(l/32) + r%4 this lane holds
+                  uint32_t bw[16];
+#pragma unroll
+                  for (int r = 0; r < 16; ++r) {
+                    const int n = wn * WTN + jf * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    bw[r] = *reinterpret_cast<const uint32_t*>(sca + BM * 16 + n * 16 + 4 * c);
+                  }
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    const bool mine = h == (j >> 1);
+                    const uint32_t lo = (j & 1) == 0;
+                    i32x8_t ob;
+                    ob[0] = mine && lo ? (int)qb[jf].x : 0;
+                    ob[1] = mine && lo ? (int)qb[jf].y : 0;
+                    ob[2] = mine && !lo ? (int)qb[jf].z : 0;
+                    ob[3] = mine && !lo ? (int)qb[jf].w : 0;
+                    ob[4] = ob[5] = ob[6] = ob[7] = 0;
+                    float sb[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sb[r] = e4m3_decode((bw[r] >> (8 * j)) & 0xFF);
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                      i32x8_t oa;
+                      oa[0] = mine && lo ? (int)qa[i].x : 0;
+                      oa[1] = mine && lo ? (int)qa[i].y : 0;
+                      oa[2] = mine && !lo ? (int)qa[i].z : 0;
+                      oa[3] = mine && !lo ? (int)qa[i].w : 0;
+                      oa[4] = oa[5] = oa[6] = oa[7] = 0;
+                      f32x16_t z;
+#pragma unroll
+                      for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+                      const f32x16_t part =
+                          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ob, oa, z, 4, 4, 0, 127, 0, 127);
+                      // the lane's result column is its A row m = l % 32: its scale is per lane
+                      const float s_a = sa[i][j];
+#pragma unroll
+                      for (int r = 0; r < 16; ++r) acc[i][jf][r] = fmaf(part[r], s_a * sb[r], acc[i][jf][r]);
+                    }
+                  }
+                }
+              }
+            }
+          } else if constexpr (NV) {
             // 64-element chunks of this stage inside the reduction (a multiple of 64).
             const int64_t k_left = red - kt * KS;
             const int nchunk = k_left >= KS ? KS / BK : (int)(k_left / BK);
@@ -1345,6 +1424,7 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case W4A8_SILU: return launch_mode<W4A8_SILU>(cfg, p, st);
     case W4A4_SILU_Q: return launch_mode<W4A4_SILU_Q>(cfg, p, st);
     case W4A4_TN: return launch_mode<W4A4_TN>(cfg, p, st);
+    case W4A4_B: return launch_mode<W4A4_B>(cfg, p, st);
     default: return launch_mode<W4A4>(cfg, p, st);
   }
 }
@@ -1360,7 +1440,8 @@ namespace {
 int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const uint8_t* b_q, const uint8_t* b_s,
                const float* b_g, const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K,
                void* c, int c_dtype, int silu, void* h, float* amax_out, hipStream_t st,
-               const float* h_amax_in = nullptr, uint8_t* hq = nullptr, uint8_t* hs = nullptr, float* hg = nullptr) {
+               const float* h_amax_in = nullptr, uint8_t* hq = nullptr, uint8_t* hs = nullptr, float* hg = nullptr,
+               bool design_b = false) {
   const bool qh = hq != nullptr;
   if (E < 1 || M_total < 0 || N < 0 || K < 0) return NVFP4MOE_EINVAL;
   if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
@@ -1401,7 +1482,7 @@ int w4a4_entry(const uint8_t* a_q, const uint8_t* a_s, const float* a_g, const u
   p.hs = hs;
   p.hg = hg;
   p.h_amax_in = h_amax_in;
-  return launch(silu ? (qh ? W4A4_SILU_Q : W4A4_SILU) : W4A4, p, st);
+  return launch(silu ? (qh ? W4A4_SILU_Q : W4A4_SILU) : design_b ? W4A4_B : W4A4, p, st);
 }
 
 }  // namespace
@@ -1530,6 +1611,14 @@ extern "C" int grouped_gemm_w4a4_wgrad(const uint8_t* a_q, const uint8_t* a_s, c
   p.E = E;
   p.c_f32 = c_dtype == NVFP4MOE_F32;
   return launch(W4A4_TN, p, as_stream(stream));
+}
+
+extern "C" int grouped_gemm_w4a4_scaled_mfma(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,
+                                             const uint8_t* b_q, const uint8_t* b_s, const float* b_g,
+                                             const int32_t* expert_offsets, int E, int64_t M_total, int64_t N,
+                                             int64_t K, void* c, int c_dtype, nvfp4moe_stream_t stream) {
+  return w4a4_entry(a_q, a_s, a_g, b_q, b_s, b_g, expert_offsets, E, M_total, N, K, c, c_dtype, 0, nullptr, nullptr,
+                    as_stream(stream), nullptr, nullptr, nullptr, nullptr, true);
 }
 
 extern "C" int grouped_gemm_bf16_tn_gather(const void* a, const void* b, const int32_t* b_src, int k,

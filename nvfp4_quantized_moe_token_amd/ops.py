@@ -217,6 +217,20 @@ def grouped_gemm_w4a4(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out=None, out_dtype
     return out
 
 
+def grouped_gemm_w4a4_scaled_mfma(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out=None, out_dtype=torch.float32):
+    """grouped_gemm_w4a4 by scale factoring onto the fp4 scaled MFMA (the
+    alternative design, for measurement)."""
+    _dev(a_q, a_s, a_g, b_q, b_s, b_g, offsets, out)
+    M = a_q.shape[0]
+    K = a_q.shape[1] * 2
+    E, N = b_q.shape[0], b_q.shape[1]
+    out = torch.empty((M, N), dtype=out_dtype, device=a_q.device) if out is None else out
+    rc = _lib.load().grouped_gemm_w4a4_scaled_mfma(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g),
+                                                   _ptr(offsets), E, M, N, K, _ptr(out), _DT[out.dtype], _stream())
+    _check("grouped_gemm_w4a4_scaled_mfma", rc)
+    return out
+
+
 def grouped_gemm_w4a4_silu_gate(a_q, a_s, a_g, b_q, b_s, b_g, offsets, y1=None, want_y1=True, h=None,
                                 amax_out=None, want_amax=True):
     """Gate+up W4A4 GEMM with the SiLU gate (and amax of H) in its epilogue.

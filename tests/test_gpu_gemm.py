@@ -292,3 +292,28 @@ def test_bf16_tn_gather_moe_8k_gate_up():
     dw_ref = ops.grouped_gemm_bf16(ops.TN, dy1, r["x_perm"], r["offsets"])
     torch.cuda.synchronize()
     assert torch.equal(dw.view(torch.int32), dw_ref.view(torch.int32))
+
+
+
+@pytest.mark.parametrize("counts,N,K", [([0, 1, 300, 0, 37, 256, 511], 96, 256), ([700], 512, 320)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_w4a4_scaled_mfma_design_matches_oracle(counts, N, K, out_dtype):
+    """The scale-factoring design (fp4 scaled MFMA, one block per issue,
+    fp32 rescale) computes the same product within the tolerance."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(sum(counts) + N + K)
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] *= 20
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    a = nvfp4.quantize(x)
+    b = quantize_weights(w)
+    g = [to_gpu(a[0], torch.uint8), to_gpu(a[1], torch.uint8), to_gpu(a[2], torch.float32),
+         to_gpu(b[0], torch.uint8), to_gpu(b[1], torch.uint8), to_gpu(b[2], torch.float32), to_gpu(off, torch.int32)]
+    c = ops.grouped_gemm_w4a4_scaled_mfma(*g, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, ab = gemm.grouped_gemm_w4a4(a[0], a[1], a[2], b[0], b[1], b[2], off)
+    assert_gemm_close(to_np(c), ref, ab, bf16_out=out_dtype == torch.bfloat16, what="scaled-mfma design")
