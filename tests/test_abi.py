@@ -31,7 +31,10 @@ def test_header_declares_entry_points():
     for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
               "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "moe_scatter",
               "grouped_gemm_bf16_tn_gather", "silu_gate_fwd",
-              "silu_gate_bwd", "moe_permute_nvfp4",
+              "silu_gate_bwd", "moe_permute_nvfp4", "moe_permute_nvfp4_noalloc",
+              "grouped_gemm_w4a4_silu_gate_nvfp4", "grouped_gemm_w4a4_scaled_mfma", "nvfp4_quantize_colwise",
+              "nvfp4_quantize_transposed", "grouped_gemm_w4a4_wgrad", "mx_quantize", "grouped_gemm_w4a8",
+              "grouped_gemm_w4a8_silu_gate",
               "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
         assert n in names
 
@@ -195,6 +198,113 @@ def test_gemm_tn_gather_validation(lib):
     assert g(*bad) == -2                       # b_src alignment
     bad = list(args); bad[4] = 1 << 25
     assert g(*bad) == -2                       # b_rows * N * 2 >= 2^31
+
+
+def test_scaled_mfma_and_silu_nvfp4_validation(lib):
+    g = lib.grouped_gemm_w4a4_scaled_mfma
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 64, FAKE, 0, None]
+    bad = list(args); bad[12] = 9
+    assert g(*bad) == -1                       # dtype
+    bad = list(args); bad[10] = 96
+    assert g(*bad) == -2                       # K % 64
+    bad = list(args); bad[7] = 0
+    assert g(*bad) == -1                       # E < 1
+    f = lib.grouped_gemm_w4a4_silu_gate_nvfp4
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 64, None, None, None, FAKE, FAKE, FAKE, FAKE,
+            None]
+    bad = list(args); bad[15] = None
+    assert f(*bad) == -1                       # q_h NULL
+    bad = list(args); bad[14] = None
+    assert f(*bad) == -1                       # amax_h_in NULL
+    bad = list(args); bad[17] = None
+    assert f(*bad) == -1                       # g_h NULL
+    bad = list(args); bad[13] = FAKE
+    assert f(*bad) == -1                       # amax_out aliases amax_h_in
+    bad = list(args); bad[9] = 96
+    assert f(*bad) == -2                       # F % 128
+    bad = list(args); bad[15] = FAKE + 2
+    assert f(*bad) == -2                       # q_h alignment
+
+
+def test_colwise_and_transposed_validation(lib):
+    c = lib.nvfp4_quantize_colwise
+    Kp = 64 * (100 // 64 + 4)
+    args = [FAKE, 1, 100, 64, FAKE, 4, FAKE, FAKE, FAKE, FAKE, Kp, None]
+    bad = list(args); bad[1] = 0
+    assert c(*bad) == -1                       # only bf16 input
+    bad = list(args); bad[6] = None
+    assert c(*bad) == -1                       # amax_in NULL
+    bad = list(args); bad[5] = 0
+    assert c(*bad) == -1                       # E < 1
+    bad = list(args); bad[3] = 60
+    assert c(*bad) == -2                       # N % 8
+    bad = list(args); bad[10] = Kp - 64
+    assert c(*bad) == -2                       # Kp below 64 * (M/64 + E)
+    bad = list(args); bad[10] = Kp + 32
+    assert c(*bad) == -2                       # Kp % 64
+    bad = list(args); bad[7] = FAKE + 4
+    assert c(*bad) == -2                       # q_t alignment
+    t = lib.nvfp4_quantize_transposed
+    args = [FAKE, 1, 4, 128, 64, FAKE, None, FAKE, FAKE, FAKE, None]
+    bad = list(args); bad[5] = None
+    assert t(*bad) == -1                       # neither amax_in nor amax_out
+    bad = list(args); bad[0] = None
+    assert t(*bad) == -1                       # x NULL with elements
+    bad = list(args); bad[3] = 96
+    assert t(*bad) == -2                       # L % 64
+    bad = list(args); bad[4] = 12
+    assert t(*bad) == -2                       # N % 8
+    bad = list(args); bad[2] = 0
+    assert t(*bad) == -1                       # groups < 1
+
+
+def test_wgrad_validation(lib):
+    w = lib.grouped_gemm_w4a4_wgrad
+    Kp = 64 * (100 // 64 + 4)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 100, Kp, 64, 64, FAKE, 0, None]
+    bad = list(args); bad[13] = 9
+    assert w(*bad) == -1                       # dtype
+    bad = list(args); bad[12] = None
+    assert w(*bad) == -1                       # c NULL
+    bad = list(args); bad[2] = None
+    assert w(*bad) == -1                       # a_g NULL
+    bad = list(args); bad[9] = Kp - 64
+    assert w(*bad) == -2                       # Kp too small for the padded segments
+    bad = list(args); bad[10] = 48
+    assert w(*bad) == -2                       # N1 % 32
+    bad = list(args); bad[11] = 40
+    assert w(*bad) == -2                       # N2 % 32
+    bad = list(args); bad[10] = 1 << 20; bad[9] = 1 << 12
+    assert w(*bad) == -2                       # N1 * Kp / 2 >= 2^31
+
+
+def test_mx_validation(lib):
+    from nvfp4_quantized_moe_token_amd import _lib
+    m = lib.mx_quantize
+    assert m(FAKE, 1, 4, 64, 7, FAKE, FAKE, None) == -1                # unknown element format
+    assert m(FAKE, 2, 4, 64, _lib.MX_E4M3, FAKE, FAKE, None) == -1     # u8 input
+    assert m(FAKE, 1, 4, 48, _lib.MX_E4M3, FAKE, FAKE, None) == -2     # K % 32
+    assert m(FAKE, 1, 4, 64, _lib.MX_E4M3, FAKE + 8, FAKE, None) == -2  # fp8 codes need 16-byte alignment
+    assert m(FAKE, 1, 4, 64, _lib.MX_E2M1, FAKE, None, None) == -1     # scales NULL
+    assert m(FAKE, 1, -1, 64, _lib.MX_E2M1, FAKE, FAKE, None) == -1    # negative rows
+    g = lib.grouped_gemm_w4a8
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 128, FAKE, 0, None]
+    bad = list(args); bad[8] = 64
+    assert g(*bad) == -2                       # K % 128
+    bad = list(args); bad[7] = 48
+    assert g(*bad) == -2                       # N % 32
+    bad = list(args); bad[4] = None
+    assert g(*bad) == -1                       # offsets NULL
+    bad = list(args); bad[10] = 2
+    assert g(*bad) == -1                       # u8 output
+    s = lib.grouped_gemm_w4a8_silu_gate
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 128, None, FAKE, None, None]
+    bad = list(args); bad[10] = None
+    assert s(*bad) == -1                       # H is required
+    bad = list(args); bad[7] = 64
+    assert s(*bad) == -2                       # F % 128
+    bad = list(args); bad[7] = -128
+    assert s(*bad) == -1                       # F < 0
 
 
 def test_silu_validation(lib):
