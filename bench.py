@@ -541,6 +541,109 @@ def pmc_summary(fetch_dir, write_dir, clock_dir=None):
     print("\n".join(lines))
 
 
+def _pmc_by_op(dirs):
+    """Counter values of `bench.py --pmc-run` runs (rocprofv3 --pmc, csv),
+    summed over each step op's GEMM dispatches (ops without a GEMM: all their
+    dispatches) in the last step; {op: {counter: value}} and {op: us}."""
+    import csv
+    per_op, us = {}, {}
+    for d in dirs:
+        vals, names, ns = {}, {}, {}
+        for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    i = int(r["Dispatch_Id"])
+                    names[i] = r["Kernel_Name"]
+                    ns[i] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                    c = vals.setdefault(i, {})
+                    c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ids = sorted(vals)
+        marks = [j for j, i in enumerate(ids) if MARKER in names[i]][-(len(STEP_OPS) + 1):]
+        if len(marks) != len(STEP_OPS) + 1:
+            sys.exit("%s: not a --pmc-run counter run" % d)
+        for j, name in enumerate(STEP_OPS):
+            seg = [ids[x] for x in range(marks[j] + 1, marks[j + 1])]
+            gem = [i for i in seg if "gemm_kernel" in names[i]]
+            seg = gem or seg
+            us.setdefault(name, sum(ns[i] for i in seg) / 1e3)
+            o = per_op.setdefault(name, {})
+            run = {}
+            for i in seg:
+                for c, v in vals[i].items():
+                    run[c] = run.get(c, 0.0) + v
+            # each counter keeps the clock count of the run that collected it
+            for c, v in run.items():
+                if c != "GRBM_GUI_ACTIVE":
+                    o[c] = v
+                    o["clk:" + c] = run.get("GRBM_GUI_ACTIVE", 0.0)
+    return per_op, us
+
+
+def counter_summary(dirs):
+    """Where the GEMMs of one moe_8k_update step spend their time, from
+    several rocprofv3 --pmc runs of `bench.py --pmc-run` (one counter set
+    each): wave-cycle shares, MFMA busy, the load path (TA and TD busy, TD
+    waiting on the L1/L2), L2 hit rate and read latencies, LDS bank
+    conflicts.  Per-CU blocks are normalised by GRBM_GUI_ACTIVE / 8 XCDs x
+    256 CUs, per-SIMD ones by x 1024 SIMDs."""
+    per_op, us = _pmc_by_op(dirs)
+
+    def ratio(o, a, b, scale=1.0):
+        if b == "GRBM_GUI_ACTIVE":
+            b = "clk:" + a
+        return o[a] / o[b] * scale if a in o and o.get(b) else float("nan")
+
+    cols = [("us", None),
+            ("wait_any", lambda o: ratio(o, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+            ("wait_issue", lambda o: ratio(o, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("active", lambda o: ratio(o, "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("mfma_busy", lambda o: ratio(o, "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", 8 / 1024)),
+            ("ta_busy", lambda o: ratio(o, "TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", 8 / 256)),
+            ("td_busy", lambda o: ratio(o, "TD_TD_BUSY_sum", "GRBM_GUI_ACTIVE", 8 / 256)),
+            ("td_wait_l2", lambda o: ratio(o, "TD_TC_STALL_sum", "GRBM_GUI_ACTIVE", 8 / 256)),
+            ("l2_hit", lambda o: o["TCC_HIT_sum"] / (o["TCC_HIT_sum"] + o["TCC_MISS_sum"])
+             if o.get("TCC_HIT_sum", 0) + o.get("TCC_MISS_sum", 0) > 0 else float("nan")),
+            ("l1l2_lat", lambda o: ratio(o, "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum")),
+            ("miss_lat", lambda o: ratio(o, "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum")),
+            ("lds_conf", lambda o: ratio(o, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"))]
+    lines = ["# Where the GEMMs of one moe_8k_update step spend their time (8192 tokens, d_model 2048,",
+             "# 128 experts, top-8, FFN 768), from rocprofv3 --pmc runs of `bench.py --pmc-run`, one counter",
+             "# set per run, summed over each op's GEMM dispatches of the last step.",
+             "# wait_any / wait_issue / active: shares of SQ_WAVE_CYCLES waiting on s_waitcnt or a barrier,",
+             "#   waiting to issue (a dependency or a busy unit), issuing; mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES",
+             "#   per SIMD-cycle; ta_busy, td_busy, td_wait_l2: TA_TA_BUSY, TD_TD_BUSY, TD_TC_STALL per",
+             "#   CU-cycle (the load path of each CU: address unit, data return, data return waiting on",
+             "#   the L1/L2); l2_hit: TCC_HIT / (TCC_HIT + TCC_MISS); l1l2_lat: mean L1->L2 read latency",
+             "#   (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ, cycles); miss_lat: mean L2-miss read latency",
+             "#   (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ); lds_conf: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.",
+             "# commands ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&",
+             "#   rocprofv3 --pmc <set> --output-format csv -d $OUT/<n> -o run -- python $REPO/bench.py --pmc-run",
+             "#   --steps 2 --warmup 1 --no-cpu-baseline, once per counter set:",
+             "#   a: SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS",
+             "#      SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_MISC GRBM_GUI_ACTIVE",
+             "#   b: SQ_WAIT_INST_LDS SQ_INST_LEVEL_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL",
+             "#      SQ_LDS_CMD_FIFO_FULL SQ_INSTS_LDS SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE",
+             "#   d: TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_UTCL1_TRANSLATION_MISS_sum",
+             "#      TCP_UTCL1_REQUEST_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+             "#   e: TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCP_PENDING_STALL_CYCLES_sum",
+             "#      TCP_TCR_TCP_STALL_CYCLES_sum GRBM_GUI_ACTIVE",
+             "#   f: TA_TA_BUSY_sum TA_DATA_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum",
+             "#      TCP_TD_TCP_STALL_CYCLES_sum TCP_PENDING_STALL_CYCLES_sum GRBM_GUI_ACTIVE",
+             "# then python $REPO/bench.py --counter-summary $OUT/a $OUT/b $OUT/d $OUT/e $OUT/f",
+             "sources %s" % source_digest(),
+             "%-18s" % "op" + "".join("%11s" % c for c, _ in cols)]
+    for name in STEP_OPS:
+        o = per_op.get(name, {})
+        if not o:
+            continue
+        row = "%-18s%11.1f" % (name, us[name])
+        for c, fn in cols[1:]:
+            v = fn(o)
+            row += "%11.0f" % v if c.endswith("lat") else "%11.3f" % v
+        lines.append(row)
+    print("\n".join(lines))
+
+
 def mfma_summary(d):
     """Per op of one moe_8k_update step, from a rocprofv3 --pmc run of
     `bench.py --pmc-run` with SQ_INSTS_VALU_MFMA_MOPS_F16,
@@ -848,6 +951,8 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="FETCH_SIZE and WRITE_SIZE run directories, optionally a GRBM_GUI_ACTIVE one")
     ap.add_argument("--kernel-stats-summary", metavar="DIR")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="per-op wave, load-path, L2 and LDS counters from several --pmc-run counter runs")
     ap.add_argument("--mfma-summary", metavar="DIR",
                     help="per-op executed MFMA FLOPs and MFMA busy fraction from a --pmc-run counter run")
     ap.add_argument("--ab-run", action="store_true",
@@ -867,6 +972,9 @@ def main():
         return
     if args.mfma_summary:
         mfma_summary(args.mfma_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
