@@ -1340,9 +1340,9 @@ def main():
         "w4a8": w4a8,
         "forward_delayed_amax_h": delayed,
         "nvfp4_backward": nvbwd,
-        "quantize": roofline_of("quantize_x_perm_cold"),
-        "quantize_16k": roofline_of("quantize_x_perm_16k_cold"),
-        "permute_quantize": roofline_of("permute_quantize_x"),
+        "quantize": dict(roofline_of("quantize_x_perm_cold"), amax="reused (amax_in from the permute)"),
+        "quantize_16k": dict(roofline_of("quantize_x_perm_16k_cold"), amax="reused (amax_in)"),
+        "permute_quantize": dict(roofline_of("permute_quantize_x"), amax="computed (fused into the metadata pass)"),
         "cpu_baseline": cpu,
         "kernels": kernels,
         "weight_quantize": {"ms": round(wq_ms, 4), "gbs": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1),
