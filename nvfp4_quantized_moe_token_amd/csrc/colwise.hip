@@ -21,17 +21,23 @@
 // the same fp32 values, so a segment's codes equal those of the row
 // quantizer applied to its transpose.
 //
-// Work: one workgroup per 64 padded rows x 256 columns.  The tile is read
-// with 16-byte row-contiguous loads into LDS (bf16), then each thread takes
-// one column: 4 blocks of 16 rows, 32 bytes of codes and a 4-byte scale word
-// written to that column's output row.  Padded rows read as zeros.
+// Work: one workgroup per 256 padded rows x 64 columns, as four 64-row
+// quarters that each resolve their own expert (or weight group).  The tile is
+// read with 16-byte loads, 128 contiguous bytes per row, into LDS (bf16).
+// Then each wave takes one quarter and each thread one column of it: 4 blocks
+// of 16 rows, 32 bytes of codes and a 4-byte scale word.  The four quarters
+// of a column fill 128 consecutive bytes of that column's output row (and 16
+// scale bytes).  The results are staged by output row in LDS and stored by
+// consecutive lanes, eight per 128-byte line.  Stored straight from the
+// column threads, each lane's piece was a request of its own, which tripled
+// the L2 requests of the row quantizer's bytes.  Padded rows read as zeros.
 #include "nvfp4_codec.hpp"
 
 namespace nvfp4moe {
 namespace {
 
-constexpr int kColTileRows = 64;
-constexpr int kColTileCols = 256;
+constexpr int kColTileRows = 256;  // padded rows per workgroup: 4 quarters of 64
+constexpr int kColTileCols = 64;
 
 // The expert whose padded segment holds padded row pr (grouped layout): the
 // last e with poff_e <= pr, offsets clamped to [0, M].
@@ -55,78 +61,161 @@ __global__ void fill_gscale_kernel(const float* __restrict__ amax, float* __rest
   if (i < n) g[i] = global_scale(amax[i]);
 }
 
+// Grouped layout: M source rows, padded extent Kp, E experts (UNIFORM:
+// false).  Uniform layout: E groups of L rows each (UNIFORM: true).  Work
+// tiles T = y * tiles_x + x (x: 256-row tile, y: 64-column tile) are taken
+// in a grid-stride loop; each workgroup loads its next tile into registers
+// while it encodes the current one from LDS.  Three workgroups per CU (the
+// register budget that holds the prefetched tile without spills).
 template <bool UNIFORM>
-__global__ __launch_bounds__(256) void colwise_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
+__global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                       const int32_t* __restrict__ off, int E, int64_t L,
                                                       const float* __restrict__ amax, uint8_t* __restrict__ q,
-                                                      uint8_t* __restrict__ s, float* __restrict__ gscale, int64_t Kp) {
+                                                      uint8_t* __restrict__ s, float* __restrict__ gscale, int64_t Kp,
+                                                      int64_t tiles_x, int64_t tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kColTileRows][kColTileCols];
-  __shared__ int64_t seg[4];  // expert, first source row, rows in the segment, segment-relative first row
+  // per work tile (two in flight) and quarter: expert (-1: nothing to
+  // write), first source row, rows in the segment, segment-relative first row
+  __shared__ int64_t seg[2][4][4];
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;              // 64-row tile of the padded row space
-  const int64_t n0 = (int64_t)blockIdx.y * kColTileCols;
-  if (tid == 0) {
-    if (UNIFORM) {
-      const int64_t tps = L / kColTileRows;
-      seg[0] = t / tps;
-      seg[1] = seg[0] * L;
-      seg[2] = L;
-      seg[3] = (t % tps) * kColTileRows;
-    } else {
-      const int e = find_padded_segment(off, E, M, t * kColTileRows);
-      int64_t lo = off[e], hi = off[e + 1];
-      lo = lo < 0 ? 0 : lo > M ? M : lo;
-      hi = hi < lo ? lo : hi > M ? M : hi;
-      seg[0] = e;
-      seg[1] = lo;
-      seg[2] = hi - lo;
-      seg[3] = t * kColTileRows - 64 * (lo / 64 + e);
+  const int64_t extent = UNIFORM ? (int64_t)E * L : Kp;
+
+  // threads 0..3: the quarters of work tile T
+  auto resolve = [&](int64_t T, int buf) {
+    const int64_t tx = T % tiles_x;
+    const int64_t pr = tx * kColTileRows + 64 * tid;   // the quarter's first padded row
+    int64_t e = -1, src0 = 0, cnt = 0, j0 = 0;
+    if (pr < extent) {
+      if (UNIFORM) {
+        e = pr / L;
+        src0 = e * L;
+        cnt = L;
+        j0 = pr - src0;
+      } else {
+        e = find_padded_segment(off, E, M, pr);
+        int64_t lo = off[e], hi = off[e + 1];
+        lo = lo < 0 ? 0 : lo > M ? M : lo;
+        hi = hi < lo ? lo : hi > M ? M : hi;
+        src0 = lo;
+        cnt = hi - lo;
+        j0 = pr - 64 * (lo / 64 + e);
+      }
+      // the segment's global scale, once (where its first block lies)
+      if (T < tiles_x && j0 == 0) gscale[UNIFORM ? e : 0] = global_scale(amax[UNIFORM ? e : 0]);
+      // a gap between padded segments (or before the first): nothing to
+      // write (uniform: never)
+      if (j0 < 0 || j0 >= (cnt + 63) / 64 * 64) e = -1;
     }
-  }
-  __syncthreads();
-  const int e = (int)seg[0];
-  const int64_t src0 = seg[1], cnt = seg[2], j0 = seg[3];
-  const float g = global_scale(amax[UNIFORM ? e : 0]);
-  if (tid == 0 && blockIdx.y == 0 && j0 == 0) gscale[UNIFORM ? e : 0] = g;
-  const int64_t padded = (cnt + 63) / 64 * 64;
-  if (j0 >= padded) return;  // a gap between padded segments: nothing to write (uniform: never)
+    seg[buf][tid][0] = e;
+    seg[buf][tid][1] = src0;
+    seg[buf][tid][2] = cnt;
+    seg[buf][tid][3] = j0;
+  };
+  // 256 rows x 8 chunks of 16 bytes, 8 per thread; rows past their segment,
+  // quarters with nothing to write and columns past N read as zeros
+  auto fetch = [&](int64_t T, int buf, uint4 (&r)[8]) {
+    const int64_t n0 = (T / tiles_x) * kColTileCols;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const int rr = c >> 3, ch = c & 7, qt = rr >> 6;
+      const int64_t row = seg[buf][qt][3] + (rr & 63), col = n0 + ch * 8;
+      r[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (seg[buf][qt][0] >= 0 && row < seg[buf][qt][2] && col < N)
+        r[i] = *reinterpret_cast<const uint4*>(x + (seg[buf][qt][1] + row) * N + col);
+    }
+  };
 
-  // Load: 64 rows x 32 chunks of 16 bytes, 8 per thread; rows past the
-  // segment and columns past N read as zeros.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 5, ch = c & 31;
-    const int64_t row = j0 + r, col = n0 + ch * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < cnt && col < N) v = *reinterpret_cast<const uint4*>(x + (src0 + row) * N + col);
-    *reinterpret_cast<uint4*>(&tile[r][ch * 8]) = v;
-  }
+  int64_t T = blockIdx.x;  // gridDim.x <= tiles: every workgroup has a first tile
+  int buf = 0;
+  if (tid < 4) resolve(T, 0);
   __syncthreads();
+  uint4 reg[8];
+  fetch(T, 0, reg);
+  for (; T < tiles; T += gridDim.x) {
+    const int64_t Tn = T + gridDim.x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(&tile[c >> 3][(c & 7) * 8]) = reg[i];
+    }
+    if (tid < 4 && Tn < tiles) resolve(Tn, buf ^ 1);
+    __syncthreads();  // the tile is in LDS; the next tile's quarters are known
+    if (Tn < tiles) fetch(Tn, buf ^ 1, reg);  // in flight while this tile is encoded
 
-  const int64_t n = n0 + tid;
-  if (n >= N) return;
-  uint32_t codes[8];
-  uint32_t sw = 0;
+    const int64_t tx = T % tiles_x, n0 = (T / tiles_x) * kColTileCols;
+    const int qt = tid >> 6, col = tid & 63;   // one wave per quarter
+    const int64_t e = seg[buf][qt][0];
+    const int64_t n = n0 + col;
+    uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t sw = 0;
+    if (e >= 0 && n < N) {
+      const float g = global_scale(amax[UNIFORM ? e : 0]);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    float v[16];
+      for (int b = 0; b < 4; ++b) {
+        float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __uint_as_float((uint32_t)tile[16 * b + i][tid] << 16);
-    uint2 c2;
-    uint32_t S;
-    quantize_block(v, g, c2, S);
-    codes[2 * b] = c2.x;
-    codes[2 * b + 1] = c2.y;
-    sw |= S << (8 * b);
+        for (int i = 0; i < 16; ++i) v[i] = __uint_as_float((uint32_t)tile[64 * qt + 16 * b + i][col] << 16);
+        uint2 c2;
+        uint32_t S;
+        quantize_block(v, g, c2, S);
+        codes[2 * b] = c2.x;
+        codes[2 * b + 1] = c2.y;
+        sw |= S << (8 * b);
+      }
+    }
+    // Stage the results by output row (column n) in the tile's LDS: 128 code
+    // bytes (quarter qt at byte 32 qt) and 16 scale bytes per column, so that
+    // the stores below write whole rows of consecutive bytes -- eight lanes
+    // per 128-byte line -- instead of one 16-byte piece per lane per line.
+    __syncthreads();  // every thread is done reading the tile
+    uint8_t* cst = reinterpret_cast<uint8_t*>(&tile[0][0]);  // [64][128] code bytes
+    uint8_t* sst = cst + 64 * 128;                           // [64][16] scale bytes
+    reinterpret_cast<uint4*>(cst + col * 128 + 32 * qt)[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    reinterpret_cast<uint4*>(cst + col * 128 + 32 * qt)[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+    *reinterpret_cast<uint32_t*>(sst + col * 16 + 4 * qt) = sw;
+    __syncthreads();
+    // element (segment e, column n, segment row j) sits at base + n * ld + j;
+    // grouped: quarter u's padded rows start at tx * 256 + 64 * u
+    auto at = [&](int u, int64_t nn) -> int64_t {
+      return UNIFORM ? seg[buf][u][0] * N * L + nn * L + seg[buf][u][3] : nn * Kp + tx * kColTileRows + 64 * u;
+    };
+    // codes: 64 rows x 8 chunks of 16 bytes (chunk c holds half c % 2 of quarter c / 2)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int idx = tid + 256 * p;
+      const int r = idx >> 3, c = idx & 7, u = c >> 1;
+      const int64_t nn = n0 + r;
+      if (seg[buf][u][0] >= 0 && nn < N)
+        *reinterpret_cast<uint4*>(q + at(u, nn) / 2 + 16 * (c & 1)) =
+            *reinterpret_cast<const uint4*>(cst + r * 128 + 16 * c);
+    }
+    // scales: 64 rows x 4 words
+    {
+      const int r = tid >> 2, u = tid & 3;
+      const int64_t nn = n0 + r;
+      if (seg[buf][u][0] >= 0 && nn < N)
+        *reinterpret_cast<uint32_t*>(s + at(u, nn) / 16) = *reinterpret_cast<const uint32_t*>(sst + r * 16 + 4 * u);
+    }
+    __syncthreads();  // the staging area is read before the next tile lands in LDS
+    buf ^= 1;
   }
-  // element (segment e, column n, segment row j) sits at base + n * ld + j
-  const int64_t base = UNIFORM ? (int64_t)e * N * L : 64 * (src0 / 64 + e);
-  const int64_t ld = UNIFORM ? L : Kp;
-  uint8_t* qd = q + (base + n * ld + j0) / 2;
-  reinterpret_cast<uint4*>(qd)[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-  reinterpret_cast<uint4*>(qd)[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
-  *reinterpret_cast<uint32_t*>(s + (base + n * ld + j0) / 16) = sw;
+}
+
+// Workgroups of the column-wise kernel: as many as are resident at once
+// (three per CU: 32 KB of LDS and up to 170 VGPRs each), at most one per
+// work tile, so that no workgroup starts its share late.
+template <bool UNIFORM>
+int64_t colwise_grid(int64_t tiles) {
+  static int per_cu = 0;
+  if (per_cu < 1) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, colwise_kernel<UNIFORM>, 256, 0) != hipSuccess || occ < 1)
+      occ = 1;
+    per_cu = occ;
+  }
+  const int64_t g = (int64_t)device_cu_count() * per_cu;
+  return tiles < g ? tiles : g;
 }
 
 }  // namespace
@@ -147,12 +236,12 @@ extern "C" int nvfp4_quantize_colwise(const void* x, int x_dtype, int64_t M_tota
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   hipStream_t st = as_stream(stream);
-  const int64_t tiles = Kp / 64 > 0 ? Kp / 64 : 1;
-  const int64_t ny = cdiv(N > 0 ? N : 1, kColTileCols);
-  if (ny > 65535) return NVFP4MOE_ESHAPE;
-  // Every tile is launched (also with N == 0: tile 0 writes the global scale).
-  colwise_kernel<false><<<dim3((unsigned)tiles, (unsigned)ny), 256, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), M_total, N, expert_offsets, E, 0, amax_in, q_t, s_t, gscale, Kp);
+  const int64_t tiles_x = cdiv(Kp > 0 ? Kp : 1, kColTileRows);
+  // Every row tile is visited (also with N == 0: row tile 0 writes the global scale).
+  const int64_t tiles = tiles_x * cdiv(N > 0 ? N : 1, kColTileCols);
+  colwise_kernel<false><<<(unsigned)colwise_grid<false>(tiles), 256, 0, st>>>(
+      reinterpret_cast<const uint16_t*>(x), M_total, N, expert_offsets, E, 0, amax_in, q_t, s_t, gscale, Kp, tiles_x,
+      tiles);
   return launch_status();
 }
 
@@ -182,9 +271,10 @@ extern "C" int nvfp4_quantize_transposed(const void* x, int x_dtype, int64_t gro
     fill_gscale_kernel<<<(unsigned)cdiv(groups, 256), 256, 0, st>>>(amax, gscale, groups);
     return launch_status();
   }
-  const int64_t ny = cdiv(N, kColTileCols);
-  if (ny > 65535) return NVFP4MOE_ESHAPE;
-  colwise_kernel<true><<<dim3((unsigned)(groups * (L / 64)), (unsigned)ny), 256, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), groups * L, N, nullptr, (int)groups, L, amax, q_t, s_t, gscale, 0);
+  const int64_t tiles_x = cdiv(groups * L, kColTileRows);
+  const int64_t tiles = tiles_x * cdiv(N, kColTileCols);
+  colwise_kernel<true><<<(unsigned)colwise_grid<true>(tiles), 256, 0, st>>>(
+      reinterpret_cast<const uint16_t*>(x), groups * L, N, nullptr, (int)groups, L, amax, q_t, s_t, gscale, 0, tiles_x,
+      tiles);
   return launch_status();
 }

@@ -55,6 +55,37 @@ def test_colwise_quantize_matches_oracle(counts, N):
     _check_colwise(q_t, s_t, g, x, off, amax / 4, ops.padded_extent(M, len(counts)))
 
 
+
+def test_colwise_tiles_straddle_experts_and_gaps_stay_unwritten():
+    """Expert segments of 10, 70, 1, 0, 130, 64 and 5 rows: padded segments at
+    columns 0, 64, 192, (256: empty), 320, 512 and 640, so one 256-column
+    work tile spans four experts, and columns 256..319 and 576..639 belong to
+    no segment.  Those gap columns keep the sentinel the outputs held."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    counts = [10, 70, 1, 0, 130, 64, 5]
+    rng = np.random.default_rng(21)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M, N = int(off[-1]), 136
+    x = workloads._bf16((rng.standard_normal((M, N)) * np.exp2(rng.integers(-2, 3, (M, 1)))).astype(np.float32))
+    amax = np.float32(np.abs(x).max())
+    Kp = ops.padded_extent(M, len(counts))
+    q_t = torch.full((N, Kp // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    s_t = torch.full((N, Kp // 16), 0xCD, dtype=torch.uint8, device="cuda")
+    q_t, s_t, g = ops.nvfp4_quantize_colwise(to_gpu(x, torch.bfloat16), to_gpu(off, torch.int32),
+                                             to_gpu(np.array([amax]), torch.float32), Kp=Kp, q_t=q_t, s_t=s_t)
+    torch.cuda.synchronize()
+    _check_colwise(q_t, s_t, g, x, off, amax, Kp)
+    poff = nvfp4.segment_pad_offset(off)
+    assert list(poff) == [0, 64, 192, 256, 320, 512, 640]
+    qn, sn = to_np(q_t), to_np(s_t)
+    covered = np.zeros(Kp, bool)
+    for e in range(len(counts)):
+        covered[poff[e]:poff[e] + -(-counts[e] // 64) * 64] = True
+    gap = ~covered
+    assert gap[256:320].all() and gap[576:640].all()
+    assert (qn[:, gap[0::2]] == 0xAB).all() and (sn[:, gap[0::16]] == 0xCD).all()
+
 def test_transposed_weights_match_oracle():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import moe_layer
