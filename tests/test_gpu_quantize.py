@@ -195,3 +195,33 @@ def test_deterministic_repeat():
     b = _gpu_quant(x, torch.bfloat16)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+def test_beyond_2_31_elements():
+    """A bf16 tensor of 262 147 x 8192 = 2 147 508 224 elements (4.3 GB),
+    just past 2^31: the amax pass and the quantizer address it with 64-bit
+    offsets.  The computed amax is checked against a host max streamed over
+    the whole tensor (its largest value planted in the last 16-byte word),
+    and rows on both sides of element 2^31, the first and the last rows,
+    against the oracle with that amax."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rows, K = 262147, 8192
+    assert rows * K > 2 ** 31
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    x = torch.randn(rows, K, device="cuda", generator=gen, dtype=torch.bfloat16)
+    x[rows - 1, K - 5] = -300.0
+    q, s, g, a = ops.nvfp4_quantize(x)
+    torch.cuda.synchronize()
+    m = np.float32(0.0)
+    for r0 in range(0, rows, 16384):
+        m = max(m, np.float32(np.abs(to_np(x[r0:r0 + 16384].float())).max()))
+    assert to_np(a)[0] == m == np.float32(300.0)
+    cross = 2 ** 31 // K                      # the row that holds element 2^31
+    sel = np.array([0, 1, cross - 1, cross, cross + 1, rows - 2, rows - 1])
+    idx = torch.as_tensor(sel, device="cuda")
+    rq, rs, rg, _ = nvfp4.quantize(to_np(x[idx].float()), amax=[m])
+    np.testing.assert_array_equal(to_np(q[idx]), rq)
+    np.testing.assert_array_equal(to_np(s[idx]), rs)
+    assert to_np(g).view(np.uint32)[0] == rg.view(np.uint32)[0]
