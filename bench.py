@@ -717,6 +717,12 @@ def kernel_stats_summary(d):
                          float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
                          float(r["Percentage"])))
     rows.sort(key=lambda r: -r[2])
+    print("# Kernel statistics of the default bench run (moe_8k_update: 5 warm-up and 20 timed steps, plus the\n"
+          "# side measurements), durations in microseconds.\n"
+          "# command ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&\n"
+          "#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_kt -o kt -- python $REPO/bench.py,\n"
+          "#   then python $REPO/bench.py --kernel-stats-summary $OUT/prof_kt\n"
+          "sources %s" % source_digest())
     print("%-72s %6s %11s %10s %10s %10s %6s" % ("kernel", "calls", "total_us", "avg_us", "min_us", "max_us", "pct"))
     for n, c, t, a, lo, hi, p in rows:
         n = n.replace("(anonymous namespace)::", "")
@@ -739,6 +745,12 @@ def dispatch_summary(d, name):
                 continue
             key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
             groups.setdefault(key, []).append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+    print("# Per-launch durations of the kernels named %r in the kernel trace of the default bench run,\n"
+          "# grouped by grid size (one group per tensor size), in microseconds.\n"
+          "# command ($REPO: the repository, $OUT: any output directory): cd /tmp && export TMPDIR=/tmp &&\n"
+          "#   rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_kt -o kt -- python $REPO/bench.py,\n"
+          "#   then python $REPO/bench.py --dispatch-summary $OUT/prof_kt %s\n"
+          "sources %s" % (name, name, source_digest()))
     print("%-40s %14s %6s %10s %10s %10s" % ("kernel", "work-items", "calls", "median_us", "min_us", "max_us"))
     for (kn, grid), ts in sorted(groups.items(), key=lambda kv: kv[0][1]):
         ts.sort()
