@@ -30,7 +30,7 @@ def test_dispatch_summary_groups_by_grid(tmp_path, capsys):
             [k, 0, 50000, 1024, 1, 1], ["other_kernel(int)", 0, 99000, 256, 1, 1]]
     _write(str(tmp_path / "run" / "kt_kernel_trace.csv"), hdr, rows)
     bench.dispatch_summary(str(tmp_path), "quantize_kernel")
-    out = capsys.readouterr().out.splitlines()
+    out = [l for l in capsys.readouterr().out.splitlines() if not l.startswith(("#", "sources "))]
     assert len(out) == 3                                    # header + two grid sizes
     first = out[1].split()
     assert first[0] == "quantize_kernel<256,true>" and first[1] == "256" and first[2] == "3"
@@ -43,7 +43,10 @@ def test_kernel_stats_summary_sorts_by_total(tmp_path, capsys):
     _write(str(tmp_path / "kt_kernel_stats.csv"), hdr,
            [["small", 2, 2000, 1000, 900, 1100, 10.0], ["big", 1, 18000, 18000, 18000, 18000, 90.0]])
     bench.kernel_stats_summary(str(tmp_path))
-    out = capsys.readouterr().out.splitlines()
+    lines = capsys.readouterr().out.splitlines()
+    assert any(l.startswith("# command") for l in lines)           # names the command that made it
+    assert ("sources " + bench.source_digest()) in lines
+    out = [l for l in lines if not l.startswith(("#", "sources "))]
     assert out[1].split()[0] == "big" and out[2].split()[0] == "small"
     assert float(out[1].split()[3]) == 18.0
 
