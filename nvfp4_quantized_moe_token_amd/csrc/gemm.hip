@@ -965,6 +965,8 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
                   for (int j = 0; j < FN; ++j) bv[buf][j] = nv_expand(fb[j], kk);
                 };
                 expand(0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NA + FN), 0);  // the fragment reads,
+                __builtin_amdgcn_sched_group_barrier(0x002, 8 * (NA + FN), 0);  // then the first expansion
 #pragma unroll
                 for (int kk = 0; kk < BK / 16; ++kk) {
                   if (kk + 1 < BK / 16) expand(kk + 1, (kk + 1) & 1);
