@@ -515,7 +515,8 @@ struct IntConst {
 };
 // Quantized operand regions of a row-grouped tile: A rows [m0, m_end) (codes
 // and scales); B the n-tile's rows of the expert (SiLU-gate tiles gather gate
-// and up rows: the region is the whole expert).  Bytes per row: NVFP4 codes
+// and up rows: the region runs from the tile's first gate row to the end of
+// the expert, so a row's offset in it does not depend on the tile).  Bytes per row: NVFP4 codes
 // K/2 and scales K/16 for both operands; MX (W4A8) A codes K (fp8), B codes
 // K/2 (fp4), scales K/32 for both.
 template <bool MX>
@@ -528,8 +529,8 @@ __device__ __forceinline__ void nv_a_regions(const Params& p, int64_t m0, int64_
 template <int BN, bool SILU, bool MX>
 __device__ __forceinline__ void nv_b_regions(const Params& p, int expert, int64_t n0, __amdgpu_buffer_rsrc_t& rb,
                                              __amdgpu_buffer_rsrc_t& rsb) {
-  const int64_t nv = SILU ? p.N : p.N - n0 < BN ? p.N - n0 : BN;
-  const int64_t brow = (int64_t)expert * p.N + (SILU ? 0 : n0);
+  const int64_t nv = SILU ? p.N - n0 / 2 : p.N - n0 < BN ? p.N - n0 : BN;
+  const int64_t brow = (int64_t)expert * p.N + (SILU ? n0 / 2 : n0);
   const int64_t sb = MX ? p.K / 32 : p.K / 16;
   rb = make_rsrc(reinterpret_cast<const uint8_t*>(p.b) + brow * (p.K / 2), nv * (p.K / 2));
   rsb = make_rsrc(p.bs + brow * sb, nv * sb);
@@ -598,6 +599,40 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
 
   float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
 
+  // NVFP4 stages: a lane's byte offsets in the regions of a tile are the same
+  // for every tile and step (A and B regions start at the tile's first rows;
+  // a step adds k0/2 code and k0/16 scale bytes), so they are computed once.
+  // Code bytes past the reduction's end are loaded unmasked: they land in the
+  // chunks of the last stage that the MFMA loop skips, and every byte past a
+  // region still reads as zero.
+  constexpr int NVA = NV ? KMajorLoader<BM, NW>::N_INSTR : 1;
+  constexpr int NVB = NV ? KMajorLoader<BN, NW>::N_INSTR : 1;
+  uint32_t nv_oa[NVA], nv_ob[NVB], nv_os[SC_INSTR > 0 ? SC_INSTR : 1];
+  if constexpr (NV) {
+    const int64_t rowb = MODE == W4A4_TN ? p.kp / 2 : p.K / 2;  // code bytes per row
+    const int64_t sld = MODE == W4A4_TN ? p.kp / 16 : p.K / 16;  // scale bytes per row
+    const int64_t gf = SILU ? p.N / 2 : 0;
+    constexpr int RPL = KMajorLoader<BM, NW>::RPL, CPR = KMajorLoader<BM, NW>::CPR;
+#pragma unroll
+    for (int i = 0; i < NVA; ++i) {
+      const int row = (wid + NW * i) * RPL + lane / CPR;
+      nv_oa[i] = (uint32_t)(row * rowb + (((lane % CPR) ^ kswz(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NVB; ++i) {
+      const int row = (wid + NW * i) * RPL + lane / CPR;
+      const int64_t grow = gf > 0 ? gate_up_row(row, gf, 0) : row;
+      nv_ob[i] = (uint32_t)(grow * rowb + (((lane % CPR) ^ kswz(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < SC_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const bool is_a = idx * 64 < BM;
+      const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+      nv_os[i] = (uint32_t)((!is_a && gf > 0 ? gate_up_row(row, gf, 0) : row) * sld);
+    }
+  }
+
   // Plain W4A4 with bf16 output (PF): the next tile's first stage is loaded
   // during the current tile's last step, into the ring slot that step does
   // not read, and the epilogue stages its results through the other slot.
@@ -610,12 +645,17 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
   // scheme raised register spills and measured slower, so they keep the
   // plain loop.
   constexpr bool PF = MODE == W4A4 && !OUT32 && S == 2;
+  // The SiLU-gate kernels prefetch the same way, right after the k-loop
+  // instead of during the last step (which raised register spills), and
+  // stage their epilogue through the slot of the tile's last stage.
+  constexpr bool PF2 = (MODE == W4A4_SILU || MODE == W4A4_SILU_Q) && S == 2;
+  constexpr bool PFX = PF || PF2;
   // Every layout keeps a copy of the expert offsets in LDS (up to 1024
   // experts), so the per-tile lookups read LDS rather than global memory.
   constexpr int kOffLds = 1025;
   __shared__ int32_t s_off[kOffLds];
   const bool off_in_lds = p.E < kOffLds;
-  const bool pf_on = PF && off_in_lds;
+  const bool pf_on = PFX && off_in_lds;
   if (off_in_lds) {
     for (int i = threadIdx.x; i <= p.E; i += NW * 64) s_off[i] = p.offsets[i];
     __syncthreads();
@@ -652,7 +692,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         poff = 64 * ((int64_t)lo / 64 + expert);
         red = (red + 63) / 64 * 64;
       }
-    } else if (PF && pre) {
+    } else if (PFX && pre) {
       // Found (and its first stage loaded) during the previous tile.
       expert = nx_e;
       m0 = nx_r0;
@@ -725,41 +765,38 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       const uint32_t voff = lane < 2 * BLoad::N_INSTR && rr < red ? (uint32_t)((lo + rr) * 4) : kOOB;
       dma4(rix, (uint32_t)(uintptr_t)(const lds_void_t*)gidx + (wid * S + (int)(s % S)) * 256, voff);
     };
-    // One NVFP4 stage (codes and scales of A and B) of a tile with the given
-    // regions into the LDS stage at byte address st.
+    // One quantized stage (codes and scales of A and B) of a tile with the
+    // given regions into the LDS stage at byte address st.
     auto nv_load = [&](__amdgpu_buffer_rsrc_t ra_, __amdgpu_buffer_rsrc_t rb_, __amdgpu_buffer_rsrc_t rsa_,
-                       __amdgpu_buffer_rsrc_t rsb_, int64_t j0_, int64_t k0, uint32_t st) {
+                       __amdgpu_buffer_rsrc_t rsb_, int64_t k0, uint32_t st) {
       if constexpr (MX) {
         // fp8 A codes: 128 bytes (128 elements) per row, a K-major tile of
         // 64 16-bit units per row; fp4 B codes: 64 bytes per row.
         KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 2, k0 / 2, p.K / 2);
-        KMajorLoader<BN, NW, 64>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, j0_);
+        KMajorLoader<BN, NW, 64>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, 0);
         // E8M0 scales: 4 bytes per row (one word), 64 rows per load, A rows first.
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
           const int idx = wid + NW * i;
           const bool is_a = idx * 64 < BM;
           const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
+          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, 0) : row;
           dma4(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 256, (uint32_t)(grow * (p.K / 32) + k0 / 32));
         }
       } else {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
-        // bf16 tile of 64 16-bit units per row.  W4A4_TN rows are kp long
-        // and hold `red` reduction elements of this expert.
-        const int64_t qld = MODE == W4A4_TN ? p.kp / 4 : p.K / 4;
-        const int64_t qlim = MODE == W4A4_TN ? red / 4 : p.K / 4;
-        KMajorLoader<BM, NW>::load(st, wid, ra_, qld, k0 / 4, qlim);
-        KMajorLoader<BN, NW>::load(st + A_BYTES, wid, rb_, qld, k0 / 4, qlim, gate_f, j0_);
-        const int64_t sld = MODE == W4A4_TN ? p.kp / 16 : p.K / 16;
-        // Scales: 16 bytes per row, 64 rows per load, A rows first.
+        // bf16 tile of 64 16-bit units per row; scales: 16 bytes per row, 64
+        // rows per load, A rows first.  The lanes' offsets are nv_oa, nv_ob
+        // and nv_os; a step adds k0/2 code and k0/16 scale bytes.
+        const uint32_t kc = (uint32_t)(k0 / 2), ksc = (uint32_t)(k0 / 16);
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) dma16(ra_, st + (wid + NW * i) * 1024, nv_oa[i] + kc);
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) dma16(rb_, st + A_BYTES + (wid + NW * i) * 1024, nv_ob[i] + kc);
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
           const int idx = wid + NW * i;
-          const bool is_a = idx * 64 < BM;
-          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, j0_) : row;
-          dma16(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, (uint32_t)(grow * sld + k0 / 16));
+          dma16(idx * 64 < BM ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 1024, nv_os[i] + ksc);
         }
       }
     };
@@ -791,7 +828,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
         index_load(kt + S - 1);
       } else {
-        nv_load(ra, rb, rsa, rsb, j0, k0, st);
+        nv_load(ra, rb, rsa, rsb, k0, st);
       }
     };
 
@@ -819,7 +856,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // space), so that no vector-memory wait -- which would also wait for the
     // previous epilogue's stores or the prefetched stage -- comes from them.
     float alpha_t = 1.0f;
-    if constexpr (PF) {
+    if constexpr (PFX) {
       typedef __attribute__((address_space(4))) const float const_f32_t;
       const_f32_t* ag = (const_f32_t*)p.ag;
       const_f32_t* bg = (const_f32_t*)p.bg;
@@ -827,8 +864,27 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     }
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
-      if (s < nk && !(PF && pre && s == 0)) load_step(s, (slot0 + s) % S);
+      if (s < nk && !(PFX && pre && s == 0)) load_step(s, (slot0 + s) % S);
     bool pre_next = false;
+    // Find the next tile (every wave, from the LDS offsets) and load its
+    // first stage into ring slot (slot0 + nk) % S.
+    auto prefetch_next = [&]() {
+      int e = -1, nt = 0;
+      int64_t r0 = 0, r1 = 0;
+      const bool ok = find_tile<BM, kNMajor>(off_lds, p.E, p.M, L + t_step, p.n_tiles, e, r0, r1, nt);
+      // The lookup is wave-uniform; say so, so that the regions stay scalar.
+      if (__builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0) {
+        nx_e = __builtin_amdgcn_readfirstlane(e);
+        nx_nt = __builtin_amdgcn_readfirstlane(nt);
+        nx_r0 = uniform64(r0);
+        nx_r1 = uniform64(r1);
+        __amdgpu_buffer_rsrc_t na, nb, nsa, nsb;
+        nv_a_regions<MX>(p, nx_r0, nx_r1, na, nsa);
+        nv_b_regions<BN, SILU, MX>(p, nx_e, (int64_t)nx_nt * BN, nb, nsb);
+        nv_load(na, nb, nsa, nsb, 0, smem_lds + (uint32_t)((slot0 + nk) % S) * STAGE);
+        pre_next = true;
+      }
+    };
 
     for (int64_t kt = 0; kt < nk; ++kt) {
       // This wave's loads for step kt are done once at most `ahead` later
@@ -837,7 +893,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       // prefetched first stage is followed only by the previous epilogue's
       // nst stores, which may stay outstanding.
       const int64_t ahead = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
-      if (PF && pre && kt == 0)
+      if (PFX && pre && kt == 0)
         wait_vmcnt_upto<kMaxEpilogueStores>(nst);
       else
         wait_steps_ahead<S - 2, NDMA>((int)ahead);
@@ -853,23 +909,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       if constexpr (PF) {
         // Last step: find the next tile (every wave, from the LDS offsets)
         // and load its first stage into the slot this step does not read.
-        if (pf_on && kt == nk - 1 && L + t_step < t_end) {
-          int e = -1, nt = 0;
-          int64_t r0 = 0, r1 = 0;
-          const bool ok = find_tile<BM, kNMajor>(off_lds, p.E, p.M, L + t_step, p.n_tiles, e, r0, r1, nt);
-          // The lookup is wave-uniform; say so, so that the regions stay scalar.
-          if (__builtin_amdgcn_readfirstlane(ok ? 1 : 0) != 0) {
-            nx_e = __builtin_amdgcn_readfirstlane(e);
-            nx_nt = __builtin_amdgcn_readfirstlane(nt);
-            nx_r0 = uniform64(r0);
-            nx_r1 = uniform64(r1);
-            __amdgpu_buffer_rsrc_t na, nb, nsa, nsb;
-            nv_a_regions<MX>(p, nx_r0, nx_r1, na, nsa);
-            nv_b_regions<BN, SILU, MX>(p, nx_e, (int64_t)nx_nt * BN, nb, nsb);
-            nv_load(na, nb, nsa, nsb, (int64_t)nx_nt * BN / 2, 0, smem_lds + (uint32_t)((slot0 + nk) % S) * STAGE);
-            pre_next = true;
-          }
-        }
+        if (pf_on && kt == nk - 1 && L + t_step < t_end) prefetch_next();
       }
 
       const uint8_t* st = smem + (int)((slot0 + kt) % S) * STAGE;
@@ -1080,6 +1120,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       if (kLateLoads && !loads_issued && kt + S - 1 < nk) load_step(kt + S - 1, (int)((slot0 + kt + S - 1) % S));
       if constexpr (NV) __builtin_amdgcn_s_setprio(0);
     }
+    if constexpr (PF2) {
+      if (pf_on && L + t_step < t_end) prefetch_next();
+      nst = 0;
+    }
 
     // Epilogue.  Register r of lane l of a 32x32 MFMA result holds result row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 (probed on the device).  The
@@ -1088,7 +1132,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     // four consecutive output columns 8*g + 4*(l/32) + 0..3 in registers
     // 4g..4g+3 -- one 8-byte (bf16) or 16-byte (fp32) store each.
     float alpha = 1.0f;
-    if (PF) alpha = alpha_t;
+    if (PFX) alpha = alpha_t;
     else if (MODE == W4A4_TN) alpha = p.ag[0] * p.bg[0];
     else if (NV) alpha = p.ag[0] * p.bg[expert];
     const int64_t ldc = p.N;
@@ -1113,9 +1157,12 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       constexpr int FW = WTN / 2;                // features per wave
       constexpr int CH = FW / 8;                 // 16-byte chunks per row and part
       constexpr int PART = 32 * FW * 2;
-      static_assert(!PF && NW * 2 * PART <= S * STAGE && (CH & (CH - 1)) == 0 && 64 % CH == 0, "SiLU staging");
+      static_assert(!PF && NW * 2 * PART <= (PF2 ? STAGE : S * STAGE) && (CH & (CH - 1)) == 0 && 64 % CH == 0,
+                    "SiLU staging");
       lds_barrier();  // the stage ring is free: every wave is past its last step
-      uint8_t* reg = smem + wid * 2 * PART;
+      // PF2: in the slot of the tile's last stage (the other one holds the
+      // next tile's first stage).
+      uint8_t* reg = (PF2 ? smem + (int)((slot0 + nk - 1) % S) * STAGE : smem) + wid * 2 * PART;
       const int q = lane & 31, hh = lane >> 5;
       const int64_t f0 = j0 + wn * FW;
 #pragma unroll
@@ -1149,6 +1196,9 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
           for (int w = 0; w < 4; ++w)
             hw[w] = pack_bf16x2(silu_gate(bf16_lo(gw[w]), bf16_lo(uw[w])), silu_gate(bf16_hi(gw[w]), bf16_hi(uw[w])));
           const bool valid = row < m_end;
+          // PF2: count this wave's stores (a store with no active lane is
+          // not counted, so the count never exceeds what is outstanding)
+          if constexpr (PF2) nst += __ballot(valid) != 0 ? (C16 ? 2 : 0) + (Hp ? 1 : 0) : 0;
           if (valid) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(hw[w])), fabsf(bf16_hi(hw[w]))));
@@ -1178,6 +1228,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
               float d;
               block_scale(a, h_g, sbyte, d);
               const uint32_t codes = encode8(hv, d);
+              if constexpr (PF2) nst += (__ballot(valid) != 0 ? 1 : 0) + (__ballot(valid && (ch & 1) == 0) != 0 ? 1 : 0);
               if (valid) {
                 *reinterpret_cast<uint32_t*>(p.hq + row * (F / 2) + f / 2) = codes;
                 if ((ch & 1) == 0) p.hs[row * (F / 16) + f / 16] = (uint8_t)sbyte;
@@ -1187,6 +1238,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
         }
       }
       silu_amax = fmaxf(silu_amax, m);
+      if constexpr (PF2) {
+        slot0 = (int)((slot0 + nk) % S);
+        pre = pre_next;
+      }
       continue;
     }
     // The wave's results leave through a private LDS region (the stage ring
