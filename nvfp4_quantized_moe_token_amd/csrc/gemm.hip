@@ -599,16 +599,41 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
 
   float silu_amax = 0.0f;  // W4A4_SILU: this lane's max |H| over its tiles
 
-  // NVFP4 stages: a lane's byte offsets in the regions of a tile are the same
-  // for every tile and step (A and B regions start at the tile's first rows;
-  // a step adds k0/2 code and k0/16 scale bytes), so they are computed once.
-  // Code bytes past the reduction's end are loaded unmasked: they land in the
-  // chunks of the last stage that the MFMA loop skips, and every byte past a
-  // region still reads as zero.
-  constexpr int NVA = NV ? KMajorLoader<BM, NW>::N_INSTR : 1;
-  constexpr int NVB = NV ? KMajorLoader<BN, NW>::N_INSTR : 1;
+  // Quantized stages: a lane's byte offsets in the regions of a tile are the
+  // same for every tile and step (A and B regions start at the tile's first
+  // rows; a step adds a fixed number of bytes per row), so they are computed
+  // once.  NVFP4 code bytes past the reduction's end are loaded unmasked:
+  // they land in the chunks of the last stage that the MFMA loop skips
+  // (MX stages are always whole), and every byte past a region still reads
+  // as zero.
+  constexpr int NVA = QM ? KMajorLoader<BM, NW>::N_INSTR : 1;
+  constexpr int NVB = NV ? KMajorLoader<BN, NW>::N_INSTR : MX ? KMajorLoader<BN, NW, 64>::N_INSTR : 1;
   uint32_t nv_oa[NVA], nv_ob[NVB], nv_os[SC_INSTR > 0 ? SC_INSTR : 1];
-  if constexpr (NV) {
+  if constexpr (MX) {
+    const int64_t gf = SILU ? p.N / 2 : 0;
+    // fp8 A: K bytes per row (128-byte chunk rows); fp4 B: K/2 bytes per row
+    // (64-byte chunk rows); E8M0 scales: K/32 bytes per row.
+#pragma unroll
+    for (int i = 0; i < NVA; ++i) {
+      constexpr int RPL = KMajorLoader<BM, NW>::RPL, CPR = KMajorLoader<BM, NW>::CPR;
+      const int row = (wid + NW * i) * RPL + lane / CPR;
+      nv_oa[i] = (uint32_t)(row * p.K + (((lane % CPR) ^ kswz(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < NVB; ++i) {
+      constexpr int RPL = KMajorLoader<BN, NW, 64>::RPL, CPR = KMajorLoader<BN, NW, 64>::CPR;
+      const int row = (wid + NW * i) * RPL + lane / CPR;
+      const int64_t grow = gf > 0 ? gate_up_row(row, gf, 0) : row;
+      nv_ob[i] = (uint32_t)(grow * (p.K / 2) + (((lane % CPR) ^ rswz<64>(row)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < SC_INSTR; ++i) {
+      const int idx = wid + NW * i;
+      const bool is_a = idx * 64 < BM;
+      const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
+      nv_os[i] = (uint32_t)((!is_a && gf > 0 ? gate_up_row(row, gf, 0) : row) * (p.K / 32));
+    }
+  } else if constexpr (NV) {
     const int64_t rowb = MODE == W4A4_TN ? p.kp / 2 : p.K / 2;  // code bytes per row
     const int64_t sld = MODE == W4A4_TN ? p.kp / 16 : p.K / 16;  // scale bytes per row
     const int64_t gf = SILU ? p.N / 2 : 0;
@@ -771,17 +796,17 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
                        __amdgpu_buffer_rsrc_t rsb_, int64_t k0, uint32_t st) {
       if constexpr (MX) {
         // fp8 A codes: 128 bytes (128 elements) per row, a K-major tile of
-        // 64 16-bit units per row; fp4 B codes: 64 bytes per row.
-        KMajorLoader<BM, NW>::load(st, wid, ra_, p.K / 2, k0 / 2, p.K / 2);
-        KMajorLoader<BN, NW, 64>::load(st + A_BYTES, wid, rb_, p.K / 4, k0 / 4, p.K / 4, gate_f, 0);
-        // E8M0 scales: 4 bytes per row (one word), 64 rows per load, A rows first.
+        // 64 16-bit units per row; fp4 B codes: 64 bytes per row; E8M0
+        // scales: 4 bytes per row (one word), 64 rows per load, A rows first.
+        // A step adds k0 A, k0/2 B and k0/32 scale bytes.
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) dma16(ra_, st + (wid + NW * i) * 1024, nv_oa[i] + (uint32_t)k0);
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) dma16(rb_, st + A_BYTES + (wid + NW * i) * 1024, nv_ob[i] + (uint32_t)(k0 / 2));
 #pragma unroll
         for (int i = 0; i < SC_INSTR; ++i) {
           const int idx = wid + NW * i;
-          const bool is_a = idx * 64 < BM;
-          const int row = (is_a ? idx * 64 : idx * 64 - BM) + lane;
-          const int64_t grow = !is_a && gate_f > 0 ? gate_up_row(row, gate_f, 0) : row;
-          dma4(is_a ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 256, (uint32_t)(grow * (p.K / 32) + k0 / 32));
+          dma4(idx * 64 < BM ? rsa_ : rsb_, st + A_BYTES + B_BYTES + idx * 256, nv_os[i] + (uint32_t)(k0 / 32));
         }
       } else {
         // Codes: 128 bytes (256 elements) per row, laid out like a K-major
