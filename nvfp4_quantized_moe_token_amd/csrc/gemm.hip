@@ -827,7 +827,12 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     };
     auto load_step = [&](int64_t kt, int stage) {
       const uint32_t st = smem_lds + stage * STAGE;
-      const int64_t k0 = kt * KS;
+      // The step's first reduction element, kept opaque to induction-variable
+      // rewriting: per-lane offsets carried across the k-loop started from
+      // spill reloads before it, and the compiler then guarded every step
+      // with a wait that also drained the LDS-direct loads in flight, which
+      // it does not count.
+      const int64_t k0 = (int64_t)__builtin_amdgcn_readfirstlane((int)(kt * KS));
       if constexpr (MODE == NT_BF16) {
         KMajorLoader<BM, NW, BKB * 2>::load(st, wid, ra, p.K, k0, p.K);
         KMajorLoader<BN, NW, BKB * 2>::load(st + A_BYTES, wid, rb, p.K, k0, p.K);
