@@ -240,13 +240,15 @@ __device__ int count_row_blocks(const int32_t* __restrict__ off, int E, int64_t 
 // Tile L of the row-grouped layouts: its expert, row range and n-tile.  The
 // tiles of one expert are numbered n-tile-major when NMAJOR (the expert's
 // row blocks that share a weight panel are neighbours, so they run side by
-// side on one XCD), row-block-major otherwise.
+// side on one XCD), row-block-major otherwise.  Tile numbers stay below 2^31
+// (checked at launch), so the divisions are 32-bit ones.
 template <int BM, bool NMAJOR, class OffPtr>
-__device__ bool find_tile(OffPtr off, int E, int64_t M, int64_t L, int n_tiles, int& e_out,
+__device__ bool find_tile(OffPtr off, int E, int64_t M, int64_t L64, int n_tiles, int& e_out,
                           int64_t& r0, int64_t& r1, int& n_out) {
   const int lane = threadIdx.x & 63;
-  const int64_t slot = L / n_tiles;  // the expert's tiles span its row blocks x n_tiles
-  int64_t running = 0;
+  const uint32_t L = (uint32_t)L64, nt = (uint32_t)n_tiles;
+  const uint32_t slot = L / nt;  // the expert's tiles span its row blocks x n_tiles
+  uint32_t running = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
     int lo = 0, hi = 0, cnt = 0;
@@ -260,25 +262,25 @@ __device__ bool find_tile(OffPtr off, int E, int64_t M, int64_t L, int n_tiles, 
       const int v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    const int total = __shfl(incl, 63, 64);
+    const uint32_t total = (uint32_t)__shfl(incl, 63, 64);
     if (slot < running + total) {
       const bool mine = slot >= running + incl - cnt && slot < running + incl;
       const uint64_t mask = __ballot(mine);
       const int srcl = __ffsll((unsigned long long)mask) - 1;
       e_out = __shfl(e, srcl, 64);
       const int lo_s = __shfl(lo, srcl, 64), hi_s = __shfl(hi, srcl, 64), ex = __shfl(incl - cnt, srcl, 64);
-      const int cnt_s = __shfl(cnt, srcl, 64);
-      const int64_t rb0 = running + ex;  // the expert's first row block
-      int64_t rb;
+      const uint32_t cnt_s = (uint32_t)__shfl(cnt, srcl, 64);
+      const uint32_t rb0 = running + (uint32_t)ex;  // the expert's first row block
+      uint32_t rb;
       if (NMAJOR) {
-        const int64_t t = L - rb0 * n_tiles;
+        const uint32_t t = L - rb0 * nt;
         n_out = (int)(t / cnt_s);
         rb = t % cnt_s;
       } else {
-        n_out = (int)(L % n_tiles);
+        n_out = (int)(L % nt);
         rb = slot - rb0;
       }
-      r0 = lo_s + rb * BM;
+      r0 = lo_s + (int64_t)rb * BM;
       r1 = r0 + BM < hi_s ? r0 + BM : hi_s;
       return true;
     }
@@ -700,9 +702,10 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
     int64_t poff = 0;   // W4A4_TN: the expert's first column in the transposed operands
     lds_barrier();      // previous tile: every wave is done with LDS and s_tile
     if (is_tn(MODE)) {
-      const int per_e = p.k_tiles_tn * p.n_tiles;
-      expert = (int)(L / per_e);
-      const int rem = (int)(L % per_e);
+      // 32-bit divisions: tile numbers stay below 2^31 (checked at launch)
+      const uint32_t per_e = (uint32_t)(p.k_tiles_tn * p.n_tiles);
+      expert = (int)((uint32_t)L / per_e);
+      const int rem = (int)((uint32_t)L % per_e);
       m0 = (int64_t)(rem / p.n_tiles) * BM;
       m_end = p.K;
       n0 = (int64_t)(rem % p.n_tiles) * BN;
