@@ -1098,6 +1098,11 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
             __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
 #pragma unroll
             for (int c = 0; c < KS / BK; ++c) {
+              // the wave behind in the stage issues first (as in the NVFP4 loop)
+              if (c == 0)
+                __builtin_amdgcn_s_setprio(1);
+              else
+                __builtin_amdgcn_s_setprio(0);
               if (c + 1 < KS / BK) read_frags(c + 1, (c + 1) & 1);
 #pragma unroll
               for (int i = 0; i < NA; ++i)
@@ -1151,7 +1156,7 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
       };
       if (n_active > 0) compute(IntConst<FM>{});
       if (kLateLoads && !loads_issued && kt + S - 1 < nk) load_step(kt + S - 1, (int)((slot0 + kt + S - 1) % S));
-      if constexpr (NV) __builtin_amdgcn_s_setprio(0);
+      if constexpr (NV || MX) __builtin_amdgcn_s_setprio(0);
     }
     if constexpr (PF2) {
       if (pf_on && L + t_step < t_end) prefetch_next();
