@@ -36,11 +36,24 @@ def _w(t):
     return (t["aq"], t["as_"], t["ag"], t["bq"], t["bs"], t["bg"], t["offs"])
 
 
+def _many(seed, E, hi):
+    counts = np.random.default_rng(seed).integers(0, hi, E)
+    counts[::7] = 0
+    return [int(c) for c in counts]
+
+
+_MANY_1 = _many(5, 300, 120)   # ~510 tiles: every workgroup runs several in a row
+_MANY_2 = _many(6, 160, 300)   # ~480 tiles of three steps, the last one partial
+
 CASES = [
     (300, 128, 192, [0, 1, 200, 0, 99]),      # empty experts, a 1-row expert, ragged row tails
     (770, 256, 128, [256, 1, 257, 256]),      # 256-row tile boundaries, two gate/up tile pairs
     (257, 384, 256, [257]),                   # one expert, three tile pairs, one row past two tiles
     (512, 768, 2048, [100, 300, 0, 112]),     # the model's FFN width and d_model
+    # more tiles than workgroups: the next tile's first stage is loaded after
+    # each tile's last step (and its offsets are the tile-independent ones)
+    (sum(_MANY_1), 256, 128, _MANY_1),
+    (sum(_MANY_2), 384, 640, _MANY_2),
 ]
 
 
