@@ -118,6 +118,38 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t 
                    float* gscale, int32_t* status, nvfp4moe_stream_t stream);
 
 /*
+ * nvfp4_quantize_onepass -- nvfp4_quantize with the amax computed
+ * (amax_in = NULL), reading x once instead of twice: the same outputs, bit
+ * for bit.  Meant for stacked expert weights (groups = E), which are
+ * quantized once per optimizer step (scaling scheme and amax reuse: [RU]
+ * fast-kernels section, [JA] fourth paragraph).
+ *
+ * Each group is cut into slices of 1024 blocks of 16.  The workgroups of a
+ * group's slices keep their slice in registers and publish its amax in a
+ * slot of `workspace`; once every slot of the group is filled they encode
+ * with the group's amax.  A workgroup that finds the group incomplete after
+ * a bounded wait reads the whole group for its amax instead, so the results
+ * never depend on scheduling (the environment variable
+ * NVFP4MOE_ONEPASS_POLL_LIMIT, read at each call, overrides the bound; 0
+ * takes that path at once, for tests).  Groups larger than what the device
+ * holds in flight at once (about 16 M elements on MI355X) take the two-pass
+ * path inside the call, with the same results.
+ *
+ *   x, x_dtype, rows, K, groups, q, scales, gscale: as for nvfp4_quantize.
+ *   amax_out  [groups] fp32 out (required): the amax of each group.
+ *   workspace device scratch of nvfp4_quantize_onepass_workspace_size(rows,
+ *             K, groups) bytes (4-byte aligned; may be NULL when that size
+ *             is 0).  Its contents on entry do not matter; calls that share
+ *             one workspace must not overlap.
+ * Errors: as nvfp4_quantize; EWORKSPACE when the workspace is missing or
+ * too small.
+ */
+size_t nvfp4_quantize_onepass_workspace_size(int64_t rows, int64_t K, int64_t groups);
+int nvfp4_quantize_onepass(const void* x, int x_dtype, int64_t rows, int64_t K, int64_t groups, float* amax_out,
+                           uint8_t* q, uint8_t* scales, float* gscale, void* workspace, size_t workspace_bytes,
+                           nvfp4moe_stream_t stream);
+
+/*
  * moe_permute -- routing metadata for the contiguous per-expert layout and
  * (optionally) the row gather into it, with the amax of the gathered rows
  * fused in (contiguous layout, device-side metadata, amax reuse: [JA],

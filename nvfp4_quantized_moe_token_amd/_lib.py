@@ -17,6 +17,9 @@ SIGNATURES = {
     "nvfp4moe_abi_version": (c_int, []),
     "nvfp4moe_status_string": (c_char_p, [c_int]),
     "nvfp4_quantize": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "nvfp4_quantize_onepass_workspace_size": (c_size, [c_i64, c_i64, c_i64]),
+    "nvfp4_quantize_onepass": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
+                                       c_vp]),
     "moe_permute_workspace_size": (c_size, [c_i64, c_int, c_int]),
     "moe_permute": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                             c_vp, c_size, c_vp, c_vp]),

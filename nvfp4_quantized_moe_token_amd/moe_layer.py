@@ -35,9 +35,10 @@ from . import ops
 
 def quantize_expert_weights(w):
     """NVFP4 weights of stacked experts [E, N, K] (one global scale per
-    expert).  Runs once per optimizer step, outside the per-batch path."""
+    expert), each expert read once.  Runs once per optimizer step, outside
+    the per-batch path."""
     E, N, K = w.shape
-    q, s, g, amax = ops.nvfp4_quantize(w.reshape(E * N, K), groups=E)
+    q, s, g, amax = ops.nvfp4_quantize_onepass(w.reshape(E * N, K), groups=E)
     return dict(q=q.view(E, N, K // 2), s=s.view(E, N, K // 16), g=g, amax=amax)
 
 

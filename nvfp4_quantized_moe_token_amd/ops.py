@@ -63,6 +63,26 @@ def nvfp4_quantize(x, groups=1, amax_in=None, amax_out=None, q=None, scales=None
     return q, scales, gscale, (amax_in if amax_in is not None else amax_out)
 
 
+
+def nvfp4_quantize_onepass(x, groups=1, amax_out=None, q=None, scales=None, gscale=None, workspace=None):
+    """nvfp4_quantize with the amax of each group computed, x read once
+    (same outputs).  Returns (q, scales, gscale, amax)."""
+    _dev(x, amax_out, q, scales, gscale, workspace)
+    rows, K = x.shape
+    dev = x.device
+    q = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev) if scales is None else scales
+    gscale = torch.empty((groups,), dtype=torch.float32, device=dev) if gscale is None else gscale
+    amax_out = torch.empty((groups,), dtype=torch.float32, device=dev) if amax_out is None else amax_out
+    lib = _lib.load()
+    ws_bytes = lib.nvfp4_quantize_onepass_workspace_size(rows, K, groups)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    rc = lib.nvfp4_quantize_onepass(_ptr(x), _DT[x.dtype], rows, K, groups, _ptr(amax_out), _ptr(q), _ptr(scales),
+                                    _ptr(gscale), _ptr(workspace), workspace.numel(), _stream())
+    _check("nvfp4_quantize_onepass", rc)
+    return q, scales, gscale, amax_out
+
 def moe_permute_workspace_size(T, k, E):
     return _lib.load().moe_permute_workspace_size(T, k, E)
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_entry_points():
     names = _declared_functions()
-    for n in ["nvfp4_quantize", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
+    for n in ["nvfp4_quantize", "nvfp4_quantize_onepass", "nvfp4_quantize_onepass_workspace_size", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
               "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "moe_scatter",
               "grouped_gemm_bf16_tn_gather", "silu_gate_fwd",
               "silu_gate_bwd", "moe_permute_nvfp4", "moe_permute_nvfp4_noalloc",
@@ -85,6 +85,30 @@ def test_quantize_validation(lib):
     # misaligned x
     assert q(FAKE + 4, 1, 4, 32, 1, None, FAKE, FAKE, FAKE, FAKE, None, None) == -2
 
+
+
+def test_quantize_onepass_validation(lib):
+    q = lib.nvfp4_quantize_onepass
+    ws = lib.nvfp4_quantize_onepass_workspace_size
+    # one 4-byte slot per group and slice of 1024 blocks of 16
+    assert ws(4, 32, 1) == 4
+    assert ws(128 * 1536, 2048, 128) == 128 * 192 * 4
+    assert ws(3 * 1000, 4096, 3) == 3 * 250 * 4
+    assert ws(0, 32, 4) == 0
+    assert ws(5, 32, 2) == 0 and ws(4, 24, 1) == 0 and ws(4, 32, 0) == 0
+    # NULL x with work to do; bad dtype; groups < 1; amax_out NULL
+    assert q(None, 1, 4, 32, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
+    assert q(FAKE, 7, 4, 32, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
+    assert q(FAKE, 1, 4, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
+    assert q(FAKE, 1, 4, 32, 1, None, FAKE, FAKE, FAKE, FAKE, 4, None) == -1
+    # K % 16, rows % groups, misaligned x
+    assert q(FAKE, 1, 4, 24, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -2
+    assert q(FAKE, 1, 5, 32, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -2
+    assert q(FAKE + 4, 1, 4, 32, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -2
+    # workspace missing or too small
+    assert q(FAKE, 1, 4, 32, 1, FAKE, FAKE, FAKE, FAKE, None, 4, None) == -5
+    assert q(FAKE, 1, 4, 32, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == -5
+    assert q(FAKE, 1, 128 * 1536, 2048, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 128 * 192 * 4 - 1, None) == -5
 
 def test_permute_validation(lib):
     p = lib.moe_permute
