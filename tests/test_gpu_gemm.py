@@ -197,6 +197,40 @@ def test_bf16_more_experts_than_lds_offsets(layout):
     assert_gemm_close(to_np(c), ref, ab, what=layout)
 
 
+
+@pytest.mark.parametrize("E,hi,K,N,accumulate", [
+    (600, 100, 64, 96, False),      # ~2-3 tiles per workgroup; 0-100 rows: 0 to 4 steps
+    (200, 70, 320, 288, False),     # four tiles per expert with K and N tails
+    (400, 140, 96, 160, True),      # accumulating into a non-zero dW
+])
+def test_bf16_tn_many_tiles_per_workgroup(E, hi, K, N, accumulate):
+    """TN with more tiles than workgroups, so that each workgroup loads its
+    next tile's first stages while its previous tile's results are still
+    being stored: every expert's dW against the oracle, empty experts zero
+    (or untouched when accumulating)."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(E + hi + K)
+    counts = rng.integers(0, hi + 1, E)
+    counts[rng.random(E) < 0.1] = 0
+    counts[:3] = [1, 31, 33]        # one-row and one-step-boundary experts
+    M = int(counts.sum())
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = _bf(rng, (M, K))
+    b = _bf(rng, (M, N), 0.05)
+    c0 = (rng.standard_normal((E, K, N)) * 0.1).astype(np.float32) if accumulate else None
+    out = to_gpu(c0, torch.float32) if accumulate else None
+    c = ops.grouped_gemm_bf16(ops.TN, to_gpu(a, torch.bfloat16), to_gpu(b, torch.bfloat16), to_gpu(offs, torch.int32),
+                              out=out, out_dtype=torch.float32, accumulate=accumulate)
+    torch.cuda.synchronize()
+    ref, ab = gemm.grouped_gemm_bf16("TN", a, b, offs)
+    if accumulate:
+        assert_gemm_close(to_np(c), ref + c0, ab + np.abs(c0), what="TN accumulate, many tiles")
+    else:
+        assert_gemm_close(to_np(c), ref, ab, what="TN many tiles")
+        for e in np.flatnonzero(counts == 0):
+            assert (to_np(c)[e] == 0).all(), "empty expert %d" % e
+
 def test_bf16_tn_accumulate():
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
