@@ -242,18 +242,19 @@ def nvfp4_backward_side(torch, ops, moe_layer, inp, wq_gu, wq_dn, buf, meta_box,
     off = m["offsets"]
     R = T * k
     seq = [
-        ("gather_dy", lambda: ops.moe_scatter(inp["dy"], m["dest"], off, k, topk_w=inp["tw"], out=buf.dy2)),
-        ("quantize_dy2", lambda: ops.nvfp4_quantize(buf.dy2, amax_out=nb.amax[0:1], q=nb.a_dy2[0],
+        ("gather_dy", lambda: ops.moe_scatter(inp["dy"], m["dest"], off, k, topk_w=inp["tw"], out=buf.dy2,
+                                              amax_out=nb.amax[0:1])),
+        ("quantize_dy2", lambda: ops.nvfp4_quantize(buf.dy2, amax_in=nb.amax[0:1], q=nb.a_dy2[0],
                                                     scales=nb.a_dy2[1], gscale=nb.a_dy2[2])),
         ("w4a4_dgrad_down", lambda: ops.grouped_gemm_w4a4(*nb.a_dy2, wt_dn["q"], wt_dn["s"], wt_dn["g"], off,
                                                           out=buf.dh)),
-        ("silu_gate_bwd", lambda: ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)),
+        ("silu_gate_bwd", lambda: ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1, amax_out=nb.amax[1:2])),
         ("colwise_dy2", lambda: ops.nvfp4_quantize_colwise(buf.dy2, off, nb.amax[0:1], Kp=nb.Kp, q_t=nb.c_dy2[0],
                                                            s_t=nb.c_dy2[1], gscale=nb.c_dy2[2])),
         ("colwise_h", lambda: ops.nvfp4_quantize_colwise(buf.h, off, buf.amax[1:2], Kp=nb.Kp, q_t=nb.c_h[0],
                                                          s_t=nb.c_h[1], gscale=nb.c_h[2])),
         ("w4a4_wgrad_down", lambda: ops.grouped_gemm_w4a4_wgrad(nb.c_dy2, nb.c_h, off, R, out=buf.dw_dn)),
-        ("quantize_dy1", lambda: ops.nvfp4_quantize(buf.dy1, amax_out=nb.amax[1:2], q=nb.a_dy1[0],
+        ("quantize_dy1", lambda: ops.nvfp4_quantize(buf.dy1, amax_in=nb.amax[1:2], q=nb.a_dy1[0],
                                                     scales=nb.a_dy1[1], gscale=nb.a_dy1[2])),
         ("w4a4_dgrad_gate_up", lambda: ops.grouped_gemm_w4a4(*nb.a_dy1, wt_gu["q"], wt_gu["s"], wt_gu["g"], off,
                                                              out=buf.dx_perm)),

@@ -80,7 +80,7 @@ typedef struct ihipStream_t* nvfp4moe_stream_t; /* == hipStream_t */
 #define NVFP4MOE_EPI_SILU_GATE 1 /* c receives H = silu(gate) * up, see below */
 
 /* ABI version of this header; returned by nvfp4moe_abi_version(). */
-#define NVFP4MOE_ABI_VERSION 1
+#define NVFP4MOE_ABI_VERSION 2
 
 int nvfp4moe_abi_version(void);
 /* Static string for a status code (never NULL). */
@@ -251,12 +251,15 @@ int moe_gather(const void* x, int x_dtype, int64_t row_elems, const int32_t* src
  *   x [T][row_elems] F32/BF16, dest [T*k], topk_w [T*k] fp32 or NULL,
  *   offsets [E+1] (device), out [T*k][row_elems]; 16-byte aligned rows,
  *   row_elems % 8 == 0.
+ *   amax_out fp32 [1] or NULL: max |out| over the stored values, for the
+ *   NVFP4 quantization of out that follows (amax reuse, [JA] fourth
+ *   paragraph); 0 when nothing is written.
  * Errors: EINVAL (NULL, negative sizes, bad dtype), ESHAPE (row_elems % 8,
  * alignment, T*k >= 2^31).
  */
 int moe_scatter(const void* x, int x_dtype, int64_t row_elems, const int32_t* dest,
                 const float* topk_w, const int32_t* offsets, int E, int64_t T, int k, void* out,
-                int out_dtype, nvfp4moe_stream_t stream);
+                int out_dtype, float* amax_out, nvfp4moe_stream_t stream);
 
 /*
  * moe_unpermute -- out[t] = sum_{j=0..k-1} w[t][j] * y_perm[dest[t*k+j]]
@@ -537,8 +540,10 @@ int silu_gate_fwd(const void* y1, int64_t R, int64_t F, void* h, float* amax_out
 /*
  * silu_gate_bwd -- dY1 = [dH*U*silu'(G) | dH*silu(G)], fp32 math, bf16 out.
  * y1 [R][2F] bf16, dh [R][F] bf16, dy1 [R][2F] bf16; F % 8 == 0.
+ * amax_out fp32 [1] or NULL: max |dY1| over the stored bf16 values, for the
+ * NVFP4 quantization of dY1 that follows (amax reuse, [JA] fourth paragraph).
  */
-int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t F, void* dy1,
+int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t F, void* dy1, float* amax_out,
                   nvfp4moe_stream_t stream);
 
 #ifdef __cplusplus

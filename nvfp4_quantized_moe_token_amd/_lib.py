@@ -28,7 +28,7 @@ SIGNATURES = {
     "moe_permute_nvfp4_noalloc": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_gather": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_vp]),
-    "moe_scatter": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_int, c_i64, c_int, c_vp, c_int, c_vp]),
+    "moe_scatter": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_int, c_i64, c_int, c_vp, c_int, c_vp, c_vp]),
     "moe_unpermute": (c_int, [c_vp, c_int, c_vp, c_vp, c_i64, c_int, c_i64, c_vp, c_int, c_vp]),
     "grouped_gemm_w4a4": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64,
                                   c_vp, c_int, c_int, c_vp, c_vp, c_size, c_vp]),
@@ -52,7 +52,7 @@ SIGNATURES = {
     "grouped_gemm_bf16_tn_gather": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_i64, c_i64, c_i64,
                                             c_vp, c_int, c_int, c_vp]),
     "silu_gate_fwd": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
-    "silu_gate_bwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "silu_gate_bwd": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]),
 }
 
 # Constants mirrored from the header.
@@ -61,7 +61,7 @@ F32, BF16, U8 = 0, 1, 2
 NT, NN, TN = 0, 1, 2
 EPI_NONE, EPI_SILU_GATE = 0, 1
 MX_E4M3, MX_E2M1 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 NOALLOC_SCRATCH_BYTES = 2 << 20
 STATUS_BAD_EXPERT = 1
 

@@ -44,6 +44,11 @@ constexpr int kStreamBlocks = 256 * 8;
 // 268 MB bf16 quantize: 6.0 against 5.3 TB/s).
 constexpr int64_t kMaxStreamGrid = int64_t(1) << 20;
 
+// Grid limit of the streaming kernels that also reduce a max with one
+// same-address atomic per workgroup (those serialize: 2048 of them on one
+// address cost ~17 us).
+constexpr int64_t kAmaxGrid = 256 * 8;
+
 // -------------------------------------------------------------- device side
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -480,14 +480,18 @@ __global__ __launch_bounds__(NT) void quantize_scatter_kernel(const uint4* __res
 // to the output type: the scatter form of the weighted gather.  One thread
 // per 8-element piece of a token row: the piece is read once and written to
 // the token's k permuted rows.  Rows of out past offsets[E] are zeros.
+// With amax_out, max |out| goes there with one atomic per workgroup: the max
+// of the fp32 products is rounded once, which equals the max of the rounded
+// values (rounding to bf16 is monotone).
 template <int IN, int OUT>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict__ x, int64_t T, int k, int64_t n8,
                                                       const int32_t* __restrict__ dest, const float* __restrict__ w,
                                                       const int32_t* __restrict__ offsets, int E, int64_t R,
-                                                      uint8_t* __restrict__ out) {
+                                                      uint8_t* __restrict__ out, float* __restrict__ amax_out) {
   constexpr int ib = IN == NVFP4MOE_F32 ? 4 : 2;
   constexpr int ob = OUT == NVFP4MOE_F32 ? 4 : 2;
   const int64_t tid = blockIdx.x * 256ll + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+  float m = 0.0f;
   for (int64_t i = tid; i < T * n8; i += stride) {
     const int64_t t = i / n8, c = i - t * n8;
     float v[8];
@@ -498,7 +502,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
       const float wt = w ? w[t * k + j] : 1.0f;
       float o[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = v[q] * wt;
+      for (int q = 0; q < 8; ++q) {
+        o[q] = v[q] * wt;
+        m = fmaxf(m, fabsf(o[q]));
+      }
       store8<OUT>(out + ((int64_t)r * n8 + c) * 8 * ob, o);
     }
   }
@@ -508,6 +515,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
     float z[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     store8<OUT>(out + i * 8 * ob, z);
   }
+  if (amax_out) block_atomic_max<256>(amax_out, OUT == NVFP4MOE_BF16 ? bf16_lo(pack_bf16x2(m, m)) : m);
 }
 
 // out[t] = sum_j w[t][j] * y[dest[t*k+j]], fp32 fma in ascending j.
@@ -652,26 +660,32 @@ extern "C" int moe_gather(const void* x, int x_dtype, int64_t row_elems, const i
 
 extern "C" int moe_scatter(const void* x, int x_dtype, int64_t row_elems, const int32_t* dest, const float* topk_w,
                            const int32_t* offsets, int E, int64_t T, int k, void* out, int out_dtype,
-                           nvfp4moe_stream_t stream) {
+                           float* amax_out, nvfp4moe_stream_t stream) {
   if (T < 0 || k < 1 || E < 1 || row_elems < 0) return NVFP4MOE_EINVAL;
   if ((x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16) || (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16))
     return NVFP4MOE_EINVAL;
   if (!offsets) return NVFP4MOE_EINVAL;
   if (T > 0 && row_elems > 0 && (!x || !dest || !out)) return NVFP4MOE_EINVAL;
-  if (row_elems % 8 != 0 || !aligned(x, 16) || !aligned(out, 16)) return NVFP4MOE_ESHAPE;
+  if (row_elems % 8 != 0 || !aligned(x, 16) || !aligned(out, 16) || (amax_out && !aligned(amax_out, 4)))
+    return NVFP4MOE_ESHAPE;
   if (T * k > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   const int64_t R = T * k, n8 = row_elems / 8;
-  if (R == 0 || n8 == 0) return NVFP4MOE_OK;
+  hipStream_t st = as_stream(stream);
+  if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+  if (R == 0 || n8 == 0) return launch_status();
   int64_t grid = cdiv(T * n8, 256);
   if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
-  hipStream_t st = as_stream(stream);
+  // one same-address atomic per workgroup for the amax: a capped grid (an
+  // uncapped one, with the atomic skipped when the workgroup's max is not
+  // larger than the value it last read, was slower still)
+  if (amax_out && grid > kAmaxGrid) grid = kAmaxGrid;
   const uint8_t* xi = reinterpret_cast<const uint8_t*>(x);
   uint8_t* o = reinterpret_cast<uint8_t*>(out);
 #define NVS(I, O)                                                                                                 \
   if (x_dtype == I && out_dtype == O) {                                                                          \
-    scatter_kernel<I, O><<<(unsigned)grid, 256, 0, st>>>(xi, T, k, n8, dest, topk_w, offsets, E, R, o);          \
+    scatter_kernel<I, O><<<(unsigned)grid, 256, 0, st>>>(xi, T, k, n8, dest, topk_w, offsets, E, R, o, amax_out); \
     return launch_status();                                                                                      \
   }
   NVS(NVFP4MOE_BF16, NVFP4MOE_BF16)

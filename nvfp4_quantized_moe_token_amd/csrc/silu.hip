@@ -31,10 +31,15 @@ __global__ __launch_bounds__(256) void silu_fwd_kernel(const uint16_t* __restric
   if (amax_out) block_atomic_max<256>(amax_out, m);
 }
 
+// dY1 = [dG | dU] from dH and Y1; with amax_out, max |dY1| (the max of the
+// fp32 results rounded once to bf16, equal to the max of the stored values)
+// with one atomic per workgroup.
 __global__ __launch_bounds__(256) void silu_bwd_kernel(const uint16_t* __restrict__ y1, const uint16_t* __restrict__ dh,
-                                                       int64_t R, int64_t F, uint16_t* __restrict__ dy1) {
+                                                       int64_t R, int64_t F, uint16_t* __restrict__ dy1,
+                                                       float* __restrict__ amax_out) {
   const int64_t n8 = F / 8;
   const int64_t total = R * n8;
+  float m = 0.0f;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t r = i / n8, c = (i - r * n8) * 8;
     const uint4 gw = *reinterpret_cast<const uint4*>(y1 + r * 2 * F + c);
@@ -53,6 +58,7 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const uint16_t* __restric
         const float dsilu = sg * (1.0f + gg[q] * (1.0f - sg));
         rg[q] = dd[q] * uu[q] * dsilu;
         ru[q] = dd[q] * gg[q] * sg;
+        m = fmaxf(m, fmaxf(fabsf(rg[q]), fabsf(ru[q])));
       }
       og[j] = pack_bf16x2(rg[0], rg[1]);
       ou[j] = pack_bf16x2(ru[0], ru[1]);
@@ -60,13 +66,13 @@ __global__ __launch_bounds__(256) void silu_bwd_kernel(const uint16_t* __restric
     *reinterpret_cast<uint4*>(dy1 + r * 2 * F + c) = make_uint4(og[0], og[1], og[2], og[3]);
     *reinterpret_cast<uint4*>(dy1 + r * 2 * F + F + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
   }
+  if (amax_out) block_atomic_max<256>(amax_out, bf16_lo(pack_bf16x2(m, m)));
 }
 
-// The forward folds max|H| into one atomic per workgroup, so its grid is
-// capped (same-address atomics serialize).
+// With an amax the grid is capped (one same-address atomic per workgroup).
 inline unsigned grid_for(int64_t work) {
   const int64_t g = cdiv(work, 256);
-  return (unsigned)(g < 1 ? 1 : g > 256 * 8 ? 256 * 8 : g);
+  return (unsigned)(g < 1 ? 1 : g > kAmaxGrid ? kAmaxGrid : g);
 }
 
 }  // namespace
@@ -89,18 +95,22 @@ extern "C" int silu_gate_fwd(const void* y1, int64_t R, int64_t F, void* h, floa
   return launch_status();
 }
 
-extern "C" int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t F, void* dy1,
+extern "C" int silu_gate_bwd(const void* y1, const void* dh, int64_t R, int64_t F, void* dy1, float* amax_out,
                              nvfp4moe_stream_t stream) {
   if (R < 0 || F < 0) return NVFP4MOE_EINVAL;
   if (R * F > 0 && (!y1 || !dh || !dy1)) return NVFP4MOE_EINVAL;
   if (F % 8 != 0 || !aligned(y1, 16) || !aligned(dh, 16) || !aligned(dy1, 16)) return NVFP4MOE_ESHAPE;
+  if (amax_out && !aligned(amax_out, 4)) return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
-  if (R * F == 0) return NVFP4MOE_OK;
+  hipStream_t st = as_stream(stream);
+  if (amax_out) fill_u32_kernel<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t*>(amax_out), 0u, 1);
+  if (R * F == 0) return launch_status();
   int64_t grid = cdiv(R * F / 8, 256);
   if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
-  silu_bwd_kernel<<<(unsigned)grid, 256, 0, as_stream(stream)>>>(
-      reinterpret_cast<const uint16_t*>(y1), reinterpret_cast<const uint16_t*>(dh), R, F,
-      reinterpret_cast<uint16_t*>(dy1));
+  if (amax_out) grid = grid_for(R * F / 8);
+  silu_bwd_kernel<<<(unsigned)grid, 256, 0, st>>>(reinterpret_cast<const uint16_t*>(y1),
+                                                  reinterpret_cast<const uint16_t*>(dh), R, F,
+                                                  reinterpret_cast<uint16_t*>(dy1), amax_out);
   return launch_status();
 }

@@ -229,25 +229,26 @@ class NVFP4BackwardBuffers:
 
 def backward_nvfp4(dy, topk_w, wt_gu, wt_dn, meta, buf, nb, amax_x=None):
     """The NVFP4 backward variant of ``backward``: the same dataflow with the
-    four grouped GEMMs in W4A4.  Each gradient's amax is taken once, by its
-    row-wise quantization, and reused by its column-wise one; H and X_perm
-    reuse the forward's amaxes (buf.amax, or ``amax_x`` when the forward
-    was given a fixed one).  wt_gu / wt_dn: quantize_expert_weights_t of the
-    bf16 weights.  Weight gradients fp32, activation gradients bf16."""
+    four grouped GEMMs in W4A4.  Each gradient's amax comes out of the kernel
+    that writes the gradient (the weighted scatter for dY2, the SiLU backward
+    for dY1) and is reused by its row-wise and column-wise quantizations; H
+    and X_perm reuse the forward's amaxes (buf.amax, or ``amax_x`` when the
+    forward was given a fixed one).  wt_gu / wt_dn: quantize_expert_weights_t
+    of the bf16 weights.  Weight gradients fp32, activation gradients bf16."""
     off = meta["offsets"]
     R = buf.T * buf.k
     amax_x = buf.amax[0:1] if amax_x is None else amax_x
-    ops.moe_scatter(dy, meta["dest"], off, buf.k, topk_w=topk_w, out=buf.dy2)
+    ops.moe_scatter(dy, meta["dest"], off, buf.k, topk_w=topk_w, out=buf.dy2, amax_out=nb.amax[0:1])
     q, sc, g = nb.a_dy2
-    ops.nvfp4_quantize(buf.dy2, amax_out=nb.amax[0:1], q=q, scales=sc, gscale=g)
+    ops.nvfp4_quantize(buf.dy2, amax_in=nb.amax[0:1], q=q, scales=sc, gscale=g)
     ops.grouped_gemm_w4a4(q, sc, g, wt_dn["q"], wt_dn["s"], wt_dn["g"], off, out=buf.dh)
-    ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1)
+    ops.silu_gate_bwd(buf.y1, buf.dh, dy1=buf.dy1, amax_out=nb.amax[1:2])
     ops.nvfp4_quantize_colwise(buf.dy2, off, nb.amax[0:1], Kp=nb.Kp, q_t=nb.c_dy2[0], s_t=nb.c_dy2[1],
                                gscale=nb.c_dy2[2])
     ops.nvfp4_quantize_colwise(buf.h, off, buf.amax[1:2], Kp=nb.Kp, q_t=nb.c_h[0], s_t=nb.c_h[1], gscale=nb.c_h[2])
     ops.grouped_gemm_w4a4_wgrad(nb.c_dy2, nb.c_h, off, R, out=buf.dw_dn)
     q, sc, g = nb.a_dy1
-    ops.nvfp4_quantize(buf.dy1, amax_out=nb.amax[1:2], q=q, scales=sc, gscale=g)
+    ops.nvfp4_quantize(buf.dy1, amax_in=nb.amax[1:2], q=q, scales=sc, gscale=g)
     ops.grouped_gemm_w4a4(q, sc, g, wt_gu["q"], wt_gu["s"], wt_gu["g"], off, out=buf.dx_perm)
     ops.moe_unpermute(buf.dx_perm, meta["dest"], buf.T, buf.k, topk_w=None, out=buf.dx)
     ops.nvfp4_quantize_colwise(buf.dy1, off, nb.amax[1:2], Kp=nb.Kp, q_t=nb.c_dy1[0], s_t=nb.c_dy1[1],

@@ -196,10 +196,11 @@ def moe_gather(x, src, k, topk_w=None, out=None, out_dtype=None):
     return out
 
 
-def moe_scatter(x, dest, offsets, k, topk_w=None, out=None, out_dtype=None):
+def moe_scatter(x, dest, offsets, k, topk_w=None, out=None, out_dtype=None, amax_out=None):
     """out[dest[t*k+j]] = w[t*k+j] * x[t]: the weighted gather written from the
-    token side (each row of x read once); rows past offsets[E] are zeros."""
-    _dev(x, dest, offsets, topk_w, out)
+    token side (each row of x read once); rows past offsets[E] are zeros.
+    amax_out (fp32 [1], optional) receives max |out|."""
+    _dev(x, dest, offsets, topk_w, out, amax_out)
     T = x.shape[0]
     R = T * k
     E = offsets.numel() - 1
@@ -207,7 +208,7 @@ def moe_scatter(x, dest, offsets, k, topk_w=None, out=None, out_dtype=None):
     odt = x.dtype if out_dtype is None else out_dtype
     out = torch.empty((R,) + tuple(x.shape[1:]), dtype=odt, device=x.device) if out is None else out
     rc = _lib.load().moe_scatter(_ptr(x), _DT[x.dtype], row_elems, _ptr(dest), _ptr(topk_w), _ptr(offsets), E, T,
-                                 k, _ptr(out), _DT[out.dtype], _stream())
+                                 k, _ptr(out), _DT[out.dtype], _ptr(amax_out), _stream())
     _check("moe_scatter", rc)
     return out
 
@@ -456,10 +457,12 @@ def silu_gate_fwd(y1, h=None, amax_out=None, want_amax=True):
     return h, amax_out
 
 
-def silu_gate_bwd(y1, dh, dy1=None):
-    _dev(y1, dh, dy1)
+def silu_gate_bwd(y1, dh, dy1=None, amax_out=None):
+    """dY1 = [dG | dU] from Y1 and dH; amax_out (fp32 [1], optional)
+    receives max |dY1|."""
+    _dev(y1, dh, dy1, amax_out)
     R, F2 = y1.shape
     dy1 = torch.empty((R, F2), dtype=torch.bfloat16, device=y1.device) if dy1 is None else dy1
-    rc = _lib.load().silu_gate_bwd(_ptr(y1), _ptr(dh), R, F2 // 2, _ptr(dy1), _stream())
+    rc = _lib.load().silu_gate_bwd(_ptr(y1), _ptr(dh), R, F2 // 2, _ptr(dy1), _ptr(amax_out), _stream())
     _check("silu_gate_bwd", rc)
     return dy1

@@ -153,10 +153,11 @@ def test_gather_unpermute_validation(lib):
     assert lib.moe_gather(FAKE, 2, 64, FAKE, FAKE, 8, 10, FAKE, 2, None) == -1  # weighted bytes
     assert lib.moe_gather(FAKE, 1, 12, FAKE, FAKE, 8, 10, FAKE, 1, None) == -2
     sc = lib.moe_scatter
-    assert sc(FAKE, 1, 64, FAKE, None, FAKE, 4, 10, 0, FAKE, 1, None) == -1       # k = 0
-    assert sc(FAKE, 2, 64, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None) == -1       # u8 payload
-    assert sc(FAKE, 1, 64, FAKE, None, None, 4, 10, 8, FAKE, 1, None) == -1       # offsets NULL
-    assert sc(FAKE, 1, 12, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None) == -2       # row_elems % 8
+    assert sc(FAKE, 1, 64, FAKE, None, FAKE, 4, 10, 0, FAKE, 1, None, None) == -1       # k = 0
+    assert sc(FAKE, 2, 64, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None, None) == -1       # u8 payload
+    assert sc(FAKE, 1, 64, FAKE, None, None, 4, 10, 8, FAKE, 1, None, None) == -1       # offsets NULL
+    assert sc(FAKE, 1, 12, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, None, None) == -2       # row_elems % 8
+    assert sc(FAKE, 1, 64, FAKE, None, FAKE, 4, 10, 8, FAKE, 1, FAKE + 2, None) == -2   # misaligned amax
     assert lib.moe_unpermute(FAKE, 2, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
     assert lib.moe_unpermute(FAKE, 1, FAKE, None, 4, 8, 60, FAKE, 1, None) == -2
     assert lib.moe_unpermute(None, 1, FAKE, None, 4, 8, 64, FAKE, 1, None) == -1
@@ -334,7 +335,8 @@ def test_mx_validation(lib):
 def test_silu_validation(lib):
     assert lib.silu_gate_fwd(None, 4, 64, FAKE, None, None) == -1
     assert lib.silu_gate_fwd(FAKE, 4, 60, FAKE, None, None) == -2
-    assert lib.silu_gate_bwd(FAKE, FAKE, -1, 64, FAKE, None) == -1
+    assert lib.silu_gate_bwd(FAKE, FAKE, -1, 64, FAKE, None, None) == -1
+    assert lib.silu_gate_bwd(FAKE, FAKE, 4, 64, FAKE, FAKE + 2, None) == -2
 
 
 def test_ops_refuse_cpu_tensors():

@@ -9,7 +9,7 @@ import torch
 import workloads
 from _helpers import assert_bf16_close, assert_gemm_close, gpu, require_gpu, to_gpu, to_np
 from oracle import layer, moe
-from oracle.layer import quantize_weights
+from oracle.layer import bf16_round, quantize_weights
 
 pytestmark = gpu
 
@@ -128,3 +128,28 @@ def test_silu_extremes():
     assert np.isfinite(hv).all()
     assert_bf16_close(hv, ref, what="silu extremes")
     assert to_np(amax)[0] == np.abs(hv).max()
+
+
+@pytest.mark.parametrize("R,F", [(300, 96), (65536, 768)])
+def test_silu_gate_bwd_amax(R, F):
+    """silu_gate_bwd with its amax: dY1 bit-equal to the call without it, the
+    amax equal to max |dY1| over the stored values (at the 8k update's size
+    the grid is capped and each thread takes many rows), and dY1 against the
+    oracle's SiLU backward."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(R + F)
+    y1 = bf16_round((rng.standard_normal((R, 2 * F)) * 2).astype(np.float32))
+    dh = bf16_round((rng.standard_normal((R, F)) * 0.1).astype(np.float32))
+    y1[R // 2, 3] = 9.0                   # a large gate: dU = dH * silu(G) peaks
+    dh[R // 2, 3] = -4.0
+    yg, dg = to_gpu(y1, torch.bfloat16), to_gpu(dh, torch.bfloat16)
+    d0 = ops.silu_gate_bwd(yg, dg)
+    amax = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    d1 = ops.silu_gate_bwd(yg, dg, amax_out=amax)
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d1)
+    assert float(amax) == float(d1.float().abs().max())
+    rows = np.arange(R) if R <= 1000 else np.unique(np.concatenate([[0, R // 2, R - 1], rng.integers(0, R, 64)]))
+    ref = moe.silu_gate_bwd(y1[rows], dh[rows])
+    assert_bf16_close(to_np(d1)[rows], ref, what="silu bwd")

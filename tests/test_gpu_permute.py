@@ -175,26 +175,35 @@ def test_scatter_equals_weighted_gather(in_dt, out_dt, weighted):
         # unweighted moe_gather copies verbatim (no dtype change): compare in the input dtype
         g = ops.moe_gather(x, r["src"], k).to(out_dt)
     sc = ops.moe_scatter(x, r["dest"], r["offsets"], k, topk_w=w, out_dtype=out_dt)
+    amax = torch.full((1,), 123.0, dtype=torch.float32, device="cuda")   # cleared by the call
+    sc2 = ops.moe_scatter(x, r["dest"], r["offsets"], k, topk_w=w, out_dtype=out_dt, amax_out=amax)
     torch.cuda.synchronize()
     assert torch.equal(sc, g)
+    assert torch.equal(sc2, sc)                 # the amax changes nothing written
+    assert float(amax) == float(sc.float().abs().max())
     R_valid = int(to_np(r["offsets"])[-1])
     assert R_valid == T * k - 2 and (to_np(sc)[R_valid:] == 0).all()
 
 
 def test_scatter_moe_8k_matches_oracle_sampled():
     """dY2 of the 8k update by scatter against the oracle's gather (fp32
-    product rounded once to bf16), on every row."""
+    product rounded once to bf16), on every row, and its fused amax."""
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
     d = workloads.moe_8k_update(weights=False)
     T, k, E = d["T"], d["k"], d["E"]
     r = _meta(d["topk_ids"], E)
     dy = to_gpu(d["dy"], torch.bfloat16)
-    out = ops.moe_scatter(dy, r["dest"], r["offsets"], k, topk_w=to_gpu(d["topk_w"], torch.float32))
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = ops.moe_scatter(dy, r["dest"], r["offsets"], k, topk_w=to_gpu(d["topk_w"], torch.float32),
+                          amax_out=amax)
     torch.cuda.synchronize()
     src = to_np(r["src"])
     ref = moe.gather_rows(to_np(dy), src, k).astype(np.float32) * d["topk_w"].reshape(-1)[src][:, None]
-    np.testing.assert_array_equal(to_np(out), bf16_round(ref.astype(np.float32)))
+    want = bf16_round(ref.astype(np.float32))
+    np.testing.assert_array_equal(to_np(out), want)
+    # the fused amax (capped grid, one atomic per workgroup) is max |dY2|
+    assert np.float32(amax.item()) == np.abs(want).max()
 
 
 @pytest.mark.parametrize("weighted", [True, False])
