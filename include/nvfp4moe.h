@@ -391,7 +391,7 @@ int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8_t* a_s, co
  *   Kp       row length of q_t/s_t: Kp % 64 == 0, Kp >= 64*(M_total/64 + E).
  *   gscale   [1] out.
  * Errors: EINVAL (NULL, negative, dtype other than BF16), ESHAPE (N % 8,
- * Kp, alignment).
+ * Kp, alignment, q_t of 2 GiB or more).
  */
 int nvfp4_quantize_colwise(const void* x, int x_dtype, int64_t M_total, int64_t N,
                            const int32_t* expert_offsets, int E, const float* amax_in, uint8_t* q_t,
@@ -405,7 +405,8 @@ int nvfp4_quantize_colwise(const void* x, int x_dtype, int64_t M_total, int64_t 
  * expert weights of the data-gradient GEMMs: W^T_e, whose amax is that of
  * W_e, so amax_in may be the forward weights' amax).  amax_in [groups] or
  * NULL (then computed into amax_out).  L % 64 == 0, N % 8 == 0; x, q_t
- * 16-byte aligned.  Errors as nvfp4_quantize.
+ * 16-byte aligned; q_t under 2 GiB.  Errors as nvfp4_quantize (ESHAPE for
+ * q_t of 2 GiB or more).
  */
 int nvfp4_quantize_transposed(const void* x, int x_dtype, int64_t groups, int64_t L, int64_t N,
                               const float* amax_in, float* amax_out, uint8_t* q_t, uint8_t* s_t,

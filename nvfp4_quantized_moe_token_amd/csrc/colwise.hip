@@ -36,12 +36,19 @@
 namespace nvfp4moe {
 namespace {
 
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+
 constexpr int kColTileRows = 256;  // padded rows per workgroup: 4 quarters of 64
 constexpr int kColTileCols = 64;
 
+// Expert offsets (and per-group global scales) kept in LDS up to this many.
+constexpr int kColLds = 1025;
+
 // The expert whose padded segment holds padded row pr (grouped layout): the
-// last e with poff_e <= pr, offsets clamped to [0, M].
-__device__ int find_padded_segment(const int32_t* __restrict__ off, int E, int64_t M, int64_t pr) {
+// last e with poff_e <= pr, offsets clamped to [0, M].  `off` is the LDS
+// copy of the offsets or, past kColLds - 1 experts, global memory.
+template <typename P>
+__device__ int find_padded_segment(P off, int E, int64_t M, int64_t pr) {
   int lo = 0, hi = E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -67,8 +74,8 @@ __global__ void fill_gscale_kernel(const float* __restrict__ amax, float* __rest
 // in a grid-stride loop; each workgroup loads its next tile into registers
 // while it encodes the current one from LDS.  Three workgroups per CU (the
 // register budget that holds the prefetched tile without spills).
-template <bool UNIFORM>
-__global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
+template <bool UNIFORM, bool IN_LDS>
+__global__ __launch_bounds__(256, 4) void colwise_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                       const int32_t* __restrict__ off, int E, int64_t L,
                                                       const float* __restrict__ amax, uint8_t* __restrict__ q,
                                                       uint8_t* __restrict__ s, float* __restrict__ gscale, int64_t Kp,
@@ -77,14 +84,33 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
   // per work tile (two in flight) and quarter: expert (-1: nothing to
   // write), first source row, rows in the segment, segment-relative first row
   __shared__ int64_t seg[2][4][4];
+  __shared__ float segg[2][4];  // and its global scale
+  // The offsets (grouped) and the groups' global scales, copied once: the
+  // per-tile lookups then read no global memory.  A global load there would
+  // also wait for the prefetched tile (a wave's memory counter retires in
+  // order), so the encode of a tile could not overlap the next one's loads.
+  // (IN_LDS: they fit; a template parameter, so that the two kinds of
+  // lookup are never merged into one flat access)
+  __shared__ int32_t s_off[IN_LDS ? kColLds : 1];
+  __shared__ float s_g[IN_LDS ? kColLds : 1];
   const int tid = threadIdx.x;
   const int64_t extent = UNIFORM ? (int64_t)E * L : Kp;
+  // outputs: [N][extent / 2] codes, [N][extent / 16] scales (each under 2 GiB)
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, N * (extent / 2)), rs = make_rsrc(s, N * (extent / 16));
+  const int ng = UNIFORM ? E : 1;
+  if constexpr (IN_LDS) {
+    if (!UNIFORM)
+      for (int i = tid; i <= E; i += 256) s_off[i] = off[i];
+    for (int i = tid; i < ng; i += 256) s_g[i] = global_scale(amax[i]);
+  }
+  __syncthreads();
 
   // threads 0..3: the quarters of work tile T
   auto resolve = [&](int64_t T, int buf) {
     const int64_t tx = T % tiles_x;
     const int64_t pr = tx * kColTileRows + 64 * tid;   // the quarter's first padded row
     int64_t e = -1, src0 = 0, cnt = 0, j0 = 0;
+    float g = 1.0f;
     if (pr < extent) {
       if (UNIFORM) {
         e = pr / L;
@@ -92,16 +118,28 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
         cnt = L;
         j0 = pr - src0;
       } else {
-        e = find_padded_segment(off, E, M, pr);
-        int64_t lo = off[e], hi = off[e + 1];
+        int64_t lo, hi;
+        if constexpr (IN_LDS) {
+          e = find_padded_segment(s_off, E, M, pr);
+          lo = s_off[e];
+          hi = s_off[e + 1];
+        } else {
+          e = find_padded_segment(off, E, M, pr);
+          lo = off[e];
+          hi = off[e + 1];
+        }
         lo = lo < 0 ? 0 : lo > M ? M : lo;
         hi = hi < lo ? lo : hi > M ? M : hi;
         src0 = lo;
         cnt = hi - lo;
         j0 = pr - 64 * (lo / 64 + e);
       }
+      if constexpr (IN_LDS)
+        g = s_g[UNIFORM ? e : 0];
+      else
+        g = global_scale(amax[UNIFORM ? e : 0]);
       // the segment's global scale, once (where its first block lies)
-      if (T < tiles_x && j0 == 0) gscale[UNIFORM ? e : 0] = global_scale(amax[UNIFORM ? e : 0]);
+      if (T < tiles_x && j0 == 0) gscale[UNIFORM ? e : 0] = g;
       // a gap between padded segments (or before the first): nothing to
       // write (uniform: never)
       if (j0 < 0 || j0 >= (cnt + 63) / 64 * 64) e = -1;
@@ -110,6 +148,7 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
     seg[buf][tid][1] = src0;
     seg[buf][tid][2] = cnt;
     seg[buf][tid][3] = j0;
+    segg[buf][tid] = g;
   };
   // 256 rows x 8 chunks of 16 bytes, 8 per thread; rows past their segment,
   // quarters with nothing to write and columns past N read as zeros
@@ -132,6 +171,12 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
   __syncthreads();
   uint4 reg[8];
   fetch(T, 0, reg);
+  // Three stores that write nothing (past the buffer, dropped): the loop's
+  // first wait then finds the same three stores after the loads as on every
+  // later iteration, so its count can leave them outstanding.
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{0u, 0u, 0u, 0u}, rq, kOOB, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{0u, 0u, 0u, 0u}, rq, kOOB + 16, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(0u, rs, kOOB, 0, 0);
   for (; T < tiles; T += gridDim.x) {
     const int64_t Tn = T + gridDim.x;
 #pragma unroll
@@ -150,8 +195,8 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
     uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     uint32_t sw = 0;
     if (e >= 0 && n < N) {
-      const float g = global_scale(amax[UNIFORM ? e : 0]);
-#pragma unroll
+      const float g = segg[buf][qt];
+#pragma unroll 1
       for (int b = 0; b < 4; ++b) {
         float v[16];
 #pragma unroll
@@ -180,22 +225,27 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
     auto at = [&](int u, int64_t nn) -> int64_t {
       return UNIFORM ? seg[buf][u][0] * N * L + nn * L + seg[buf][u][3] : nn * Kp + tx * kColTileRows + 64 * u;
     };
+    // Every thread issues its three stores; one with nothing to write gets an
+    // offset past the buffer and is dropped.  The count is then the same on
+    // every path, so the wait for the next tile's loads at the top of the
+    // loop leaves these stores outstanding (a conditional store made the
+    // compiler wait for everything there).
     // codes: 64 rows x 8 chunks of 16 bytes (chunk c holds half c % 2 of quarter c / 2)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int idx = tid + 256 * p;
       const int r = idx >> 3, c = idx & 7, u = c >> 1;
       const int64_t nn = n0 + r;
-      if (seg[buf][u][0] >= 0 && nn < N)
-        *reinterpret_cast<uint4*>(q + at(u, nn) / 2 + 16 * (c & 1)) =
-            *reinterpret_cast<const uint4*>(cst + r * 128 + 16 * c);
+      const uint32_t voff = seg[buf][u][0] >= 0 && nn < N ? (uint32_t)(at(u, nn) / 2 + 16 * (c & 1)) : kOOB;
+      const uint4 w = *reinterpret_cast<const uint4*>(cst + r * 128 + 16 * c);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{w.x, w.y, w.z, w.w}, rq, voff, 0, 0);
     }
     // scales: 64 rows x 4 words
     {
       const int r = tid >> 2, u = tid & 3;
       const int64_t nn = n0 + r;
-      if (seg[buf][u][0] >= 0 && nn < N)
-        *reinterpret_cast<uint32_t*>(s + at(u, nn) / 16) = *reinterpret_cast<const uint32_t*>(sst + r * 16 + 4 * u);
+      const uint32_t voff = seg[buf][u][0] >= 0 && nn < N ? (uint32_t)(at(u, nn) / 16) : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(sst + r * 16 + 4 * u), rs, voff, 0, 0);
     }
     __syncthreads();  // the staging area is read before the next tile lands in LDS
     buf ^= 1;
@@ -205,17 +255,26 @@ __global__ __launch_bounds__(256, 3) void colwise_kernel(const uint16_t* __restr
 // Workgroups of the column-wise kernel: as many as are resident at once
 // (three per CU: 32 KB of LDS and up to 170 VGPRs each), at most one per
 // work tile, so that no workgroup starts its share late.
-template <bool UNIFORM>
+template <bool UNIFORM, bool IN_LDS>
 int64_t colwise_grid(int64_t tiles) {
   static int per_cu = 0;
   if (per_cu < 1) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, colwise_kernel<UNIFORM>, 256, 0) != hipSuccess || occ < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, colwise_kernel<UNIFORM, IN_LDS>, 256, 0) != hipSuccess ||
+        occ < 1)
       occ = 1;
     per_cu = occ;
   }
   const int64_t g = (int64_t)device_cu_count() * per_cu;
   return tiles < g ? tiles : g;
+}
+
+template <bool UNIFORM, bool IN_LDS>
+void colwise_launch(const uint16_t* x, int64_t M, int64_t N, const int32_t* off, int E, int64_t L, const float* amax,
+                    uint8_t* q, uint8_t* s, float* gscale, int64_t Kp, int64_t tiles_x, int64_t tiles,
+                    hipStream_t st) {
+  colwise_kernel<UNIFORM, IN_LDS><<<(unsigned)colwise_grid<UNIFORM, IN_LDS>(tiles), 256, 0, st>>>(
+      x, M, N, off, E, L, amax, q, s, gscale, Kp, tiles_x, tiles);
 }
 
 }  // namespace
@@ -233,15 +292,19 @@ extern "C" int nvfp4_quantize_colwise(const void* x, int x_dtype, int64_t M_tota
   if (N % 8 != 0 || Kp % 64 != 0 || Kp < 64 * (M_total / 64 + (int64_t)E)) return NVFP4MOE_ESHAPE;
   if (!aligned(x, 16) || !aligned(q_t, 16) || !aligned(s_t, 4) || !aligned(gscale, 4)) return NVFP4MOE_ESHAPE;
   if (M_total > 0x7FFFFFFFLL || Kp / 64 > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  if (N * (Kp / 2) > 0x7FFFFFF0LL) return NVFP4MOE_ESHAPE;  // codes under 2 GiB (32-bit store offsets)
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   hipStream_t st = as_stream(stream);
   const int64_t tiles_x = cdiv(Kp > 0 ? Kp : 1, kColTileRows);
   // Every row tile is visited (also with N == 0: row tile 0 writes the global scale).
   const int64_t tiles = tiles_x * cdiv(N > 0 ? N : 1, kColTileCols);
-  colwise_kernel<false><<<(unsigned)colwise_grid<false>(tiles), 256, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), M_total, N, expert_offsets, E, 0, amax_in, q_t, s_t, gscale, Kp, tiles_x,
-      tiles);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (E + 1 <= kColLds)
+    colwise_launch<false, true>(xb, M_total, N, expert_offsets, E, 0, amax_in, q_t, s_t, gscale, Kp, tiles_x, tiles, st);
+  else
+    colwise_launch<false, false>(xb, M_total, N, expert_offsets, E, 0, amax_in, q_t, s_t, gscale, Kp, tiles_x, tiles,
+                                 st);
   return launch_status();
 }
 
@@ -257,6 +320,7 @@ extern "C" int nvfp4_quantize_transposed(const void* x, int x_dtype, int64_t gro
       (amax_in && !aligned(amax_in, 4)) || (amax_out && !aligned(amax_out, 4)))
     return NVFP4MOE_ESHAPE;
   if (groups * (L / 64) > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  if (groups * L * (N / 2) > 0x7FFFFFF0LL) return NVFP4MOE_ESHAPE;  // codes under 2 GiB (32-bit store offsets)
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
   hipStream_t st = as_stream(stream);
@@ -273,8 +337,12 @@ extern "C" int nvfp4_quantize_transposed(const void* x, int x_dtype, int64_t gro
   }
   const int64_t tiles_x = cdiv(groups * L, kColTileRows);
   const int64_t tiles = tiles_x * cdiv(N, kColTileCols);
-  colwise_kernel<true><<<(unsigned)colwise_grid<true>(tiles), 256, 0, st>>>(
-      reinterpret_cast<const uint16_t*>(x), groups * L, N, nullptr, (int)groups, L, amax, q_t, s_t, gscale, 0, tiles_x,
-      tiles);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (groups <= kColLds)
+    colwise_launch<true, true>(xb, groups * L, N, nullptr, (int)groups, L, amax, q_t, s_t, gscale, 0, tiles_x, tiles,
+                               st);
+  else
+    colwise_launch<true, false>(xb, groups * L, N, nullptr, (int)groups, L, amax, q_t, s_t, gscale, 0, tiles_x, tiles,
+                                st);
   return launch_status();
 }

@@ -50,6 +50,15 @@ constexpr int64_t kMaxStreamGrid = int64_t(1) << 20;
 constexpr int64_t kAmaxGrid = 256 * 8;
 
 // -------------------------------------------------------------- device side
+// Raw buffer resources: accesses at or past `bytes` (or at kOOB) are not
+// made -- loads read zeros, stores are dropped.
+constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRawBufferWord3);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -66,8 +66,6 @@ constexpr int BK = 64;                       // reduction elements per MFMA grou
 constexpr bool kNMajor = NVFP4MOE_GEMM_NMAJOR;  // tile order within an expert (find_tile)
 constexpr int NV_KS = 256;                   // reduction elements per NVFP4 stage
 constexpr int MX_KS = 128;                   // reduction elements per MX (W4A8) stage
-constexpr uint32_t kOOB = 0x80000000u;       // a buffer offset past every range
-constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
 // W4A4_SILU: the W4A4 gate+up GEMM with the SiLU-gate epilogue.  W4A8:
 // MXFP8 activations x MXFP4 weights on the scaled MFMA (W4A8_SILU: with the
@@ -168,10 +166,6 @@ __device__ __forceinline__ void wait_steps_ahead(int ahead) {
   }
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRawBufferWord3);
-}
 // One wave-wide LDS-direct load: lane l's `size` bytes land at LDS byte
 // address lds + size*l (lds wave-uniform).  Issued as inline assembly so the
 // compiler does not make every later LDS read wait for it: the kernel keeps

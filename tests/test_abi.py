@@ -269,6 +269,8 @@ def test_colwise_and_transposed_validation(lib):
     assert c(*bad) == -2                       # Kp % 64
     bad = list(args); bad[7] = FAKE + 4
     assert c(*bad) == -2                       # q_t alignment
+    bad = list(args); bad[3] = 1 << 20; bad[10] = 1 << 13
+    assert c(*bad) == -2                       # codes of 2^20 x 2^12 bytes: past 2 GiB
     t = lib.nvfp4_quantize_transposed
     args = [FAKE, 1, 4, 128, 64, FAKE, None, FAKE, FAKE, FAKE, None]
     bad = list(args); bad[5] = None
@@ -281,6 +283,8 @@ def test_colwise_and_transposed_validation(lib):
     assert t(*bad) == -2                       # N % 8
     bad = list(args); bad[2] = 0
     assert t(*bad) == -1                       # groups < 1
+    bad = list(args); bad[2] = 1 << 10; bad[3] = 1 << 12; bad[4] = 1 << 11
+    assert t(*bad) == -2                       # codes of 2^10 x 2^12 x 2^10 bytes: past 2 GiB
 
 
 def test_wgrad_validation(lib):
