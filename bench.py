@@ -312,13 +312,11 @@ def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
     box = {}
 
     def permute():
-        box["m"] = ops.moe_permute(inp["ids"], E, x=buf.xq, x_perm=buf.a1_q, workspace=buf.ws)
+        box["m"] = ops.moe_permute_mx(inp["ids"], E, inp["x"], q=buf.a1_q, scales=buf.a1_s, workspace=buf.ws)
 
     m = lambda: box["m"]  # noqa: E731
     seq = [
-        ("mx_quantize_x", lambda: ops.mx_quantize(inp["x"], ops.MX_E4M3, q=buf.xq, scales=buf.xs)),
-        ("permute_codes", permute),
-        ("gather_scales", lambda: ops.moe_gather(buf.xs, m()["src"], k, out=buf.a1_s)),
+        ("permute_quantize_mx", permute),
         ("w4a8_gate_up_silu", lambda: ops.grouped_gemm_w4a8_silu_gate(
             buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], m()["offsets"], want_y1=False, h=buf.h, want_amax=False)),
         ("mx_quantize_h", lambda: ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)),
@@ -854,14 +852,12 @@ def ab_run(args):
     wq_gu = moe_layer.quantize_expert_weights(inp["w_gu"])
     wx_gu = moe_layer.quantize_expert_weights_mx(inp["w_gu"])
     m = ops.moe_permute_nvfp4(inp["ids"], E, inp["x"], want_x_perm=True)
-    xq, xs = ops.mx_quantize(inp["x"], ops.MX_E4M3)
-    pm = ops.moe_permute(inp["ids"], E, x=xq)
-    a8s = ops.moe_gather(xs, pm["src"], k)
+    pm = ops.moe_permute_mx(inp["ids"], E, inp["x"])
     y = torch.empty(T * k, 2 * F, dtype=torch.bfloat16, device=dev)
     w4 = (m["q"], m["scales"], m["gscale"], wq_gu["q"], wq_gu["s"], wq_gu["g"], m["offsets"])
     runs = [lambda: ops.grouped_gemm_w4a4(*w4, out=y),
             lambda: ops.grouped_gemm_w4a4_scaled_mfma(*w4, out=y),
-            lambda: ops.grouped_gemm_w4a8(pm["x_perm"], a8s, wx_gu["q"], wx_gu["s"], pm["offsets"], out=y),
+            lambda: ops.grouped_gemm_w4a8(pm["q"], pm["scales"], wx_gu["q"], wx_gu["s"], pm["offsets"], out=y),
             lambda: ops.grouped_gemm_bf16(ops.NT, m["x_perm"], inp["w_gu"], m["offsets"], out=y)]
     for fn in runs:
         for _ in range(3):

@@ -228,6 +228,29 @@ int moe_permute_nvfp4_noalloc(const int32_t* topk_ids, int64_t T, int k, int E, 
                               int32_t* status, nvfp4moe_stream_t stream);
 
 /*
+ * moe_permute_mx -- moe_permute's routing metadata with the MXFP8
+ * quantization of X fused into the permutation (the W4A8 variant's
+ * activations, [JA] third paragraph; contiguous layout and op fusion, [JA]
+ * fourth paragraph): each row of X is read once, quantized once (E4M3
+ * elements, one E8M0 scale per 32, the rule of mx_quantize) and its codes
+ * and scales are written to the token's k permuted rows.  Rows past
+ * offsets[E] (skipped assignments) are zeros.  The results equal, bit for
+ * bit, mx_quantize(x, NVFP4MOE_MX_E4M3) followed by the row gather of the
+ * codes and of the scales through src.
+ *   topk_ids, T, k, E, offsets, dest, src, workspace, ws_bytes, status: as
+ *             moe_permute (workspace of moe_permute_workspace_size bytes).
+ *   x         [T][D] of x_dtype (NVFP4MOE_BF16 or NVFP4MOE_F32), 16-byte
+ *             aligned; D % 32 == 0.
+ *   q         [T*k][D] E4M3 codes out (16-byte aligned).
+ *   scales    [T*k][D/32] E8M0 scale bytes out.
+ * Errors: EINVAL (NULL, negative, bad dtype), ESHAPE (D % 32, alignment,
+ * E > 4096, k > 64, T*k >= 2^31), EWORKSPACE.
+ */
+int moe_permute_mx(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype, int64_t D,
+                   uint8_t* q, uint8_t* scales, int32_t* offsets, int32_t* dest, int32_t* src, void* workspace,
+                   size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream);
+
+/*
  * moe_gather -- out[p] = w[src[p]] * x[src[p] / k] for p < R (w = 1 when
  * topk_w is NULL); rows with src[p] < 0 are written as zeros.  With
  * topk_w == NULL any dtype is copied verbatim (NVFP4MOE_U8 row payloads,

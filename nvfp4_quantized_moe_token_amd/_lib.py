@@ -27,6 +27,8 @@ SIGNATURES = {
                                   c_vp, c_vp, c_vp, c_vp, c_size, c_vp, c_vp]),
     "moe_permute_nvfp4_noalloc": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_permute_mx": (c_int, [c_vp, c_i64, c_int, c_int, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                               c_size, c_vp, c_vp]),
     "moe_gather": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_vp]),
     "moe_scatter": (c_int, [c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_int, c_i64, c_int, c_vp, c_int, c_vp, c_vp]),
     "moe_unpermute": (c_int, [c_vp, c_int, c_vp, c_vp, c_i64, c_int, c_i64, c_vp, c_int, c_vp]),

@@ -114,6 +114,10 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n);
 // max |x| per row-group (quantize.hip); amax_out is cleared first.
 int launch_amax(const void* x, int x_dtype, int64_t n16_per_group, int64_t groups, float* amax_out, hipStream_t st);
 // MX quantizer (mx.hip); arguments validated, rows * K > 0.
+// MXFP8 quantize-scatter of T token rows into their permuted rows (mx.hip);
+// arguments validated, D % 32 == 0, the routing metadata already enqueued.
+int mx_quantize_scatter_launch(const void* x, int x_dtype, int64_t T, int k, int64_t D, const int32_t* dest,
+                               const int32_t* offsets, int E, uint8_t* q, uint8_t* scales, hipStream_t st);
 int mx_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q, uint8_t* scales,
                        hipStream_t st);
 // The same without clearing amax_out (an earlier launch on the stream did).

@@ -116,7 +116,82 @@ __global__ __launch_bounds__(NT) void mx_quantize_kernel(const uint4* __restrict
   }
 }
 
+// MXFP8 (E4M3) quantization fused with the token permutation, by scatter:
+// each 16-element half-block of X is read once, encoded once, and its codes
+// (and, from the even lane of the pair, its block's scale byte) are written
+// to the k permuted rows dest[t*k+j] of its token.  Rows past offsets[E]
+// (skipped assignments) are written as zeros, the encoding of a zero row.
+// Equal bit for bit to mx_quantize of X followed by the row gathers of the
+// codes and of the scales.
+template <int NT, bool BF16>
+__global__ __launch_bounds__(NT) void mx_quantize_scatter_kernel(const uint4* __restrict__ x, int64_t T, int k,
+                                                                 int64_t hpr, const int32_t* __restrict__ dest,
+                                                                 const int32_t* __restrict__ offsets, int E,
+                                                                 int64_t R, uint4* __restrict__ q,
+                                                                 uint8_t* __restrict__ scales) {
+  const int64_t nhalf = T * hpr;
+  const int64_t tid = blockIdx.x * (int64_t)NT + threadIdx.x, stride = (int64_t)gridDim.x * NT;
+  for (int64_t hb = tid; hb < nhalf; hb += stride) {
+    const int64_t t = hb / hpr, j = hb - t * hpr;  // token, half-block of its row
+    float v[16];
+    if (BF16) {
+      const uint4 w0 = x[2 * hb], w1 = x[2 * hb + 1];
+      const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_lo(ws[i]);
+        v[2 * i + 1] = bf16_hi(ws[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 w = x[4 * hb + i];
+        v[4 * i] = __uint_as_float(w.x);
+        v[4 * i + 1] = __uint_as_float(w.y);
+        v[4 * i + 2] = __uint_as_float(w.z);
+        v[4 * i + 3] = __uint_as_float(w.w);
+      }
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));  // the partner half of the block (hpr is even)
+    const int se = shared_exp<8>(a);
+    const uint4 codes = encode16_e4m3(v, se);
+    for (int jj = 0; jj < k; ++jj) {
+      const int32_t r = dest[t * k + jj];
+      if (r < 0) continue;
+      const int64_t oh = (int64_t)r * hpr + j;
+      q[oh] = codes;
+      if ((j & 1) == 0) scales[oh >> 1] = (uint8_t)(se + 127);
+    }
+  }
+  int64_t valid = offsets[E];
+  valid = valid < 0 ? 0 : valid > R ? R : valid;
+  for (int64_t h = valid * hpr + tid; h < R * hpr; h += stride) {
+    q[h] = make_uint4(0u, 0u, 0u, 0u);
+    if ((h & 1) == 0) scales[h >> 1] = 0;
+  }
+}
+
 }  // namespace
+
+// Enqueue the MXFP8 quantize-scatter of T token rows of D elements into the
+// permuted rows given by dest (metadata already enqueued; D % 32 == 0).
+int mx_quantize_scatter_launch(const void* x, int x_dtype, int64_t T, int k, int64_t D, const int32_t* dest,
+                               const int32_t* offsets, int E, uint8_t* q, uint8_t* scales, hipStream_t st) {
+  constexpr int NT = 256;
+  const int64_t R = T * k, hpr = D / 16;
+  int64_t grid = cdiv(T * hpr > 0 ? T * hpr : 1, NT);
+  if (grid > kMaxStreamGrid) grid = kMaxStreamGrid;
+  if (x_dtype == NVFP4MOE_BF16)
+    mx_quantize_scatter_kernel<NT, true><<<(unsigned)grid, NT, 0, st>>>(
+        reinterpret_cast<const uint4*>(x), T, k, hpr, dest, offsets, E, R, reinterpret_cast<uint4*>(q), scales);
+  else
+    mx_quantize_scatter_kernel<NT, false><<<(unsigned)grid, NT, 0, st>>>(
+        reinterpret_cast<const uint4*>(x), T, k, hpr, dest, offsets, E, R, reinterpret_cast<uint4*>(q), scales);
+  return launch_status();
+}
 
 // Enqueue the MX quantizer (arguments validated; rows * K > 0).
 int mx_quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t K, int elem, uint8_t* q, uint8_t* scales,

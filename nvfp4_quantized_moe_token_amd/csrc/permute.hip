@@ -760,6 +760,32 @@ int permute_nvfp4_impl(const int32_t* topk_ids, int64_t T, int k, int E, const v
 
 }  // namespace
 
+extern "C" int moe_permute_mx(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int x_dtype,
+                              int64_t D, uint8_t* q, uint8_t* scales, int32_t* offsets, int32_t* dest, int32_t* src,
+                              void* workspace, size_t ws_bytes, int32_t* status, nvfp4moe_stream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || D < 0) return NVFP4MOE_EINVAL;
+  if (x_dtype != NVFP4MOE_BF16 && x_dtype != NVFP4MOE_F32) return NVFP4MOE_EINVAL;
+  if (E > kMaxExperts || k > 64) return NVFP4MOE_ESHAPE;
+  if (!offsets || (T > 0 && (!topk_ids || !dest || !src))) return NVFP4MOE_EINVAL;
+  if (T > 0 && D > 0 && (!x || !q || !scales)) return NVFP4MOE_EINVAL;
+  if (D % 32 != 0) return NVFP4MOE_ESHAPE;
+  if (T > 0 && D > 0 && (!aligned(x, 16) || !aligned(q, 16))) return NVFP4MOE_ESHAPE;
+  const int64_t R = T * k;
+  if (R > 0x7FFFFFFFLL) return NVFP4MOE_ESHAPE;
+  if (ws_bytes < moe_permute_workspace_size(T, k, E) || (R > 0 && !workspace)) return NVFP4MOE_EWORKSPACE;
+  const int arch = check_arch();
+  if (arch != NVFP4MOE_OK) return arch;
+  hipStream_t st = as_stream(stream);
+  if (R == 0) {
+    fill_u32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<uint32_t*>(offsets), 0u, E + 1);
+    return launch_status();
+  }
+  const int rc = launch_metadata(topk_ids, R, E, nullptr, workspace, offsets, dest, src, status, st);
+  if (rc != NVFP4MOE_OK) return rc;
+  if (D == 0) return NVFP4MOE_OK;
+  return mx_quantize_scatter_launch(x, x_dtype, T, k, D, dest, offsets, E, q, scales, st);
+}
+
 extern "C" int moe_permute_nvfp4(const int32_t* topk_ids, int64_t T, int k, int E, const void* x, int64_t D,
                                  void* x_perm, const float* amax_in, float* amax_out, uint8_t* q, uint8_t* scales,
                                  float* gscale, int32_t* offsets, int32_t* dest, int32_t* src, void* workspace,

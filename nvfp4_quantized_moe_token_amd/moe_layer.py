@@ -177,7 +177,6 @@ class BuffersW4A8:
         e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=device)  # noqa: E731
         self.T, self.k, self.E, self.D, self.F = T, k, E, D, F
         self.ws = e(max(ops.moe_permute_workspace_size(T, k, E), 1), dt=u8)
-        self.xq, self.xs = e(T, D, dt=u8), e(T, D // 32, dt=u8)
         self.a1_q, self.a1_s = e(R, D, dt=u8), e(R, D // 32, dt=u8)
         self.h = e(R, F)
         self.a2_q, self.a2_s = e(R, F, dt=u8), e(R, F // 32, dt=u8)
@@ -189,9 +188,7 @@ def forward_w4a8(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
     """W4A8 MoE forward (MXFP8 activations, MXFP4 weights); returns the
     routing metadata dict.  H is not kept (a forward-only path)."""
     E = buf.E
-    ops.mx_quantize(x, ops.MX_E4M3, q=buf.xq, scales=buf.xs)
-    meta = ops.moe_permute(topk_ids, E, x=buf.xq, x_perm=buf.a1_q, workspace=buf.ws)
-    ops.moe_gather(buf.xs, meta["src"], buf.k, out=buf.a1_s)
+    meta = ops.moe_permute_mx(topk_ids, E, x, q=buf.a1_q, scales=buf.a1_s, workspace=buf.ws)
     ops.grouped_gemm_w4a8_silu_gate(buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], meta["offsets"], want_y1=False,
                                     h=buf.h, want_amax=False)
     ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)

@@ -118,6 +118,31 @@ def moe_permute(topk_ids, num_experts, x=None, x_perm=None, amax_out=None, want_
     return dict(offsets=offsets, dest=dest, src=src, x_perm=x_perm, amax=amax_out)
 
 
+
+def moe_permute_mx(topk_ids, num_experts, x, q=None, scales=None, status=None, workspace=None):
+    """moe_permute fused with the MXFP8 (E4M3) quantization of the permuted
+    rows: codes [T*k, D] and E8M0 scales [T*k, D/32].  Returns a dict with
+    offsets, dest, src, q and scales."""
+    _dev(topk_ids, x, q, scales, status, workspace)
+    T, k = topk_ids.shape
+    D = x.shape[1]
+    dev = x.device
+    R = T * k
+    lib = _lib.load()
+    offsets = torch.empty((num_experts + 1,), dtype=torch.int32, device=dev)
+    dest = torch.empty((R,), dtype=torch.int32, device=dev)
+    src = torch.empty((R,), dtype=torch.int32, device=dev)
+    q = torch.empty((R, D), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((R, D // 32), dtype=torch.uint8, device=dev) if scales is None else scales
+    ws_bytes = lib.moe_permute_workspace_size(T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    rc = lib.moe_permute_mx(_ptr(topk_ids), T, k, num_experts, _ptr(x), _DT[x.dtype], D, _ptr(q), _ptr(scales),
+                            _ptr(offsets), _ptr(dest), _ptr(src), _ptr(workspace), workspace.numel(), _ptr(status),
+                            _stream())
+    _check("moe_permute_mx", rc)
+    return dict(offsets=offsets, dest=dest, src=src, q=q, scales=scales)
+
 def moe_permute_nvfp4(topk_ids, num_experts, x, x_perm=None, want_x_perm=True, amax_in=None, amax_out=None,
                       q=None, scales=None, gscale=None, status=None, workspace=None):
     """moe_permute fused with the NVFP4 quantization of the gathered rows.

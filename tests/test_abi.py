@@ -31,7 +31,7 @@ def test_header_declares_entry_points():
     for n in ["nvfp4_quantize", "nvfp4_quantize_onepass", "nvfp4_quantize_onepass_workspace_size", "moe_permute", "moe_permute_workspace_size", "moe_gather", "moe_unpermute",
               "grouped_gemm_w4a4", "grouped_gemm_w4a4_silu_gate", "grouped_gemm_bf16", "moe_scatter",
               "grouped_gemm_bf16_tn_gather", "silu_gate_fwd",
-              "silu_gate_bwd", "moe_permute_nvfp4", "moe_permute_nvfp4_noalloc",
+              "silu_gate_bwd", "moe_permute_nvfp4", "moe_permute_nvfp4_noalloc", "moe_permute_mx",
               "grouped_gemm_w4a4_silu_gate_nvfp4", "grouped_gemm_w4a4_scaled_mfma", "nvfp4_quantize_colwise",
               "nvfp4_quantize_transposed", "grouped_gemm_w4a4_wgrad", "mx_quantize", "grouped_gemm_w4a8",
               "grouped_gemm_w4a8_silu_gate",
@@ -147,6 +147,26 @@ def test_permute_nvfp4_validation(lib):
     bad = list(ok); bad[16] = ws - 1
     assert f(*bad) == -5                       # workspace too small
 
+
+
+def test_permute_mx_validation(lib):
+    p = lib.moe_permute_mx
+    ws = lib.moe_permute_workspace_size(10, 8, 4)
+    args = [FAKE, 10, 8, 4, FAKE, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None]
+    bad = list(args); bad[5] = 2
+    assert p(*bad) == -1                       # u8 payload: not quantizable
+    bad = list(args); bad[4] = None
+    assert p(*bad) == -1                       # x NULL with rows
+    bad = list(args); bad[8] = None
+    assert p(*bad) == -1                       # scales NULL
+    bad = list(args); bad[6] = 48
+    assert p(*bad) == -2                       # D % 32
+    bad = list(args); bad[7] = FAKE + 8
+    assert p(*bad) == -2                       # q alignment
+    bad = list(args); bad[3] = 5000
+    assert p(*bad) == -2                       # E > 4096
+    bad = list(args); bad[13] = ws - 1
+    assert p(*bad) == -5                       # workspace too small
 
 def test_gather_unpermute_validation(lib):
     assert lib.moe_gather(FAKE, 1, 64, FAKE, None, 0, 10, FAKE, 1, None) == -1

@@ -5,7 +5,8 @@ random fp32 over a wide range), the grouped W4A8 GEMM within
 |C - C_ref| <= 1e-3 * sum|a*b| against the fp64 oracle (empty and one-row
 experts, row and column tails, fp32 and bf16 outputs, the full 8k-update
 gate+up shape on sampled rows), and the SiLU-gate epilogue bit for bit
-against the GEMM followed by silu_gate_fwd."""
+against the GEMM followed by silu_gate_fwd; the MXFP8 quantization fused
+into the permutation bit for bit against quantize-then-gather."""
 
 import os
 
@@ -197,6 +198,46 @@ def test_w4a8_silu_epilogue_equals_gemm_then_silu():
     hv = to_np(h)
     assert (np.abs(hv - moe.silu_gate_fwd(to_np(y1))) <= 2.0 ** -7 * np.abs(hv) + 1e-6).all()
 
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [512, 320])
+def test_permute_mx_equals_quantize_then_gather(dtype, D):
+    """moe_permute_mx (MXFP8 quantization fused into the permutation, each
+    token row read once) against the oracle's quantization of the gathered
+    rows and, where the scale rows are whole 16-byte units (D = 512), bit for
+    bit against mx_quantize followed by the row gathers of codes and scales;
+    out-of-range ids are skipped, the rows they leave past offsets[E] are
+    zeros, and the metadata equals moe_permute's."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(71 + D)
+    T, k, E = 500, 8, 24
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[7, 2] = E + 3
+    ids[300, 0] = -1
+    x_np = (rng.standard_normal((T, D)) * np.exp(rng.uniform(-6, 6, (T, 1)))).astype(np.float32)
+    x_np[11, 40:72] = 0.0                      # an all-zero block: scale 2^-127
+    x = to_gpu(x_np, dtype)
+    ids_g = to_gpu(ids, torch.int32)
+    got = ops.moe_permute_mx(ids_g, E, x)
+    xq, xs = ops.mx_quantize(x, ELEM["e4m3"])
+    pm = ops.moe_permute(ids_g, E, x=xq)
+    torch.cuda.synchronize()
+    for name in ("offsets", "dest", "src"):
+        assert torch.equal(got[name], pm[name]), name
+    assert torch.equal(got["q"], pm["x_perm"])
+    if (D // 32) % 16 == 0:
+        assert torch.equal(got["scales"], ops.moe_gather(xs, pm["src"], k))
+    off = to_np(got["offsets"])
+    R_valid = int(off[-1])
+    assert R_valid == T * k - 2
+    assert (to_np(got["q"])[R_valid:] == 0).all() and (to_np(got["scales"])[R_valid:] == 0).all()
+    src = to_np(got["src"])[:R_valid]
+    xv = x_np if dtype == torch.float32 else bf16_round(x_np)
+    rq, rs = mx.quantize(xv[src // k], "e4m3")
+    np.testing.assert_array_equal(to_np(got["q"])[:R_valid], rq)
+    np.testing.assert_array_equal(to_np(got["scales"])[:R_valid], rs)
 
 def test_w4a8_full_size_gate_up_sampled():
     """The moe_8k_update gate+up shape (65536 routed rows, 128 experts,
