@@ -317,9 +317,8 @@ def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
     m = lambda: box["m"]  # noqa: E731
     seq = [
         ("permute_quantize_mx", permute),
-        ("w4a8_gate_up_silu", lambda: ops.grouped_gemm_w4a8_silu_gate(
-            buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], m()["offsets"], want_y1=False, h=buf.h, want_amax=False)),
-        ("mx_quantize_h", lambda: ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)),
+        ("w4a8_gate_up_silu_mx", lambda: ops.grouped_gemm_w4a8_silu_gate_mx(
+            buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], m()["offsets"], q_h=buf.a2_q, s_h=buf.a2_s)),
         ("w4a8_down", lambda: ops.grouped_gemm_w4a8(buf.a2_q, buf.a2_s, wq_dn["q"], wq_dn["s"], m()["offsets"],
                                                     out=buf.y2)),
         ("unpermute", lambda: ops.moe_unpermute(buf.y2, m()["dest"], T, k, topk_w=inp["tw"], out=buf.out)),
@@ -359,14 +358,14 @@ def w4a8_side(torch, ops, moe_layer, inp, T, k, E, D, F, nrep):
     torch.cuda.synchronize()
     times["w4a8_gate_up"] = b0.elapsed_time(b1) / nrep
     f1, f2 = gemm_flops(T * k, D, F)
-    gemm_ms = times["w4a8_gate_up_silu"] + times["w4a8_down"]
+    gemm_ms = times["w4a8_gate_up_silu_mx"] + times["w4a8_down"]
     out = {"forward_ms": round(fwd_ms, 4), "tokens_per_s_forward": round(T / (fwd_ms * 1e-3), 1),
            "gemm_ms": round(gemm_ms, 4), "tflops": round((f1 + f2) / (gemm_ms * 1e-3) / 1e12, 1)}
     out["frac_fp8_mfma_peak"] = round(out["tflops"] / PEAK_FP8_TFLOPS, 4)
     out["frac_bf16_mfma_peak"] = round(out["tflops"] / PEAK_BF16_TFLOPS, 4)
     ops_out = {}
     for name, ms in times.items():
-        fl = {"w4a8_gate_up_silu": f1, "w4a8_gate_up": f1, "w4a8_down": f2}.get(name)
+        fl = {"w4a8_gate_up_silu_mx": f1, "w4a8_gate_up": f1, "w4a8_down": f2}.get(name)
         ent = {"ms": round(ms, 4)}
         if fl:
             tf = fl / (ms * 1e-3) / 1e12

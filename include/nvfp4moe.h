@@ -508,6 +508,23 @@ int grouped_gemm_w4a8_silu_gate(const uint8_t* a_q, const uint8_t* a_s, const ui
                                 nvfp4moe_stream_t stream);
 
 /*
+ * grouped_gemm_w4a8_silu_gate_mx -- grouped_gemm_w4a8_silu_gate that also
+ * quantizes H to MXFP8 in the epilogue ([JA], fourth paragraph: op fusion;
+ * the W4A8 variant, third paragraph), ready for the down GEMM: q_h and s_h
+ * equal, bit for bit, mx_quantize(H, NVFP4MOE_MX_E4M3) of the bf16 H the
+ * epilogue computes.  MX has no global scale, so no amax is needed first.
+ *   operands, y1, amax_out as grouped_gemm_w4a8_silu_gate; h may be NULL
+ *   (H is then not stored in bf16).
+ *   q_h [M_total][F] E4M3 codes (8-byte aligned), s_h [M_total][F/32] E8M0
+ *   scale bytes; rows >= offsets[E] are not written.
+ * Errors as grouped_gemm_w4a8 (EINVAL for q_h or s_h NULL).
+ */
+int grouped_gemm_w4a8_silu_gate_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
+                                   const uint8_t* b_s, const int32_t* expert_offsets, int E, int64_t M_total,
+                                   int64_t F, int64_t K, void* y1, void* h, float* amax_out, uint8_t* q_h,
+                                   uint8_t* s_h, nvfp4moe_stream_t stream);
+
+/*
  * grouped_gemm_bf16 -- grouped BF16 GEMM, fp32 accumulation (the BF16
  * backward, [JA] first paragraph; also the BF16 baseline of the forward).
  *   NVFP4MOE_NT: a [M_total][K], b [E][N][K] -> c [M_total][N]

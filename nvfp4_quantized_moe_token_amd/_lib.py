@@ -49,6 +49,8 @@ SIGNATURES = {
     "grouped_gemm_w4a8": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_vp]),
     "grouped_gemm_w4a8_silu_gate": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
                                             c_vp, c_vp]),
+    "grouped_gemm_w4a8_silu_gate_mx": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp,
+                                               c_vp, c_vp, c_vp, c_vp]),
     "grouped_gemm_bf16": (c_int, [c_int, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_int, c_int,
                                   c_vp, c_size, c_vp]),
     "grouped_gemm_bf16_tn_gather": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_int, c_i64, c_i64, c_i64,

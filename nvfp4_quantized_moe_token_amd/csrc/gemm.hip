@@ -44,6 +44,7 @@
 // at kernel start (up to 1024 experts) for the per-tile lookups.  The plain
 // W4A4 GEMM with bf16 output also loads the next tile's first stage during
 // the current tile's last step (see the kernel).
+#include "mx_codec.hpp"
 #include "nvfp4_codec.hpp"
 
 namespace nvfp4moe {
@@ -72,7 +73,8 @@ constexpr int MX_KS = 128;                   // reduction elements per MX (W4A8)
 // SiLU-gate epilogue).
 // W4A4_SILU_Q: W4A4_SILU that also requantizes H to NVFP4 in the epilogue
 // (its own instantiation, so that the plain SiLU-gate kernel keeps its
-// registers).
+// registers).  W4A8_SILU_Q: W4A8_SILU that quantizes H to MXFP8 in the
+// epilogue (no global scale, so no amax is needed first).
 // W4A4_TN: the NVFP4 weight gradient, C_e = A_e^T . B_e reduced over the
 // rows of expert e, both operands quantized column-wise (stored transposed:
 // K-major rows whose reduction index runs over the expert's padded segment).
@@ -82,15 +84,17 @@ constexpr int MX_KS = 128;                   // reduction elements per MX (W4A8)
 // exact fp16 expansion, kept to measure the two against each other.
 enum Mode {
   NT_BF16 = 0, NN_BF16 = 1, TN_BF16 = 2, W4A4 = 3, W4A4_SILU = 4, W4A8 = 5, W4A8_SILU = 6, W4A4_SILU_Q = 7,
-  W4A4_TN = 8, W4A4_B = 9
+  W4A4_TN = 8, W4A4_B = 9, W4A8_SILU_Q = 10
 };
 constexpr bool is_nv(int mode) {
   return mode == W4A4 || mode == W4A4_SILU || mode == W4A4_SILU_Q || mode == W4A4_TN || mode == W4A4_B;
 }
 constexpr bool is_tn(int mode) { return mode == TN_BF16 || mode == W4A4_TN; }
-constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU; }
+constexpr bool is_mx(int mode) { return mode == W4A8 || mode == W4A8_SILU || mode == W4A8_SILU_Q; }
 constexpr bool is_q(int mode) { return is_nv(mode) || is_mx(mode); }
-constexpr bool is_silu(int mode) { return mode == W4A4_SILU || mode == W4A8_SILU || mode == W4A4_SILU_Q; }
+constexpr bool is_silu(int mode) {
+  return mode == W4A4_SILU || mode == W4A8_SILU || mode == W4A4_SILU_Q || mode == W4A8_SILU_Q;
+}
 
 struct Params {
   const void* a;       // NT/NN/TN: bf16 A; W4A4: packed codes of A
@@ -116,6 +120,7 @@ struct Params {
   int64_t b_rows;      // TN with gathered B: rows of B
   // W4A4_SILU with H requantized in the epilogue (hq != NULL): NVFP4 codes,
   // scales and global scale of H with the handed-in amax h_amax_in[0].
+  // W4A8_SILU_Q: MXFP8 codes (hq, one byte each) and E8M0 scales (hs).
   uint8_t* hq;
   uint8_t* hs;
   float* hg;
@@ -1267,6 +1272,30 @@ __global__ __launch_bounds__(WM* WN * 64, WM* WN == 4 && (BM / WM) * (BN / WN) <
               }
             }
           }
+          if constexpr (MODE == W4A8_SILU_Q) {
+            // MXFP8 of H from the stored bf16 values: lanes ch .. ch ^ 3 (one
+            // row, chunks 4b .. 4b+3) hold the 32 features of one block, 8
+            // each; their amax is combined by two shuffles, every lane of the
+            // group takes the shared exponent and encodes its 8 values, and
+            // the group's first lane stores the scale byte.
+            float hv[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              hv[2 * w] = bf16_lo(hw[w]);
+              hv[2 * w + 1] = bf16_hi(hw[w]);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int i2 = 0; i2 < 8; ++i2) a = fmaxf(a, fabsf(hv[i2]));
+            a = fmaxf(a, __shfl_xor(a, 1, 64));
+            a = fmaxf(a, __shfl_xor(a, 2, 64));
+            const int se = shared_exp<8>(a);
+            const uint2 codes = make_uint2(encode4_e4m3(hv, se), encode4_e4m3(hv + 4, se));
+            if (valid) {
+              *reinterpret_cast<uint2*>(p.hq + row * F + f) = codes;
+              if ((ch & 3) == 0) p.hs[row * (F / 32) + f / 32] = (uint8_t)(se + 127);
+            }
+          }
         }
       }
       silu_amax = fmaxf(silu_amax, m);
@@ -1536,6 +1565,7 @@ int launch(int mode, const Params& p, hipStream_t st) {
     case W4A4_SILU: return launch_mode<W4A4_SILU>(cfg, p, st);
     case W4A8: return launch_mode<W4A8>(cfg, p, st);
     case W4A8_SILU: return launch_mode<W4A8_SILU>(cfg, p, st);
+    case W4A8_SILU_Q: return launch_mode<W4A8_SILU_Q>(cfg, p, st);
     case W4A4_SILU_Q: return launch_mode<W4A4_SILU_Q>(cfg, p, st);
     case W4A4_TN: return launch_mode<W4A4_TN>(cfg, p, st);
     case W4A4_B: return launch_mode<W4A4_B>(cfg, p, st);
@@ -1630,16 +1660,17 @@ namespace {
 // Shared by both W4A8 entry points.  silu: c = Y1 (NULL: not stored), h = H.
 int w4a8_entry(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                const int32_t* expert_offsets, int E, int64_t M_total, int64_t N, int64_t K, void* c, int c_dtype,
-               int silu, void* h, float* amax_out, hipStream_t st) {
+               int silu, void* h, float* amax_out, hipStream_t st, uint8_t* hq = nullptr, uint8_t* hs = nullptr) {
+  const bool qh = hq != nullptr;
   if (E < 1 || M_total < 0 || N < 0 || K < 0) return NVFP4MOE_EINVAL;
   if (c_dtype != NVFP4MOE_F32 && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
   if (silu && c_dtype != NVFP4MOE_BF16) return NVFP4MOE_EINVAL;
-  if (!expert_offsets) return NVFP4MOE_EINVAL;
-  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h : !c))) return NVFP4MOE_EINVAL;
+  if (!expert_offsets || (qh && (!silu || !hs))) return NVFP4MOE_EINVAL;
+  if (M_total > 0 && N > 0 && (!a_q || !a_s || !b_q || !b_s || (silu ? !h && !qh : !c))) return NVFP4MOE_EINVAL;
   if (K % 128 != 0 || N % 32 != 0) return NVFP4MOE_ESHAPE;
   if (silu && N % 256 != 0) return NVFP4MOE_ESHAPE;
   if (M_total > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || K > 0x7FFFFFFFLL || !aligned(a_q, 16) || !aligned(b_q, 16) ||
-      !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, 16) || !aligned(h, 16))
+      !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, 16) || !aligned(h, 16) || !aligned(hq, 8))
     return NVFP4MOE_ESHAPE;
   const int arch = check_arch();
   if (arch != NVFP4MOE_OK) return arch;
@@ -1659,7 +1690,9 @@ int w4a8_entry(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const
   p.c_f32 = c_dtype == NVFP4MOE_F32;
   p.h = h;
   p.amax = amax_out;
-  return launch(silu ? W4A8_SILU : W4A8, p, st);
+  p.hq = hq;
+  p.hs = hs;
+  return launch(silu ? (qh ? W4A8_SILU_Q : W4A8_SILU) : W4A8, p, st);
 }
 
 }  // namespace
@@ -1678,6 +1711,17 @@ extern "C" int grouped_gemm_w4a8_silu_gate(const uint8_t* a_q, const uint8_t* a_
   if (F < 0) return NVFP4MOE_EINVAL;
   return w4a8_entry(a_q, a_s, b_q, b_s, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h, amax_out,
                     as_stream(stream));
+}
+
+extern "C" int grouped_gemm_w4a8_silu_gate_mx(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
+                                              const uint8_t* b_s, const int32_t* expert_offsets, int E,
+                                              int64_t M_total, int64_t F, int64_t K, void* y1, void* h,
+                                              float* amax_out, uint8_t* q_h, uint8_t* s_h,
+                                              nvfp4moe_stream_t stream) {
+  if (F < 0) return NVFP4MOE_EINVAL;
+  if (!q_h) return NVFP4MOE_EINVAL;
+  return w4a8_entry(a_q, a_s, b_q, b_s, expert_offsets, E, M_total, 2 * F, K, y1, NVFP4MOE_BF16, 1, h, amax_out,
+                    as_stream(stream), q_h, s_h);
 }
 
 extern "C" int grouped_gemm_w4a4_silu_gate_nvfp4(const uint8_t* a_q, const uint8_t* a_s, const float* a_g,

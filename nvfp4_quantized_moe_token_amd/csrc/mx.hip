@@ -19,43 +19,14 @@
 // so a wave stores one contiguous run; the even lane of a pair stores the
 // scale byte.  The grid covers the tensor once (grid-stride only past the
 // launch limit), as the NVFP4 quantizer does.
-#include "common.hpp"
+#include "mx_codec.hpp"
 
 namespace nvfp4moe {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) short s16x2_t;
-
-// Unbiased shared exponent of a block with amax a: floor(log2 a) - emax,
-// clamped to [-127, 127]; -127 when a == 0 (also when a is an fp32
-// subnormal, whose exponent is below -126: the clamp gives -127 there).
-template <int EMAX>
-__device__ __forceinline__ int shared_exp(float a) {
-  if (!(a > 0.0f)) return -127;
-  const int e = __builtin_amdgcn_frexp_expf(a) - 1 - EMAX;  // a = m * 2^(e+1), m in [0.5, 1)
-  return e < -127 ? -127 : e > 127 ? 127 : e;
-}
-
-// 16 fp32 values of a half-block to E4M3 codes (16 bytes): scaled by
-// 2^-se (exact), clamped to +-448 (the format saturates; the converter
-// would otherwise overflow), then rounded to nearest even by the hardware
-// converter with a unit scale.
+// 16 fp32 values of a half-block to E4M3 codes (16 bytes).
 __device__ __forceinline__ uint4 encode16_e4m3(const float (&v)[16], int se) {
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = __builtin_ldexpf(v[4 * q + i], -se);
-      r[i] = __builtin_copysignf(fminf(fabsf(s), 448.0f), s);
-    }
-    s16x2_t p = {0, 0};
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, r[0], r[1], 1.0f, false);
-    p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, r[2], r[3], 1.0f, true);
-    w[q] = __builtin_bit_cast(uint32_t, p);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(encode4_e4m3(v, se), encode4_e4m3(v + 4, se), encode4_e4m3(v + 8, se), encode4_e4m3(v + 12, se));
 }
 
 // 16 fp32 values to E2M1 codes (8 bytes, element 2j in the low nibble of

@@ -184,14 +184,15 @@ class BuffersW4A8:
         self.out = e(T, D)
 
 
-def forward_w4a8(x, topk_ids, topk_w, wq_gu, wq_dn, buf):
+def forward_w4a8(x, topk_ids, topk_w, wq_gu, wq_dn, buf, keep_h=False):
     """W4A8 MoE forward (MXFP8 activations, MXFP4 weights); returns the
-    routing metadata dict.  H is not kept (a forward-only path)."""
+    routing metadata dict.  X is quantized inside the permutation and H
+    inside the gate+up epilogue; H is kept in bf16 (buf.h) only with
+    ``keep_h`` (a forward-only path)."""
     E = buf.E
     meta = ops.moe_permute_mx(topk_ids, E, x, q=buf.a1_q, scales=buf.a1_s, workspace=buf.ws)
-    ops.grouped_gemm_w4a8_silu_gate(buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], meta["offsets"], want_y1=False,
-                                    h=buf.h, want_amax=False)
-    ops.mx_quantize(buf.h, ops.MX_E4M3, q=buf.a2_q, scales=buf.a2_s)
+    ops.grouped_gemm_w4a8_silu_gate_mx(buf.a1_q, buf.a1_s, wq_gu["q"], wq_gu["s"], meta["offsets"], q_h=buf.a2_q,
+                                       s_h=buf.a2_s, h=buf.h if keep_h else None)
     ops.grouped_gemm_w4a8(buf.a2_q, buf.a2_s, wq_dn["q"], wq_dn["s"], meta["offsets"], out=buf.y2)
     ops.moe_unpermute(buf.y2, meta["dest"], buf.T, buf.k, topk_w=topk_w, out=buf.out)
     return meta

@@ -431,6 +431,25 @@ def grouped_gemm_w4a8_silu_gate(a_q, a_s, b_q, b_s, offsets, y1=None, want_y1=Tr
     return y1, h, amax_out
 
 
+def grouped_gemm_w4a8_silu_gate_mx(a_q, a_s, b_q, b_s, offsets, q_h=None, s_h=None, y1=None, h=None,
+                                   amax_out=None):
+    """Gate+up W4A8 GEMM with the SiLU gate and the MXFP8 quantization of H
+    in its epilogue.  y1, h (bf16) and amax_out are written only when given.
+    Returns (q_h, s_h)."""
+    _dev(a_q, a_s, b_q, b_s, offsets, q_h, s_h, y1, h, amax_out)
+    M, K = a_q.shape
+    E, N = b_q.shape[0], b_q.shape[1]
+    F = N // 2
+    dev = a_q.device
+    q_h = torch.empty((M, F), dtype=torch.uint8, device=dev) if q_h is None else q_h
+    s_h = torch.empty((M, F // 32), dtype=torch.uint8, device=dev) if s_h is None else s_h
+    rc = _lib.load().grouped_gemm_w4a8_silu_gate_mx(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), E,
+                                                    M, F, K, _ptr(y1), _ptr(h), _ptr(amax_out), _ptr(q_h), _ptr(s_h),
+                                                    _stream())
+    _check("grouped_gemm_w4a8_silu_gate_mx", rc)
+    return q_h, s_h
+
+
 def grouped_gemm_bf16(layout, a, b, offsets, num_experts=None, out=None, out_dtype=torch.float32, accumulate=False):
     """Grouped BF16 GEMM; layout NT / NN / TN as in the C header."""
     _dev(a, b, offsets, out)

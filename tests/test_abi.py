@@ -34,7 +34,7 @@ def test_header_declares_entry_points():
               "silu_gate_bwd", "moe_permute_nvfp4", "moe_permute_nvfp4_noalloc", "moe_permute_mx",
               "grouped_gemm_w4a4_silu_gate_nvfp4", "grouped_gemm_w4a4_scaled_mfma", "nvfp4_quantize_colwise",
               "nvfp4_quantize_transposed", "grouped_gemm_w4a4_wgrad", "mx_quantize", "grouped_gemm_w4a8",
-              "grouped_gemm_w4a8_silu_gate",
+              "grouped_gemm_w4a8_silu_gate", "grouped_gemm_w4a8_silu_gate_mx",
               "nvfp4moe_abi_version", "nvfp4moe_status_string"]:
         assert n in names
 
@@ -354,6 +354,16 @@ def test_mx_validation(lib):
     assert s(*bad) == -2                       # F % 128
     bad = list(args); bad[7] = -128
     assert s(*bad) == -1                       # F < 0
+    m = lib.grouped_gemm_w4a8_silu_gate_mx
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 128, None, None, None, FAKE, FAKE, None]
+    bad = list(args); bad[12] = None
+    assert m(*bad) == -1                       # q_h is required
+    bad = list(args); bad[13] = None
+    assert m(*bad) == -1                       # s_h is required
+    bad = list(args); bad[12] = FAKE + 4
+    assert m(*bad) == -2                       # q_h alignment
+    bad = list(args); bad[7] = 64
+    assert m(*bad) == -2                       # F % 128
 
 
 def test_silu_validation(lib):

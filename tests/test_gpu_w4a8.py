@@ -239,6 +239,35 @@ def test_permute_mx_equals_quantize_then_gather(dtype, D):
     np.testing.assert_array_equal(to_np(got["q"])[:R_valid], rq)
     np.testing.assert_array_equal(to_np(got["scales"])[:R_valid], rs)
 
+
+@pytest.mark.parametrize("counts,F,K", [([0, 1, 300, 0, 37, 256, 511], 128, 256), ([700, 33], 384, 512)])
+def test_w4a8_silu_mx_epilogue_equals_silu_then_quantize(counts, F, K):
+    """The gate+up epilogue's MXFP8 quantization of H equals, bit for bit,
+    mx_quantize of the bf16 H of the plain SiLU-gate epilogue (empty and
+    one-row experts, row tails, several tiles); H, Y1 and the amax written
+    beside the codes equal the plain epilogue's."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    rng = np.random.default_rng(sum(counts) + F + K)
+    E, M = len(counts), sum(counts)
+    off = to_gpu(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), torch.int32)
+    a = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-3, 3, (M, 1)))).astype(np.float32)
+    b = (rng.standard_normal((E, 2 * F, K)) * 0.05).astype(np.float32)
+    aq, as_ = ops.mx_quantize(to_gpu(a, torch.bfloat16), ELEM["e4m3"])
+    bq, bs = ops.mx_quantize(to_gpu(b.reshape(E * 2 * F, K), torch.bfloat16), ELEM["e2m1"])
+    bq, bs = bq.view(E, 2 * F, K // 2), bs.view(E, 2 * F, K // 32)
+    y1, h, amax = ops.grouped_gemm_w4a8_silu_gate(aq, as_, bq, bs, off)
+    y1b = torch.empty_like(y1)
+    hb = torch.empty_like(h)
+    amax_b = torch.empty_like(amax)
+    q_h, s_h = ops.grouped_gemm_w4a8_silu_gate_mx(aq, as_, bq, bs, off, y1=y1b, h=hb, amax_out=amax_b)
+    q_only, s_only = ops.grouped_gemm_w4a8_silu_gate_mx(aq, as_, bq, bs, off)
+    rq, rs = ops.mx_quantize(h, ELEM["e4m3"])
+    torch.cuda.synchronize()
+    assert torch.equal(q_h, rq) and torch.equal(s_h, rs)
+    assert torch.equal(q_only, rq) and torch.equal(s_only, rs)
+    assert torch.equal(y1b, y1) and torch.equal(hb, h) and torch.equal(amax_b, amax)
+
 def test_w4a8_full_size_gate_up_sampled():
     """The moe_8k_update gate+up shape (65536 routed rows, 128 experts,
     2F = 1536, K = 2048) as the W4A8 layer runs it: quantize X, permute the
@@ -253,8 +282,14 @@ def test_w4a8_full_size_gate_up_sampled():
     wq_gu = moe_layer.quantize_expert_weights_mx(to_gpu(d["w_gu"], torch.bfloat16))
     wq_dn = moe_layer.quantize_expert_weights_mx(to_gpu(d["w_dn"], torch.bfloat16))
     buf = moe_layer.BuffersW4A8(T, k, E, D, F, torch.device("cuda:0"))
-    meta = moe_layer.forward_w4a8(x, ids, tw, wq_gu, wq_dn, buf)
+    meta = moe_layer.forward_w4a8(x, ids, tw, wq_gu, wq_dn, buf, keep_h=True)
     torch.cuda.synchronize()
+    # H's MXFP8 codes from the gate+up epilogue equal mx_quantize of its bf16 H
+    hq, hs = ops.mx_quantize(buf.h, ELEM["e4m3"])
+    torch.cuda.synchronize()
+    R_valid = int(to_np(meta["offsets"])[-1])
+    assert torch.equal(buf.a2_q[:R_valid], hq[:R_valid])
+    assert torch.equal(buf.a2_s[:R_valid], hs[:R_valid])
     off, dest, src = moe.permute_metadata(d["topk_ids"], E)
     np.testing.assert_array_equal(to_np(meta["offsets"]), off)
     rng = np.random.default_rng(5)
