@@ -18,6 +18,9 @@
 //                       with ballots over the id bits, so the rank of an
 //                       assignment is a popcount, never an atomic: the
 //                       result does not depend on scheduling.
+// For small histograms (E <= 1024, chunks * E <= 16384) steps 2 and 3 are
+// one launch, rank_scan_kernel: each chunk's workgroup scans the histograms
+// itself.
 // Out-of-range ids are skipped (dest = -1) and flagged in the status word.
 #include <mutex>
 
@@ -253,6 +256,134 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
     // writer per expert, after every lane of the wave has read it.
     __builtin_amdgcn_wave_barrier();
     if (valid && (match >> lane) == 1ull) cur[e] += __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The scan folded into the ranks, for small histograms (E <= 1024 and
+// nchunks * E <= kFusedScanMax): one launch fewer.  Workgroup c reads every
+// chunk's histogram (at most 64 KB, from L2) and forms, for each expert,
+// the total over all chunks and the sum over the chunks before c; the
+// exclusive scan of the totals gives offsets[e], and offsets[e] plus the
+// earlier chunks' count is this chunk's first row of expert e -- what
+// scan_kernel writes for every chunk.  The ranks inside the chunk then
+// follow rank_kernel's split path.  Workgroup 0 writes the offsets and
+// reduces the amax parts; every workgroup writes its share of the src tail.
+constexpr int64_t kFusedScanMax = 16384;
+__global__ __launch_bounds__(256) void rank_scan_kernel(const int32_t* __restrict__ ids, int64_t R, int E,
+                                                        int64_t nchunks, const int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
+                                                        int32_t* __restrict__ src, int32_t* __restrict__ status,
+                                                        const float* __restrict__ amax_part, int nparts,
+                                                        float* __restrict__ amax_out) {
+  __shared__ int32_t cursor[4 * 1024];
+  __shared__ int32_t base[1024];
+  __shared__ int32_t wsum[4];
+  __shared__ float amax_red[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t c = blockIdx.x;
+  if (amax_part && c == 0) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, amax_part[i]);
+    m = wave_max(m);
+    if (lane == 0) amax_red[wid] = m;
+  }
+  // Per expert (thread e, e + 256, ... of at most 4): total and the count
+  // of the chunks before this one.
+  int32_t tot[4] = {0, 0, 0, 0}, before[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    if (e < E) {
+      for (int64_t q = 0; q < nchunks; q += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = q + u < nchunks ? counts[(q + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tot[i] += v[u];
+          if (q + u < c) before[i] += v[u];
+        }
+      }
+    }
+  }
+  // Exclusive scan of the totals in expert order: thread t owns experts t,
+  // t + 256, ...; the scan runs over (i, t) with i outer.
+  int32_t run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int32_t incl = tot[i];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int32_t pre = incl - tot[i];
+    for (int w = 0; w < wid; ++w) pre += wsum[w];
+    const int32_t round_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    const int e = threadIdx.x + 256 * i;
+    if (e < E) {
+      const int32_t off = run + pre;
+      base[e] = off + before[i];
+      if (c == 0) offsets[e] = off;
+    }
+    run += round_total;
+    __syncthreads();  // wsum is rewritten by the next round
+  }
+  const int32_t valid = run;
+  if (c == 0 && threadIdx.x == 0) {
+    offsets[E] = valid;
+    if (amax_part) *amax_out = fmaxf(fmaxf(amax_red[0], amax_red[1]), fmaxf(amax_red[2], amax_red[3]));
+  }
+  // Rows past the valid assignments (ids outside [0, E) were skipped).
+  for (int64_t p = valid + c * 256 + threadIdx.x; p < R; p += nchunks * 256) src[p] = -1;
+  // Ranks inside the chunk: rank_kernel's split path from these bases.
+  const int64_t cbase = c * kChunk;
+  const int64_t wbase = cbase + wid * (kChunk / 4);
+  for (int e = threadIdx.x; e < 4 * E; e += 256) cursor[e] = 0;
+  __syncthreads();
+  for (int st = 0; st < kChunk / 4; st += 64) {
+    const int64_t a = wbase + st + lane;
+    const int32_t e = a < R ? ids[a] : -1;
+    if (e >= 0 && e < E) atomicAdd(&cursor[wid * E + e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int32_t r = base[e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int32_t n = cursor[w * E + e];
+      cursor[w * E + e] = r;
+      r += n;
+    }
+  }
+  __syncthreads();
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  int32_t* cur = &cursor[wid * E];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int st = 0; st < kChunk / 4 / 64; ++st) {
+    const int64_t a = wbase + (int64_t)st * 64 + lane;
+    const int32_t raw = a < R ? ids[a] : -1;
+    const bool ok = raw >= 0 && raw < E;
+    if (a < R && !ok && status) atomicOr(status, NVFP4MOE_STATUS_BAD_EXPERT);
+    const int32_t e = ok ? raw : 0;
+    uint64_t match = __ballot(ok);
+    for (int b = 0; b < bits; ++b) {
+      const uint64_t m = __ballot((e >> b) & 1);
+      match &= ((e >> b) & 1) ? m : ~m;
+    }
+    if (ok) {
+      const int32_t row = cur[e] + __popcll(match & lt);
+      dest[a] = row;
+      src[row] = (int32_t)a;
+    } else if (a < R) {
+      dest[a] = -1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok && (match >> lane) == 1ull) cur[e] += __popcll(match);
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -589,6 +720,11 @@ static int launch_metadata(const int32_t* topk_ids, int64_t R, int E, float* ama
   const int64_t nblk = amax_x ? (chunks > kAmaxParts ? chunks : kAmaxParts) : chunks;
   count_kernel<<<(unsigned)nblk, 256, 0, st>>>(topk_ids, R, E, chunks, counts, amax_cleared,
                                                reinterpret_cast<const uint4*>(amax_x), amax_n16, parts);
+  if (E <= 1024 && chunks * E <= kFusedScanMax) {
+    rank_scan_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, chunks, counts, offsets, dest, src, status,
+                                                       amax_x ? parts : nullptr, (int)nblk, amax_dst);
+    return launch_status();
+  }
   scan_kernel<<<1, 1024, 0, st>>>(counts, chunks, E, offsets, R, src, amax_x ? parts : nullptr, (int)nblk,
                                   amax_dst);
   rank_kernel<<<(unsigned)chunks, 256, 0, st>>>(topk_ids, R, E, counts, dest, src, status);
