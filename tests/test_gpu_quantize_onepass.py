@@ -187,3 +187,33 @@ def test_wait_bound_fallback_reads_the_group():
         del os.environ["NVFP4MOE_ONEPASS_POLL_LIMIT"]
     _assert_same_gpu(got_w, _twopass(w, 12), "fallback, bf16")
     _assert_same_gpu(got_x, _twopass(x, 4), "fallback, fp32")
+
+
+def test_two_calls_overlapping_on_two_streams():
+    """Two one-pass calls issued on two streams at once, each sized to fill
+    the device with its own teams: whatever share of the device each gets,
+    every workgroup either sees its group's slices or reads the group
+    itself, so both results equal the two-pass quantizer's bit for bit."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(29)
+    a = (torch.randn(64 * 1536, 2048, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    b = (torch.randn(96 * 1024, 2048, device="cuda", generator=gen) * 0.05).to(torch.bfloat16)
+    b[77 * 1024 + 5, 9] = -31.0
+    want_a, want_b = _twopass(a, 64), _twopass(b, 96)
+    lib = ops._lib.load()
+    ws_a = torch.empty(lib.nvfp4_quantize_onepass_workspace_size(a.shape[0], 2048, 64), dtype=torch.uint8,
+                       device="cuda")
+    ws_b = torch.empty(lib.nvfp4_quantize_onepass_workspace_size(b.shape[0], 2048, 96), dtype=torch.uint8,
+                       device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            got_a = ops.nvfp4_quantize_onepass(a, groups=64, workspace=ws_a)
+        with torch.cuda.stream(s2):
+            got_b = ops.nvfp4_quantize_onepass(b, groups=96, workspace=ws_b)
+        torch.cuda.synchronize()
+        _assert_same_gpu(got_a, want_a, "stream 1")
+        _assert_same_gpu(got_b, want_b, "stream 2")
