@@ -72,8 +72,9 @@ __global__ void fill_gscale_kernel(const float* __restrict__ amax, float* __rest
 // false).  Uniform layout: E groups of L rows each (UNIFORM: true).  Work
 // tiles T = y * tiles_x + x (x: 256-row tile, y: 64-column tile) are taken
 // in a grid-stride loop; each workgroup loads its next tile into registers
-// while it encodes the current one from LDS.  Three workgroups per CU (the
-// register budget that holds the prefetched tile without spills).
+// while it encodes the current one from LDS.  Four workgroups per CU (the
+// register budget, 128 VGPRs, that holds the prefetched tile without spills;
+// the encode loop over a column's four blocks stays rolled to fit it).
 template <bool UNIFORM, bool IN_LDS>
 __global__ __launch_bounds__(256, 4) void colwise_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                       const int32_t* __restrict__ off, int E, int64_t L,
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256, 4) void colwise_kernel(const uint16_t* __restr
 }
 
 // Workgroups of the column-wise kernel: as many as are resident at once
-// (three per CU: 32 KB of LDS and up to 170 VGPRs each), at most one per
+// (four per CU: 40 KB of LDS and up to 128 VGPRs each), at most one per
 // work tile, so that no workgroup starts its share late.
 template <bool UNIFORM, bool IN_LDS>
 int64_t colwise_grid(int64_t tiles) {
