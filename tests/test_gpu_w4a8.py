@@ -240,6 +240,26 @@ def test_permute_mx_equals_quantize_then_gather(dtype, D):
     np.testing.assert_array_equal(to_np(got["scales"])[:R_valid], rs)
 
 
+def test_permute_mx_zero_tokens_and_zero_width():
+    """No tokens: the offsets are all zero.  D = 0: only the routing
+    metadata, equal to moe_permute's (every token on one expert, the others
+    empty)."""
+    require_gpu()
+    from nvfp4_quantized_moe_token_amd import ops
+    r = ops.moe_permute_mx(torch.zeros((0, 8), dtype=torch.int32, device="cuda"), 16,
+                           torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert (to_np(r["offsets"]) == 0).all() and r["q"].numel() == 0 and r["scales"].numel() == 0
+    ids = torch.full((300, 4), 5, dtype=torch.int32, device="cuda")
+    ids[17, 3] = 2
+    got = ops.moe_permute_mx(ids, 9, torch.zeros((300, 0), dtype=torch.float32, device="cuda"))
+    want = ops.moe_permute(ids, 9)
+    torch.cuda.synchronize()
+    for name in ("offsets", "dest", "src"):
+        assert torch.equal(got[name], want[name]), name
+    np.testing.assert_array_equal(to_np(got["offsets"]), [0, 0, 0, 1, 1, 1, 1200, 1200, 1200, 1200])
+
+
 @pytest.mark.parametrize("counts,F,K", [([0, 1, 300, 0, 37, 256, 511], 128, 256), ([700, 33], 384, 512)])
 def test_w4a8_silu_mx_epilogue_equals_silu_then_quantize(counts, F, K):
     """The gate+up epilogue's MXFP8 quantization of H equals, bit for bit,
