@@ -71,8 +71,9 @@ __global__ void fill_gscale_kernel(const float* __restrict__ amax, float* __rest
 // Grouped layout: M source rows, padded extent Kp, E experts (UNIFORM:
 // false).  Uniform layout: E groups of L rows each (UNIFORM: true).  Work
 // tiles T = y * tiles_x + x (x: 256-row tile, y: 64-column tile) are taken
-// in a grid-stride loop; each workgroup loads its next tile into registers
-// while it encodes the current one from LDS.  Four workgroups per CU (the
+// in a grid-stride loop over XCD-contiguous ranges of T (below); each
+// workgroup loads its next tile into registers while it encodes the
+// current one from LDS.  Four workgroups per CU (the
 // register budget, 128 VGPRs, that holds the prefetched tile without spills;
 // the encode loop over a column's four blocks stays rolled to fit it).
 template <bool UNIFORM, bool IN_LDS>
@@ -166,7 +167,20 @@ __global__ __launch_bounds__(256, 4) void colwise_kernel(const uint16_t* __restr
     }
   };
 
-  int64_t T = blockIdx.x;  // gridDim.x <= tiles: every workgroup has a first tile
+  // Visit number Li -> work tile: Li = 8 j + x is the j-th tile of the x-th
+  // of eight contiguous ranges of tiles (a bijection on [0, tiles)).  With a
+  // grid that is a multiple of 8, workgroup b stays on XCD b % 8 and all its
+  // tiles are in that XCD's range, so the workgroups of one XCD take
+  // neighbouring row tiles together: the 16-byte scale pieces that eight
+  // neighbouring row tiles write into one 128-byte line of an output row then
+  // meet in that XCD's L2 instead of leaving as eight partial lines.
+  const int64_t tq = tiles / 8, tr = tiles % 8;
+  auto tile_of = [&](int64_t Lx) -> int64_t {
+    const int64_t x = Lx % 8, j = Lx / 8;
+    return x * tq + (x < tr ? x : tr) + j;
+  };
+  int64_t Li = blockIdx.x;  // gridDim.x <= tiles: every workgroup has a first tile
+  int64_t T = tile_of(Li);
   int buf = 0;
   if (tid < 4) resolve(T, 0);
   __syncthreads();
@@ -178,8 +192,10 @@ __global__ __launch_bounds__(256, 4) void colwise_kernel(const uint16_t* __restr
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{0u, 0u, 0u, 0u}, rq, kOOB, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b128(u32x4_v{0u, 0u, 0u, 0u}, rq, kOOB + 16, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(0u, rs, kOOB, 0, 0);
-  for (; T < tiles; T += gridDim.x) {
-    const int64_t Tn = T + gridDim.x;
+  for (; Li < tiles; Li += gridDim.x) {
+    const int64_t Ln = Li + gridDim.x;
+    T = tile_of(Li);
+    const int64_t Tn = Ln < tiles ? tile_of(Ln) : tiles;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;

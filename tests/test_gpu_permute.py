@@ -156,16 +156,18 @@ def test_weighted_gather(in_dt, out_dt):
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float32),
                                            (torch.float32, torch.float32), (torch.float32, torch.bfloat16)])
 @pytest.mark.parametrize("weighted", [True, False])
-def test_scatter_equals_weighted_gather(in_dt, out_dt, weighted):
+@pytest.mark.parametrize("k", [3, 8, 11])
+def test_scatter_equals_weighted_gather(in_dt, out_dt, weighted, k):
     """moe_scatter (token side) and moe_gather (row side) write the same bits
     for one permutation, including invalid ids (skipped, rows past
-    offsets[E] zero)."""
+    offsets[E] zero); with the amax, top-k below, at and above the eight ids
+    the amax variant's kernel holds per piece (past eight: the plain loop)."""
     require_gpu()
     from nvfp4_quantized_moe_token_amd import ops
-    rng = np.random.default_rng(41)
-    T, k, E, D = 700, 8, 24, 264
+    rng = np.random.default_rng(41 + k)
+    T, E, D = 700, 24, 264
     ids = rng.integers(0, E, (T, k)).astype(np.int32)
-    ids[5, 3] = E + 1
+    ids[5, k - 1] = E + 1
     ids[99, 0] = -2
     r = _meta(ids, E)
     x = to_gpu(rng.standard_normal((T, D)).astype(np.float32) * 3, in_dt)
